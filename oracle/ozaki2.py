@@ -1,0 +1,368 @@
+"""Plain CPU oracle of Ozaki Scheme II (FP64 GEMM from exact INT8 GEMMs + CRT).
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.  Slow on purpose:
+every step is written the way the Ozaki II notes state it, in exact integer
+arithmetic (Python ``int``) or in float64 operations that are exact for the
+values they see.  Matrices here are logical numpy arrays (A is m x q, B is
+q x n); memory layout plays no part.
+
+Pipeline, in the notes' order (Ozaki II notes §7, "Algorithm 1"):
+
+  step 1  bit budget k from M = prod(m_t) and q           -> :func:`kbits`
+  step 2  power-of-two scaling D, E and truncation        -> :func:`row_exponents`,
+          A' = trunc(DA), B' = trunc(BE)                      :func:`truncate_rows`
+  step 3  per modulus: symmetric residues, one exact       -> :func:`smod`,
+          integer product, re-reduction of the product        :func:`residue_product`,
+                                                              :func:`reduce_product`
+  step 4  CRT accumulation Z = sum_t C''_t M_t y_t         -> :func:`crt_combine`
+  step 5  range reduction to the symmetric representative -> :func:`crt_combine`
+  step 6  unscaling C = D^-1 C''' E^-1                     -> :func:`unscale`
+
+Readings taken where the notes leave a choice open (each one also listed with
+its reason in the design notes of the repository):
+
+* moduli: the greedy pairwise-coprime sequence from 256 downward
+  (256, 255, 253, 251, 247, ...); the notes only require pairwise coprime
+  moduli in [2, 256] (§4, §6);
+* exponents: e_i is the frexp exponent of max_l |a_il|, i.e. 2^(e_i-1) <=
+  max < 2^e_i, so |a_il * 2^(k-e_i)| < 2^k; D = diag(2^(k-e_i)) (§3, §5);
+* truncation is toward zero (§3, §7 step 2);
+* k_A = k_B = k, the notes' equal-precision choice (§5), evaluated with exact
+  integers;
+* symmetric residue range for modulus m is [-floor(m/2), ceil(m/2) - 1],
+  which is [-128, 127] for m = 256 (§6);
+* C_t mod m_t takes the non-negative representative (§4, §7 step 3);
+* the final FP64 value is X * 2^(e_i + f_j - 2k) rounded once to nearest-even,
+  including the subnormal and overflow ranges (§7 step 6);
+* a row of A or column of B holding Inf or NaN gets the exponent sentinel
+  ``NONFINITE``; its integer row/column is zero and every output it touches
+  is NaN.  An all-zero row/column has exponent 0 (frexp of 0.0) and yields +0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+#: Exponent recorded for a row/column that contains Inf or NaN.
+NONFINITE = 2**31 - 1
+
+#: Largest modulus usable with signed int8 residues (Ozaki II notes §6).
+MODULUS_MAX = 256
+
+
+# ----------------------------------------------------------------------------
+# Step 1: moduli, CRT constants, bit budget
+# ----------------------------------------------------------------------------
+
+def greedy_moduli(s: int) -> list[int]:
+    """First ``s`` moduli: scan 256, 255, ... and keep each candidate that is
+    coprime to every modulus already kept.
+
+    Ozaki II notes §4 require pairwise-coprime moduli; §6 bounds them by
+    2 <= m_t <= 256 so that symmetric residues fit in int8.
+    """
+    if s < 1:
+        raise ValueError("s must be >= 1")
+    chosen: list[int] = []
+    cand = MODULUS_MAX
+    while len(chosen) < s:
+        if cand < 2:
+            raise ValueError(f"fewer than {s} pairwise-coprime moduli in [2, 256]")
+        if all(math.gcd(cand, c) == 1 for c in chosen):
+            chosen.append(cand)
+        cand -= 1
+    return chosen
+
+
+def crt_constants(moduli: list[int]):
+    """M = prod m_t, M_t = M / m_t and y_t = M_t^-1 mod m_t (Ozaki II notes §4).
+
+    Returns ``(M, Mt, yt)`` with Python integers; y_t is the representative in
+    [0, m_t).
+    """
+    M = 1
+    for m in moduli:
+        M *= m
+    Mt = [M // m for m in moduli]
+    yt = [pow(Mt_t % m, -1, m) for Mt_t, m in zip(Mt, moduli)]
+    return M, Mt, yt
+
+
+def kbits(M: int, q: int) -> int:
+    """k = floor(1/2 * log2((M/2 - 1) / q)), evaluated exactly (Ozaki II notes §5).
+
+    floor(log2(x)) for x = (M/2 - 1)/q is the largest integer j with
+    q * 2^j <= M/2 - 1, i.e. 2q * 2^j <= M - 2.  For j >= 0 it equals the bit
+    length of floor((M - 2) / (2q)) minus one.  Returns a value < 1 when the
+    budget leaves no bits (the caller must then reject the problem).
+    """
+    if q < 1:
+        raise ValueError("q must be >= 1")
+    t = (M - 2) // (2 * q)
+    if t < 1:
+        return -1
+    j = t.bit_length() - 1
+    return j // 2
+
+
+# ----------------------------------------------------------------------------
+# Step 2: exponents and truncation
+# ----------------------------------------------------------------------------
+
+def row_exponents(A: np.ndarray) -> np.ndarray:
+    """e_i with 2^(e_i - 1) <= max_l |a_il| < 2^e_i (frexp exponent), int32.
+
+    All-zero rows get 0; rows holding Inf/NaN get ``NONFINITE``.
+    (Ozaki II notes §3: D has power-of-two diagonal entries; §5: the bound
+    c_max <= q 2^(k_A+k_B) needs |DA| < 2^k_A.)
+    """
+    A = np.asarray(A, dtype=np.float64)
+    e = np.zeros(A.shape[0], dtype=np.int64)
+    if A.shape[1] == 0:
+        return e.astype(np.int32)
+    amax = np.max(np.abs(A), axis=1)
+    for i, v in enumerate(amax):
+        v = float(v)
+        if not math.isfinite(v):
+            e[i] = NONFINITE
+        else:
+            e[i] = math.frexp(v)[1]
+    return e.astype(np.int32)
+
+
+def col_exponents(B: np.ndarray) -> np.ndarray:
+    """f_j, the exponent of column j of B (same rule as :func:`row_exponents`)."""
+    return row_exponents(np.asarray(B).T)
+
+
+def truncate_rows(A: np.ndarray, e: np.ndarray, k: int) -> np.ndarray:
+    """A' = trunc(D A) with D = diag(2^(k - e_i)) (Ozaki II notes §3, §7 step 2).
+
+    Returned as float64 holding exact integers (|A'| <= 2^k - 1, at most 53
+    significant bits).  Multiplying by a power of two is exact unless the
+    product drops below 2^-1022; such products are below 1 in magnitude and
+    truncate to 0 either way, so trunc(ldexp(a, k - e_i)) is exact.  Rows with
+    the ``NONFINITE`` sentinel are zero.  -0.0 is normalised to +0.0.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    e64 = np.asarray(e, dtype=np.int64)
+    bad = e64 == NONFINITE
+    shift = np.where(bad, 0, k - e64).astype(np.int32)
+    Ap = np.trunc(np.ldexp(A, shift[:, None]))
+    Ap[bad, :] = 0.0
+    return Ap + 0.0
+
+
+def truncate_cols(B: np.ndarray, f: np.ndarray, k: int) -> np.ndarray:
+    """B' = trunc(B E) with E = diag(2^(k - f_j))."""
+    return truncate_rows(np.asarray(B).T, f, k).T
+
+
+# ----------------------------------------------------------------------------
+# Step 3: symmetric residues, exact products, re-reduction
+# ----------------------------------------------------------------------------
+
+def smod(X: np.ndarray, m: int) -> np.ndarray:
+    """Symmetric residue of integer-valued float64 X modulo m, as int8.
+
+    The result r satisfies r = X (mod m) and -floor(m/2) <= r <= ceil(m/2) - 1
+    (Ozaki II notes §6: residues lie in [-128, 127]).  ``np.fmod`` of two
+    doubles is exact, so no rounding enters.
+    """
+    r = np.fmod(np.asarray(X, dtype=np.float64), float(m))   # in (-m, m), sign of X
+    r = np.where(r < 0, r + m, r)                              # in [0, m)
+    r = np.where(r >= (m + 1) // 2, r - m, r)                  # in [-floor(m/2), ceil(m/2)-1]
+    return r.astype(np.int8)
+
+
+def residue_product(At: np.ndarray, Bt: np.ndarray) -> np.ndarray:
+    """C'_t = A'_t B'_t for int8 residue matrices, exact, as int32
+    (Ozaki II notes §4; §6: exact while q < 2^17).
+
+    Every product is an integer of magnitude <= 2^14 and every partial sum of
+    a length-q dot product is an integer of magnitude <= q 2^14 < 2^31, far
+    inside the 53-bit float64 significand, so a float64 matrix product is
+    exact in any summation order.
+    """
+    q = At.shape[1]
+    if q >= 2**17:
+        raise ValueError("q >= 2^17: int32 accumulation would not be exact")
+    C = np.asarray(At, dtype=np.float64) @ np.asarray(Bt, dtype=np.float64)
+    return C.astype(np.int32)
+
+
+def reduce_product(Ct: np.ndarray, m: int) -> np.ndarray:
+    """C''_t = C'_t mod m_t, non-negative representative, as uint8
+    (Ozaki II notes §4, §7 step 3)."""
+    return np.mod(np.asarray(Ct, dtype=np.int64), m).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# Steps 4-5: CRT accumulation and range reduction
+# ----------------------------------------------------------------------------
+
+def crt_combine(r: list[np.ndarray], moduli: list[int]) -> np.ndarray:
+    """Z = sum_t C''_t M_t y_t, C''' = Z mod M, symmetric representative
+    (Ozaki II notes §4 for the CRT sum, §5 for the range reduction).
+
+    Returns an object array of Python ints X with |X| < M/2.  With 2 c_max < M
+    the tie X = M/2 cannot occur; it is asserted absent.
+    """
+    M, Mt, yt = crt_constants(moduli)
+    Z = np.zeros(np.asarray(r[0]).shape, dtype=object)
+    for rt, Mt_t, yt_t in zip(r, Mt, yt):
+        Z = Z + np.asarray(rt, dtype=np.int64).astype(object) * (Mt_t * yt_t)
+    X = Z % M
+    half = M // 2
+    if M % 2 == 0:
+        assert not np.any(X == half), "symmetric representative is ambiguous"
+    X = np.where(X > half, X - M, X)
+    return X
+
+
+# ----------------------------------------------------------------------------
+# Step 6: unscaling with a single rounding
+# ----------------------------------------------------------------------------
+
+def round_scaled(X: int, p: int) -> float:
+    """X * 2^p rounded once to the nearest float64 (ties to even).
+
+    Python's int -> float conversion and its int / int true division are both
+    correctly rounded, subnormal range included; overflow becomes +-Inf.
+    """
+    X = int(X)
+    if X == 0:
+        return 0.0
+    try:
+        if p >= 0:
+            return float(X << p)
+        return X / (1 << (-p))
+    except OverflowError:
+        return math.copysign(math.inf, X)
+
+
+def unscale(X: np.ndarray, e: np.ndarray, f: np.ndarray, k: int) -> np.ndarray:
+    """C = D^-1 C''' E^-1, i.e. C_ij = RN(X_ij * 2^(e_i + f_j - 2k))
+    (Ozaki II notes §7 step 6).  NaN where e_i or f_j is ``NONFINITE``."""
+    m, n = X.shape
+    C = np.empty((m, n), dtype=np.float64)
+    for i in range(m):
+        ei = int(e[i])
+        for j in range(n):
+            fj = int(f[j])
+            if ei == NONFINITE or fj == NONFINITE:
+                C[i, j] = math.nan
+            else:
+                C[i, j] = round_scaled(X[i, j], ei + fj - 2 * k)
+    return C
+
+
+# ----------------------------------------------------------------------------
+# The whole scheme
+# ----------------------------------------------------------------------------
+
+def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False):
+    """C ~= A B by Ozaki Scheme II with s moduli (Ozaki II notes §7).
+
+    With ``stages=True`` also returns a dict of every intermediate:
+    ``moduli, M, k, e, f, Ap, Bp, Ares (s x m x q int8), Bres (s x q x n int8),
+    Ct (s x m x n int32), rt (s x m x n uint8), X (object), C``.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    m, q = A.shape
+    q2, n = B.shape
+    if q != q2:
+        raise ValueError("inner dimensions differ")
+    mods = greedy_moduli(s)
+    M, _, _ = crt_constants(mods)
+    if q == 0:
+        C = np.zeros((m, n))
+        return (C, {"moduli": mods, "M": M, "k": None, "C": C}) if stages else C
+    if q >= 2**17:
+        raise ValueError("q >= 2^17 is outside the exact int32 range")
+    k = kbits(M, q)
+    if k < 1:
+        raise ValueError(f"s={s} leaves no bits for q={q}")
+    e = row_exponents(A)
+    f = col_exponents(B)
+    Ap = truncate_rows(A, e, k)
+    Bp = truncate_cols(B, f, k)
+    Ares, Bres, Ct, rt = [], [], [], []
+    for mt in mods:
+        At = smod(Ap, mt)
+        Bt = smod(Bp, mt)
+        Ct_t = residue_product(At, Bt)
+        Ares.append(At)
+        Bres.append(Bt)
+        Ct.append(Ct_t)
+        rt.append(reduce_product(Ct_t, mt))
+    X = crt_combine(rt, mods)
+    C = unscale(X, e, f, k)
+    if not stages:
+        return C
+    return C, {
+        "moduli": mods, "M": M, "k": k, "e": e, "f": f, "Ap": Ap, "Bp": Bp,
+        "Ares": np.stack(Ares), "Bres": np.stack(Bres), "Ct": np.stack(Ct),
+        "rt": np.stack(rt), "X": X, "C": C,
+    }
+
+
+def dgemm_block(A: np.ndarray, B: np.ndarray, s: int, rows, cols, stages: bool = False):
+    """The oracle on the sub-problem A[rows, :] x B[:, cols].
+
+    Exponents depend only on their own row of A or column of B and k only on
+    q, so these are exactly the entries (rows x cols) of ``dgemm(A, B, s)``.
+    Used to check sampled outputs of problems too large for the full oracle.
+    """
+    A = np.asarray(A)
+    B = np.asarray(B)
+    return dgemm(A[np.asarray(rows), :], B[:, np.asarray(cols)], s, stages=stages)
+
+
+# ----------------------------------------------------------------------------
+# Exact reference product (for correct-bit measurements and error bounds)
+# ----------------------------------------------------------------------------
+
+def _exact_int(x: float):
+    """x = mant * 2^expo with integer mant (exact decomposition of a double)."""
+    mant, expo = math.frexp(x)
+    return int(mant * (1 << 53)), expo - 53
+
+
+def exact_dot(a: np.ndarray, b: np.ndarray):
+    """Exact sum_l a_l b_l of two float64 vectors as ``(N, p)`` meaning N * 2^p."""
+    terms = []
+    for x, y in zip(np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)):
+        if x == 0.0 or y == 0.0:
+            continue
+        mx, ex = _exact_int(float(x))
+        my, ey = _exact_int(float(y))
+        terms.append((mx * my, ex + ey))
+    if not terms:
+        return 0, 0
+    p = min(t[1] for t in terms)
+    return sum(v << (ep - p) for v, ep in terms), p
+
+
+def correct_bits(C: np.ndarray, A: np.ndarray, B: np.ndarray, rows, cols) -> float:
+    """-log2 max |C_ij - (AB)_ij| / (|A||B|)_ij over the given entries, with
+    (AB)_ij computed exactly.  Returns 64.0 for an exact match everywhere."""
+    from fractions import Fraction
+    worst = Fraction(0)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    absB = np.abs(B)
+    for i, j in zip(rows, cols):
+        N, p = exact_dot(A[i, :], B[:, j])
+        exact = Fraction(N) * (Fraction(2) ** p)
+        Na, pa = exact_dot(np.abs(A[i, :]), absB[:, j])
+        denom = Fraction(Na) * (Fraction(2) ** pa)
+        if denom == 0:
+            continue
+        err = abs(Fraction(float(C[i, j])) - exact) / denom
+        worst = max(worst, err)
+    if worst == 0:
+        return 64.0
+    return -math.log2(float(worst))
