@@ -1,0 +1,74 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/ozgemm.h"
+
+namespace oz {
+
+// Tiling constants.  Residue planes are padded so that every kernel works on
+// whole tiles: rows to ROW_PAD, the inner dimension to K_PAD.
+constexpr int ROW_PAD = 256;
+constexpr int K_PAD = 128;
+constexpr int MAX_LIMBS = 5;      // 32-bit limbs of M: log2 M < 160 for s <= 20
+constexpr int SCALE_CHUNK = 128;  // columns of A per partial row-max block
+constexpr int MAX_SHIFT = 32;     // |A'| < 2^(53 + MAX_SHIFT); k <= 78 for s <= 20
+
+inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
+
+// Per-modulus constants for the residue kernel (Ozaki II notes §6).
+struct ResidueConsts {
+  int s;
+  int k;                        // bits kept: |A'| <= 2^k - 1
+  int big;                      // k > 53: A' may exceed the 53-bit significand
+  int m[OZGEMM_S_MAX];          // moduli
+  int lo[OZGEMM_S_MAX];         // -floor(m/2)
+  int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1
+  double inv[OZGEMM_S_MAX];     // RN(1/m)
+  uint8_t pow2[OZGEMM_S_MAX][MAX_SHIFT];  // 2^sh mod m, sh < MAX_SHIFT
+};
+
+// Per-modulus constants for the GEMM epilogue.
+struct GemmConsts {
+  int s;
+  int m[OZGEMM_S_MAX];
+  double inv[OZGEMM_S_MAX];
+};
+
+// CRT constants (Ozaki II notes §4): W_t = M_t y_t < M split in 32-bit limbs,
+// stored as doubles so that sum_t r_t W_t accumulates exactly in FP64.
+struct CrtConsts {
+  int s;
+  int L;                             // limbs of M (top limb nonzero)
+  int k;
+  double w[OZGEMM_S_MAX][MAX_LIMBS]; // limbs of W_t
+  uint32_t M[MAX_LIMBS + 1];         // limbs of M (extra zero limb)
+  uint32_t half[MAX_LIMBS + 1];      // limbs of M/2 (M is even: m_1 = 256)
+  double invM;                       // RN(1/M)
+};
+
+// Launchers (each enqueues on `st`).
+hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,
+                                  int nchunks, hipStream_t st);
+hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
+                                   hipStream_t st);
+hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st);
+
+// Residues of the rows of X where element (r, l) sits at X[r*rs + l*ls].
+// Writes `rows_pad` x q_pad int8 planes (plane stride rows_pad*q_pad).
+hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
+                          const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad,
+                          double* prime, long prime_rs, long prime_ls, hipStream_t st);
+
+hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad,
+                       const GemmConsts& c, int32_t* Ct, uint8_t* rt, hipStream_t st);
+
+hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e,
+                      const int32_t* f, const CrtConsts& c, double* C, int ldc, hipStream_t st);
+
+hipError_t launch_fill_zero(double* C, int m, int n, int ldc, hipStream_t st);
+
+}  // namespace oz

@@ -1,0 +1,533 @@
+// Host side of the C-ABI: configuration, argument checks, exact constants
+// and the launch sequence of the four steps (Ozaki II notes §7).
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "oz_internal.h"
+
+namespace oz {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Fixed-width unsigned integers (32-bit limbs, little endian) for the CRT
+// constants: M < 2^160 for s <= 20, and Z/2q style divisions by small values.
+// ---------------------------------------------------------------------------
+constexpr int BIG_LIMBS = 6;
+struct Big {
+  uint32_t w[BIG_LIMBS] = {0, 0, 0, 0, 0, 0};
+};
+
+Big big_from(uint32_t v) {
+  Big b;
+  b.w[0] = v;
+  return b;
+}
+
+void big_mul_small(Big& a, uint32_t v) {
+  uint64_t carry = 0;
+  for (int i = 0; i < BIG_LIMBS; ++i) {
+    const uint64_t p = (uint64_t)a.w[i] * v + carry;
+    a.w[i] = (uint32_t)p;
+    carry = p >> 32;
+  }
+}
+
+// a / v (v > 0), returns the remainder
+uint32_t big_divmod_small(const Big& a, uint32_t v, Big* quot) {
+  uint64_t rem = 0;
+  Big q;
+  for (int i = BIG_LIMBS - 1; i >= 0; --i) {
+    const uint64_t cur = (rem << 32) | a.w[i];
+    q.w[i] = (uint32_t)(cur / v);
+    rem = cur % v;
+  }
+  if (quot) *quot = q;
+  return (uint32_t)rem;
+}
+
+void big_sub_small(Big& a, uint32_t v) {
+  uint64_t borrow = v;
+  for (int i = 0; i < BIG_LIMBS && borrow; ++i) {
+    const uint64_t cur = a.w[i];
+    a.w[i] = (uint32_t)(cur - borrow);
+    borrow = cur < borrow ? 1 : 0;
+  }
+}
+
+int big_bitlen(const Big& a) {
+  for (int i = BIG_LIMBS - 1; i >= 0; --i)
+    if (a.w[i]) return 32 * i + (32 - __builtin_clz(a.w[i]));
+  return 0;
+}
+
+double big_to_double(const Big& a) {
+  double d = 0.0;
+  for (int i = BIG_LIMBS - 1; i >= 0; --i) d = d * 4294967296.0 + (double)a.w[i];
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// Moduli: scan 256 downward, keep each value coprime to all kept ones
+// (Ozaki II notes §4 pairwise coprime; §6 m_t <= 256).
+// ---------------------------------------------------------------------------
+int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+const std::vector<int>& moduli_list() {
+  static std::vector<int> mods = [] {
+    std::vector<int> out;
+    for (int cand = 256; cand >= 2 && (int)out.size() < OZGEMM_S_MAX; --cand) {
+      bool ok = true;
+      for (int x : out) ok = ok && gcd_int(cand, x) == 1;
+      if (ok) out.push_back(cand);
+    }
+    return out;
+  }();
+  return mods;
+}
+
+Big product_M(int s) {
+  Big M = big_from(1);
+  for (int t = 0; t < s; ++t) big_mul_small(M, (uint32_t)moduli_list()[t]);
+  return M;
+}
+
+// k = floor(1/2 floor(log2((M/2 - 1)/q))): largest j with 2q 2^j <= M - 2 is
+// bitlen(floor((M - 2) / 2q)) - 1 (Ozaki II notes §5).
+int kbits_exact(int s, int q) {
+  if (s < 1 || s > OZGEMM_S_MAX || q < 1) return -1;
+  Big M = product_M(s);
+  big_sub_small(M, 2);
+  Big t;
+  big_divmod_small(M, 2u * (uint32_t)q, &t);
+  const int bl = big_bitlen(t);
+  if (bl == 0) return -1;
+  return (bl - 1) / 2;
+}
+
+int modinv_small(int a, int m) {  // a^-1 mod m, gcd(a, m) = 1
+  int t = 0, newt = 1, r = m, newr = a % m;
+  while (newr) {
+    const int qq = r / newr;
+    int tmp = t - qq * newt;
+    t = newt;
+    newt = tmp;
+    tmp = r - qq * newr;
+    r = newr;
+    newr = tmp;
+  }
+  return t < 0 ? t + m : t;
+}
+
+void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc) {
+  const auto& mods = moduli_list();
+  const int k = kbits_exact(s, q);
+  std::memset(rc, 0, sizeof(*rc));
+  std::memset(gc, 0, sizeof(*gc));
+  std::memset(cc, 0, sizeof(*cc));
+  rc->s = gc->s = cc->s = s;
+  rc->k = cc->k = k;
+  rc->big = k > 53 ? 1 : 0;
+  for (int t = 0; t < s; ++t) {
+    const int m = mods[t];
+    rc->m[t] = gc->m[t] = m;
+    rc->lo[t] = -(m / 2);
+    rc->hi[t] = (m + 1) / 2 - 1;
+    rc->inv[t] = gc->inv[t] = 1.0 / (double)m;
+    int p = 1 % m;
+    for (int sh = 0; sh < MAX_SHIFT; ++sh) {
+      rc->pow2[t][sh] = (uint8_t)p;
+      p = (p * 2) % m;
+    }
+  }
+  const Big M = product_M(s);
+  const int bits = big_bitlen(M);
+  cc->L = (bits + 31) / 32;
+  for (int l = 0; l <= MAX_LIMBS; ++l) cc->M[l] = l < BIG_LIMBS ? M.w[l] : 0;
+  Big half;
+  big_divmod_small(M, 2, &half);
+  for (int l = 0; l <= MAX_LIMBS; ++l) cc->half[l] = l < BIG_LIMBS ? half.w[l] : 0;
+  cc->invM = 1.0 / big_to_double(M);
+  for (int t = 0; t < s; ++t) {
+    Big Mt;
+    const uint32_t mt = (uint32_t)mods[t];
+    big_divmod_small(M, mt, &Mt);
+    const uint32_t Mt_mod = big_divmod_small(Mt, mt, nullptr);
+    const int y = modinv_small((int)Mt_mod, (int)mt);
+    Big W = Mt;
+    big_mul_small(W, (uint32_t)y);  // W_t = M_t y_t < M
+    for (int l = 0; l < MAX_LIMBS; ++l) cc->w[t][l] = (double)W.w[l];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Global configuration and workspace layout
+// ---------------------------------------------------------------------------
+constexpr int NCH_MAX = 256;  // partial row-max chunks of A
+
+struct Layout {
+  size_t pmax, e, f, ares, bres, rt, total;
+};
+
+Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
+  const size_t mp = round_up((size_t)std::max(max_m, 1), ROW_PAD);
+  const size_t np = round_up((size_t)std::max(max_n, 1), ROW_PAD);
+  const size_t qp = round_up((size_t)std::max(max_q, 1), K_PAD);
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L.pmax = take((size_t)NCH_MAX * mp * 8);
+  L.e = take(mp * 4);
+  L.f = take(np * 4);
+  L.ares = take((size_t)s_max * mp * qp);
+  L.bres = take((size_t)s_max * np * qp);
+  L.rt = take((size_t)s_max * mp * np);
+  L.total = off;
+  return L;
+}
+
+struct State {
+  bool configured = false;
+  int s_max = 0, max_m = 0, max_n = 0, max_q = 0;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  Layout lay{};
+  bool timing = false;
+  std::vector<std::array<hipEvent_t, 5>> events;
+  std::string hip_err;
+};
+State g;
+
+constexpr size_t TIMING_MAX_CALLS = 4096;
+// residue grids index tiles of 32 rows in grid.y (<= 65535)
+constexpr int OZ_MAX_ROWS = 1 << 21;
+
+int hip_fail(hipError_t err) {
+  g.hip_err = hipGetErrorString(err);
+  return OZGEMM_HIP_ERROR;
+}
+
+#define OZ_CHECK(expr)                             \
+  do {                                             \
+    const hipError_t oz_err_ = (expr);             \
+    if (oz_err_ != hipSuccess) return hip_fail(oz_err_); \
+  } while (0)
+
+void dims(int m, int n, int q, int* mp, int* np, int* qp) {
+  *mp = (int)round_up((size_t)std::max(m, 1), ROW_PAD);
+  *np = (int)round_up((size_t)std::max(n, 1), ROW_PAD);
+  *qp = (int)round_up((size_t)std::max(q, 1), K_PAD);
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + bbytes && pb < pa + abytes;
+}
+
+size_t mat_bytes(int rows, int cols, int ld) {
+  if (rows == 0 || cols == 0) return 0;
+  return ((size_t)ld * (size_t)(cols - 1) + (size_t)rows) * sizeof(double);
+}
+
+// Shared checks of (m, n, q, A, lda, B, ldb) and the size/range limits.
+int check_common(int m, int n, int q, const double* A, int lda, const double* B, int ldb) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 0) return -3;
+  if (A == nullptr && m > 0 && q > 0) return -4;
+  if (lda < std::max(1, m)) return -5;
+  if (B == nullptr && q > 0 && n > 0) return -6;
+  if (ldb < std::max(1, q)) return -7;
+  return 0;
+}
+
+int check_range(int m, int n, int q, int s) {
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
+  if (q >= OZGEMM_Q_LIMIT) return OZGEMM_RANGE;
+  if (q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+  return 0;
+}
+
+int nchunks_for(int m, int q) {
+  const int xblocks = (m + 255) / 256;
+  int nch = (4096 + xblocks - 1) / xblocks;
+  nch = std::min(nch, (q + 31) / 32);
+  nch = std::min(nch, NCH_MAX);
+  return std::max(nch, 1);
+}
+
+int run_scale(int m, int n, int q, const double* A, int lda, const double* B, int ldb, int32_t* e, int32_t* f) {
+  const int mp = (int)round_up((size_t)std::max(g.max_m, 1), ROW_PAD);
+  uint64_t* pmax = reinterpret_cast<uint64_t*>(g.ws + g.lay.pmax);
+  const int nch = nchunks_for(m, q);
+  if (m > 0) {
+    OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, g.stream));
+    OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, g.stream));
+  }
+  if (n > 0) OZ_CHECK(launch_col_exp(B, q, n, ldb, f, g.stream));
+  return 0;
+}
+
+int run_residue(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, const int32_t* e,
+                const int32_t* f, int8_t* Ares, int8_t* Bres, double* Ap, double* Bp) {
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  ResidueConsts rc;
+  GemmConsts gc;
+  CrtConsts cc;
+  make_consts(s, q, &rc, &gc, &cc);
+  // A: element (i, l) at A[i + l*lda]; A' copy m x q with ld m
+  OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, Ap, 1, m, g.stream));
+  // B seen as rows j: element (j, l) at B[l + j*ldb]; B' copy q x n with ld q
+  OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, Bp, q, 1, g.stream));
+  return 0;
+}
+
+}  // namespace
+}  // namespace oz
+
+using namespace oz;
+
+extern "C" {
+
+size_t ozgemm_workspace_bytes(int max_m, int max_n, int max_q, int s_max) {
+  if (max_m < 0 || max_n < 0 || max_q < 0 || s_max < 1 || s_max > OZGEMM_S_MAX) return 0;
+  return make_layout(max_m, max_n, max_q, s_max).total;
+}
+
+int ozgemm_config(int s_max, int max_m, int max_n, int max_q, void* hip_stream, void* workspace,
+                  size_t workspace_bytes) {
+  if (s_max < 1 || s_max > OZGEMM_S_MAX) return -1;
+  if (max_m < 0 || max_m > OZ_MAX_ROWS) return -2;
+  if (max_n < 0 || max_n > OZ_MAX_ROWS) return -3;
+  if (max_q < 0 || max_q >= OZGEMM_Q_LIMIT) return -4;
+  if (workspace == nullptr) return -6;
+  const Layout lay = make_layout(max_m, max_n, max_q, s_max);
+  if (workspace_bytes < lay.total) return OZGEMM_WORKSPACE_TOO_SMALL;
+  ozgemm_timing(0);
+  g.configured = true;
+  g.s_max = s_max;
+  g.max_m = max_m;
+  g.max_n = max_n;
+  g.max_q = max_q;
+  g.stream = (hipStream_t)hip_stream;
+  g.ws = (char*)workspace;
+  g.ws_bytes = workspace_bytes;
+  g.lay = lay;
+  return OZGEMM_OK;
+}
+
+int ozgemm_set_stream(void* hip_stream) {
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  g.stream = (hipStream_t)hip_stream;
+  return OZGEMM_OK;
+}
+
+int ozgemm_free(void) {
+  ozgemm_timing(0);
+  g = State{};
+  return OZGEMM_OK;
+}
+
+const char* ozgemm_strerror(int status) {
+  static thread_local std::string msg;
+  if (status == OZGEMM_OK) return "success";
+  if (status < 0) {
+    msg = "invalid argument " + std::to_string(-status);
+    return msg.c_str();
+  }
+  switch (status) {
+    case OZGEMM_NOT_CONFIGURED: return "ozgemm_config has not been called";
+    case OZGEMM_RANGE: return "problem outside the supported range (q >= 2^17, k < 1, or above the configured maximum)";
+    case OZGEMM_WORKSPACE_TOO_SMALL: return "workspace smaller than ozgemm_workspace_bytes";
+    case OZGEMM_HIP_ERROR:
+      msg = "HIP error: " + g.hip_err;
+      return msg.c_str();
+    default: return "unknown status";
+  }
+}
+
+int ozgemm_moduli(int s, int* moduli_out) {
+  if (s < 1 || s > OZGEMM_S_MAX || moduli_out == nullptr) return -1;
+  for (int t = 0; t < s; ++t) moduli_out[t] = moduli_list()[t];
+  return 0;
+}
+
+int ozgemm_kbits(int s, int q) {
+  if (q >= OZGEMM_Q_LIMIT) return -2;
+  return kbits_exact(s, q);
+}
+
+int ozgemm_plane_dims(int m, int n, int q, int* m_pad, int* n_pad, int* q_pad) {
+  if (m < 0 || n < 0 || q < 0 || !m_pad || !n_pad || !q_pad) return -1;
+  dims(m, n, q, m_pad, n_pad, q_pad);
+  return 0;
+}
+
+int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B, int ldb, double* C, int ldc,
+                 int s) {
+  int st = check_common(m, n, q, A, lda, B, ldb);
+  if (st) return st;
+  if (C == nullptr && m > 0 && n > 0) return -8;
+  if (ldc < std::max(1, m)) return -9;
+  if (s < 1 || s > OZGEMM_S_MAX) return -10;
+  if ((st = check_range(m, n, q, s))) return st;
+  if (m == 0 || n == 0) return OZGEMM_OK;
+  const size_t cb = mat_bytes(m, n, ldc);
+  if (overlaps(C, cb, A, mat_bytes(m, q, lda)) || overlaps(C, cb, B, mat_bytes(q, n, ldb))) return -8;
+  if (q == 0) {
+    OZ_CHECK(launch_fill_zero(C, m, n, ldc, g.stream));
+    return OZGEMM_OK;
+  }
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  int32_t* e = reinterpret_cast<int32_t*>(g.ws + g.lay.e);
+  int32_t* f = reinterpret_cast<int32_t*>(g.ws + g.lay.f);
+  int8_t* Ares = reinterpret_cast<int8_t*>(g.ws + g.lay.ares);
+  int8_t* Bres = reinterpret_cast<int8_t*>(g.ws + g.lay.bres);
+  uint8_t* rt = reinterpret_cast<uint8_t*>(g.ws + g.lay.rt);
+
+  ResidueConsts rc;
+  GemmConsts gc;
+  CrtConsts cc;
+  make_consts(s, q, &rc, &gc, &cc);
+
+  std::array<hipEvent_t, 5> ev{};
+  const bool timed = g.timing && g.events.size() < TIMING_MAX_CALLS;
+  if (timed) {
+    for (auto& x : ev) OZ_CHECK(hipEventCreate(&x));
+    OZ_CHECK(hipEventRecord(ev[0], g.stream));
+  }
+  if ((st = run_scale(m, n, q, A, lda, B, ldb, e, f))) return st;
+  if (timed) OZ_CHECK(hipEventRecord(ev[1], g.stream));
+  OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, g.stream));
+  OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
+  if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, g.stream));
+  if (timed) OZ_CHECK(hipEventRecord(ev[3], g.stream));
+  OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
+  if (timed) {
+    OZ_CHECK(hipEventRecord(ev[4], g.stream));
+    g.events.push_back(ev);
+  }
+  return OZGEMM_OK;
+}
+
+int ozgemm_stage_scale(int m, int n, int q, const double* A, int lda, const double* B, int ldb, int32_t* e,
+                       int32_t* f) {
+  int st = check_common(m, n, q, A, lda, B, ldb);
+  if (st) return st;
+  if (e == nullptr && m > 0) return -8;
+  if (f == nullptr && n > 0) return -9;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > g.max_m || n > g.max_n || q > g.max_q) return OZGEMM_RANGE;
+  return run_scale(m, n, q, A, lda, B, ldb, e, f);
+}
+
+int ozgemm_stage_residue(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb,
+                         const int32_t* e, const int32_t* f, int8_t* Ares, int8_t* Bres, double* Aprime,
+                         double* Bprime) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 1) return -3;
+  if (s < 1 || s > OZGEMM_S_MAX) return -4;
+  if (A == nullptr && m > 0) return -5;
+  if (lda < std::max(1, m)) return -6;
+  if (B == nullptr && n > 0) return -7;
+  if (ldb < std::max(1, q)) return -8;
+  if (e == nullptr) return -9;
+  if (f == nullptr) return -10;
+  if (Ares == nullptr) return -11;
+  if (Bres == nullptr) return -12;
+  int st = check_range(m, n, q, s);
+  if (st) return st;
+  return run_residue(m, n, q, s, A, lda, B, ldb, e, f, Ares, Bres, Aprime, Bprime);
+}
+
+int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8_t* Bres, int32_t* Ct,
+                      uint8_t* rt) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 1) return -3;
+  if (s < 1 || s > OZGEMM_S_MAX) return -4;
+  if (Ares == nullptr) return -5;
+  if (Bres == nullptr) return -6;
+  int st = check_range(m, n, q, s);
+  if (st) return st;
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  ResidueConsts rc;
+  GemmConsts gc;
+  CrtConsts cc;
+  make_consts(s, q, &rc, &gc, &cc);
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, g.stream));
+  return 0;
+}
+
+int ozgemm_stage_crt(int m, int n, int q, int s, const uint8_t* rt, const int32_t* e, const int32_t* f, double* C,
+                     int ldc) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 1) return -3;
+  if (s < 1 || s > OZGEMM_S_MAX) return -4;
+  if (rt == nullptr) return -5;
+  if (e == nullptr) return -6;
+  if (f == nullptr) return -7;
+  if (C == nullptr && m > 0 && n > 0) return -8;
+  if (ldc < std::max(1, m)) return -9;
+  int st = check_range(m, n, q, s);
+  if (st) return st;
+  if (m == 0 || n == 0) return 0;
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  ResidueConsts rc;
+  GemmConsts gc;
+  CrtConsts cc;
+  make_consts(s, q, &rc, &gc, &cc);
+  OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
+  return 0;
+}
+
+int ozgemm_timing(int enable) {
+  for (auto& ev : g.events)
+    for (auto& x : ev) (void)hipEventDestroy(x);
+  g.events.clear();
+  g.timing = enable != 0;
+  return OZGEMM_OK;
+}
+
+int ozgemm_phase_ms(double* ms_out, int* calls) {
+  if (ms_out == nullptr) return -1;
+  for (int p = 0; p < 4; ++p) ms_out[p] = 0.0;
+  for (auto& ev : g.events) {
+    OZ_CHECK(hipEventSynchronize(ev[4]));
+    for (int p = 0; p < 4; ++p) {
+      float ms = 0.f;
+      OZ_CHECK(hipEventElapsedTime(&ms, ev[p], ev[p + 1]));
+      ms_out[p] += ms;
+    }
+  }
+  if (calls) *calls = (int)g.events.size();
+  return OZGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Residue step: truncation to integers and symmetric int8 residues, fused.
+//
+// Ozaki II notes §3: A' = trunc(DA) with D = diag(2^(k - e_i)); §4: one
+// residue matrix per modulus; §6: moduli <= 256 with symmetric residues in
+// [-floor(m/2), ceil(m/2) - 1], which fit signed int8; §15 asks for scaling,
+// truncation, modulo and int8 packing in one kernel, which this is.
+//
+// Each block converts a tile of TR rows x TK inner-dimension entries.  The
+// doubles are staged through LDS so that the global reads are coalesced
+// whatever the source layout (rows contiguous for column-major A, the inner
+// dimension contiguous for column-major B), and every thread then owns 16
+// consecutive inner-dimension entries of one row and writes them as one
+// 16-byte store per modulus into the K-contiguous plane the GEMM reads.
+//
+// Exactness.  a * 2^(k - e) is exact (a power-of-two scaling) unless it
+// falls below 2^-1022, where it is below 1 and truncates to 0 anyway.  For
+// |A'| < 2^53, q = rint(A' * RN(1/m)) is within one of the nearest-integer
+// quotient (relative error <= 2^-52, quotient < 2^53/173), so
+// r = fma(-q, m, A') is the exact small remainder and one +-m correction
+// lands it in the symmetric range.  When k > 53, A' = u * 2^sh with
+// u < 2^53 and A' mod m = (u mod m)(2^sh mod m) mod m.
+#include "oz_internal.h"
+
+namespace oz {
+
+namespace {
+
+constexpr int TR = 32;           // rows per tile
+constexpr int TK = 128;          // inner-dimension entries per tile
+constexpr int LDS_STRIDE = TK + 1;  // doubles; odd stride spreads banks
+
+__device__ __forceinline__ int smod_small(double a, int m, double inv, int lo, int hi) {
+  double qf = __builtin_rint(a * inv);
+  double r = __builtin_fma(-qf, (double)m, a);
+  int ri = (int)r;
+  ri = ri > hi ? ri - m : ri;
+  ri = ri < lo ? ri + m : ri;
+  return ri;
+}
+
+template <bool ROWS_CONTIG, bool BIG>
+__global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
+                                                       long ls, const int32_t* __restrict__ ex, ResidueConsts c,
+                                                       int8_t* __restrict__ planes, long plane_stride, int q_pad,
+                                                       double* __restrict__ prime, long prime_rs, long prime_ls) {
+  __shared__ double tile[TR * LDS_STRIDE];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.y * TR;
+  const int l0 = blockIdx.x * TK;
+
+  // ---- coalesced load into LDS (zero outside the matrix) ----
+  if (ROWS_CONTIG) {
+    // consecutive lanes -> consecutive rows of one column
+    const int r = tid & (TR - 1);
+    const int lsub = tid >> 5;  // 0..7
+    const bool rok = (r0 + r) < rows;
+#pragma unroll
+    for (int it = 0; it < TK / 8; ++it) {
+      const int l = lsub + 8 * it;
+      double v = 0.0;
+      if (rok && (l0 + l) < q) v = __builtin_nontemporal_load(X + (long)(r0 + r) + (long)(l0 + l) * ls);
+      tile[r * LDS_STRIDE + l] = v;
+    }
+  } else {
+    // consecutive lanes -> consecutive inner-dimension entries of one row
+    const int l = tid & (TK - 1);
+    const int rsub = tid >> 7;  // 0..1
+    const bool lok = (l0 + l) < q;
+#pragma unroll
+    for (int it = 0; it < TR / 2; ++it) {
+      const int r = rsub + 2 * it;
+      double v = 0.0;
+      if (lok && (r0 + r) < rows) v = __builtin_nontemporal_load(X + (long)(r0 + r) * rs + (long)(l0 + l));
+      tile[r * LDS_STRIDE + l] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- each thread: one row, 16 consecutive entries ----
+  const int r = tid >> 3;          // 0..31
+  const int cseg = (tid & 7) * 16; // 0..112
+  const int grow = r0 + r;
+  int e = 0;
+  bool zero_row = true;
+  if (grow < rows) {
+    e = ex[grow];
+    zero_row = (e == OZGEMM_EXP_NONFINITE);
+  }
+  const int shift = zero_row ? 0 : c.k - e;
+
+  double a[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    double x = tile[r * LDS_STRIDE + cseg + j];
+    double t = __builtin_trunc(__builtin_ldexp(x, shift));
+    a[j] = zero_row ? 0.0 : t + 0.0;  // + 0.0 turns -0.0 into +0.0
+  }
+
+  if (prime != nullptr && grow < rows) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int gl = l0 + cseg + j;
+      if (gl < q) prime[(long)grow * prime_rs + (long)gl * prime_ls] = a[j];
+    }
+  }
+
+  int sh[16];
+  if (BIG) {
+    // A' = u * 2^sh with |u| < 2^53 (sh = 0 when |A'| < 2^53)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ebits = (int)(((uint64_t)__double_as_longlong(a[j]) >> 52) & 0x7ff) - 1023;
+      sh[j] = max(0, ebits - 52);
+      a[j] = __builtin_ldexp(a[j], -sh[j]);
+    }
+  }
+
+  int8_t* dst = planes + (long)grow * q_pad + l0 + cseg;
+  for (int t = 0; t < c.s; ++t) {
+    const int m = c.m[t];
+    const double inv = c.inv[t];
+    const int lo = c.lo[t], hi = c.hi[t];
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int ri = smod_small(a[j], m, inv, lo, hi);
+      if (BIG) {
+        int v = ri * (int)c.pow2[t][sh[j]];
+        v = v % m;  // in (-m, m)
+        v = v > hi ? v - m : v;
+        v = v < lo ? v + m : v;
+        ri = v;
+      }
+      packed[j >> 2] |= ((uint32_t)ri & 0xffu) << (8 * (j & 3));
+    }
+    uint4 out;
+    out.x = packed[0];
+    out.y = packed[1];
+    out.z = packed[2];
+    out.w = packed[3];
+    *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
+                          const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad, double* prime,
+                          long prime_rs, long prime_ls, hipStream_t st) {
+  dim3 grid(q_pad / TK, rows_pad / TR);
+  const long plane_stride = (long)rows_pad * q_pad;
+  const bool rows_contig = (rs == 1);
+  if (rows_contig) {
+    if (c.big)
+      hipLaunchKernelGGL((residue_kernel<true, true>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
+                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+    else
+      hipLaunchKernelGGL((residue_kernel<true, false>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
+                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+  } else {
+    if (c.big)
+      hipLaunchKernelGGL((residue_kernel<false, true>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
+                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+    else
+      hipLaunchKernelGGL((residue_kernel<false, false>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
+                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oz

@@ -1,0 +1,111 @@
+// Scale step: per-row exponents of A and per-column exponents of B.
+//
+// Ozaki II notes §3: D and E are diagonal powers of two; §5: keeping k bits
+// needs |a_il 2^(k - e_i)| < 2^k.  e_i is the frexp exponent of the row
+// maximum: 2^(e_i - 1) <= max_l |a_il| < 2^e_i.
+//
+// The maxima are taken on the IEEE bit patterns with the sign cleared: for
+// non-negative doubles the unsigned integer order is the numeric order, and
+// Inf/NaN patterns (>= 0x7ff0...) sort above every finite value, so a
+// non-finite row is recognised from its maximum alone.
+//
+// A is column-major, so a row is strided: one thread per row walks a chunk of
+// columns (consecutive threads read consecutive rows -> coalesced), the
+// chunks are combined by a second small kernel.  A column of B is
+// contiguous: one wavefront per column, then a cross-lane reduction.
+#include "oz_internal.h"
+
+namespace oz {
+
+__device__ __forceinline__ uint64_t abs_bits(double x) {
+  return (uint64_t)__double_as_longlong(x) & 0x7fffffffffffffffull;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// frexp exponent of the double whose |.| bit pattern is b.
+__device__ __forceinline__ int32_t exponent_of_bits(uint64_t b) {
+  if (b == 0) return 0;
+  if (b >= 0x7ff0000000000000ull) return OZGEMM_EXP_NONFINITE;
+  int biased = (int)(b >> 52);
+  if (biased > 0) return biased - 1022;         // value in [2^(E-1023), 2^(E-1022))
+  int top = 63 - __clzll((long long)b);          // subnormal: mant * 2^-1074
+  return top - 1073;
+}
+
+__global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __restrict__ A, int m, int q,
+                                                               long lda, int chunk,
+                                                               uint64_t* __restrict__ pmax, int m_stride) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int l0 = blockIdx.y * chunk;
+  const int l1 = min(q, l0 + chunk);
+  uint64_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  if (i < m) {
+    const double* p = A + i + (long)l0 * lda;
+    int l = l0;
+    for (; l + 4 <= l1; l += 4) {
+      v0 = umax64(v0, abs_bits(__builtin_nontemporal_load(p)));
+      v1 = umax64(v1, abs_bits(__builtin_nontemporal_load(p + lda)));
+      v2 = umax64(v2, abs_bits(__builtin_nontemporal_load(p + 2 * lda)));
+      v3 = umax64(v3, abs_bits(__builtin_nontemporal_load(p + 3 * lda)));
+      p += 4 * lda;
+    }
+    for (; l < l1; ++l) {
+      v0 = umax64(v0, abs_bits(*p));
+      p += lda;
+    }
+  }
+  pmax[(long)blockIdx.y * m_stride + i] = umax64(umax64(v0, v1), umax64(v2, v3));
+}
+
+__global__ __launch_bounds__(256) void row_exp_finalize_kernel(const uint64_t* __restrict__ pmax, int m,
+                                                                int m_stride, int nchunks,
+                                                                int32_t* __restrict__ e) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= m) return;
+  uint64_t v = 0;
+  for (int c = 0; c < nchunks; ++c) v = umax64(v, pmax[(long)c * m_stride + i]);
+  e[i] = exponent_of_bits(v);
+}
+
+__global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__ B, int q, int n, long ldb,
+                                                       int32_t* __restrict__ f) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= n) return;  // whole wavefront exits together
+  const double* col = B + (long)j * ldb;
+  uint64_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  int l = lane;
+  for (; l + 192 < q; l += 256) {
+    v0 = umax64(v0, abs_bits(__builtin_nontemporal_load(col + l)));
+    v1 = umax64(v1, abs_bits(__builtin_nontemporal_load(col + l + 64)));
+    v2 = umax64(v2, abs_bits(__builtin_nontemporal_load(col + l + 128)));
+    v3 = umax64(v3, abs_bits(__builtin_nontemporal_load(col + l + 192)));
+  }
+  for (; l < q; l += 64) v0 = umax64(v0, abs_bits(col[l]));
+  uint64_t v = umax64(umax64(v0, v1), umax64(v2, v3));
+  for (int off = 32; off > 0; off >>= 1) v = umax64(v, (uint64_t)__shfl_xor((unsigned long long)v, off, 64));
+  if (lane == 0) f[j] = exponent_of_bits(v);
+}
+
+hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,
+                                  int nchunks, hipStream_t st) {
+  const int chunk = (q + nchunks - 1) / nchunks;
+  dim3 grid((m + 255) / 256, nchunks);
+  hipLaunchKernelGGL(row_max_partial_kernel, grid, dim3(256), 0, st, A, m, q, (long)lda, chunk, pmax, m_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(row_exp_finalize_kernel, dim3((m + 255) / 256), dim3(256), 0, st, pmax, m, m_stride, nchunks,
+                     e);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st) {
+  hipLaunchKernelGGL(col_exp_kernel, dim3((n + 3) / 4), dim3(256), 0, st, B, q, n, (long)ldb, f);
+  return hipGetLastError();
+}
+
+}  // namespace oz

@@ -1,0 +1,207 @@
+"""ctypes binding of ``libozgemm.so`` (the C-ABI declared in ``include/ozgemm.h``).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers, ``None`` becomes NULL, the stream defaults to torch's
+current stream.  Every step of the computation runs in the HIP library; if
+the library is missing this module raises instead of computing anything.
+
+A non-zero status raises :class:`OzgemmError` (with ``ozgemm_strerror``'s
+text) unless the function is documented to return a value.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libozgemm.so")
+
+OZGEMM_OK = 0
+OZGEMM_NOT_CONFIGURED = 1
+OZGEMM_RANGE = 2
+OZGEMM_WORKSPACE_TOO_SMALL = 3
+OZGEMM_HIP_ERROR = 4
+OZGEMM_S_MAX = 20
+OZGEMM_Q_LIMIT = 1 << 17
+OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
+
+#: every symbol the header declares
+EXPORTS = (
+    "ozgemm_workspace_bytes", "ozgemm_config", "ozgemm_set_stream", "ozgemm_free", "ozgemm_strerror",
+    "ozgemm_dgemm", "ozgemm_moduli", "ozgemm_kbits", "ozgemm_plane_dims", "ozgemm_stage_scale",
+    "ozgemm_stage_residue", "ozgemm_stage_gemm", "ozgemm_stage_crt", "ozgemm_timing", "ozgemm_phase_ms",
+)
+
+_lib = None
+_workspace = None  # keeps a library-config workspace tensor alive
+
+
+class OzgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {ozgemm_strerror(status)}")
+
+
+def lib():
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fp64_gemm_emulation_ozii_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "ozgemm_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
+        "ozgemm_config": (c_int, [c_int, c_int, c_int, c_int, vp, vp, c_size]),
+        "ozgemm_set_stream": (c_int, [vp]),
+        "ozgemm_free": (c_int, []),
+        "ozgemm_strerror": (ctypes.c_char_p, [c_int]),
+        "ozgemm_dgemm": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, c_int, c_int]),
+        "ozgemm_moduli": (c_int, [c_int, ip]),
+        "ozgemm_kbits": (c_int, [c_int, c_int]),
+        "ozgemm_plane_dims": (c_int, [c_int, c_int, c_int, ip, ip, ip]),
+        "ozgemm_stage_scale": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp]),
+        "ozgemm_stage_residue": (c_int, [c_int, c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp, vp, vp, vp, vp]),
+        "ozgemm_stage_gemm": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp]),
+        "ozgemm_stage_crt": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_int]),
+        "ozgemm_timing": (c_int, [c_int]),
+        "ozgemm_phase_ms": (c_int, [ctypes.POINTER(ctypes.c_double), ip]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _ptr(x):
+    """Device pointer of a tensor, an int address, or None (NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(status: int, where: str) -> int:
+    if status != OZGEMM_OK:
+        raise OzgemmError(status, where)
+    return status
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# --------------------------------------------------------------------------
+# host-only
+# --------------------------------------------------------------------------
+
+def ozgemm_strerror(status: int) -> str:
+    return lib().ozgemm_strerror(status).decode()
+
+
+def ozgemm_workspace_bytes(max_m: int, max_n: int, max_q: int, s_max: int) -> int:
+    return int(lib().ozgemm_workspace_bytes(max_m, max_n, max_q, s_max))
+
+
+def ozgemm_moduli(s: int) -> list[int]:
+    buf = (ctypes.c_int * max(s, 1))()
+    _check(lib().ozgemm_moduli(s, buf), "ozgemm_moduli")
+    return list(buf)[:s]
+
+
+def ozgemm_kbits(s: int, q: int) -> int:
+    """Returns k (negative when no bits are left); never raises."""
+    return int(lib().ozgemm_kbits(s, q))
+
+
+def ozgemm_plane_dims(m: int, n: int, q: int):
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().ozgemm_plane_dims(m, n, q, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "ozgemm_plane_dims")
+    return a.value, b.value, c.value
+
+
+# --------------------------------------------------------------------------
+# configuration
+# --------------------------------------------------------------------------
+
+def ozgemm_config(s_max: int, max_m: int, max_n: int, max_q: int, stream=None, workspace=None,
+                  workspace_bytes: int | None = None) -> int:
+    """Configure the library.  With ``workspace=None`` a torch uint8 device
+    tensor of ``ozgemm_workspace_bytes(...)`` bytes is allocated and kept
+    alive here."""
+    global _workspace
+    need = ozgemm_workspace_bytes(max_m, max_n, max_q, s_max)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        workspace_bytes = need
+    elif workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().ozgemm_config(s_max, max_m, max_n, max_q, _stream(stream), _ptr(workspace), workspace_bytes)
+    _check(st, "ozgemm_config")
+    _workspace = workspace
+    return st
+
+
+def ozgemm_set_stream(stream=None) -> int:
+    return _check(lib().ozgemm_set_stream(_stream(stream)), "ozgemm_set_stream")
+
+
+def ozgemm_free() -> int:
+    global _workspace
+    st = lib().ozgemm_free()
+    _workspace = None
+    return st
+
+
+# --------------------------------------------------------------------------
+# compute (raw C-ABI signatures; matrices are column-major device buffers)
+# --------------------------------------------------------------------------
+
+def ozgemm_dgemm(m, n, q, A, lda, B, ldb, C, ldc, s, check: bool = True) -> int:
+    st = lib().ozgemm_dgemm(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, s)
+    return _check(st, "ozgemm_dgemm") if check else st
+
+
+def ozgemm_stage_scale(m, n, q, A, lda, B, ldb, e, f, check: bool = True) -> int:
+    st = lib().ozgemm_stage_scale(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(e), _ptr(f))
+    return _check(st, "ozgemm_stage_scale") if check else st
+
+
+def ozgemm_stage_residue(m, n, q, s, A, lda, B, ldb, e, f, Ares, Bres, Aprime=None, Bprime=None,
+                         check: bool = True) -> int:
+    st = lib().ozgemm_stage_residue(m, n, q, s, _ptr(A), lda, _ptr(B), ldb, _ptr(e), _ptr(f), _ptr(Ares),
+                                    _ptr(Bres), _ptr(Aprime), _ptr(Bprime))
+    return _check(st, "ozgemm_stage_residue") if check else st
+
+
+def ozgemm_stage_gemm(m, n, q, s, Ares, Bres, Ct=None, rt=None, check: bool = True) -> int:
+    st = lib().ozgemm_stage_gemm(m, n, q, s, _ptr(Ares), _ptr(Bres), _ptr(Ct), _ptr(rt))
+    return _check(st, "ozgemm_stage_gemm") if check else st
+
+
+def ozgemm_stage_crt(m, n, q, s, rt, e, f, C, ldc, check: bool = True) -> int:
+    st = lib().ozgemm_stage_crt(m, n, q, s, _ptr(rt), _ptr(e), _ptr(f), _ptr(C), ldc)
+    return _check(st, "ozgemm_stage_crt") if check else st
+
+
+def ozgemm_timing(enable: bool) -> int:
+    return _check(lib().ozgemm_timing(1 if enable else 0), "ozgemm_timing")
+
+
+def ozgemm_phase_ms():
+    """Returns ([scale, residue, gemm, crt] total milliseconds, calls)."""
+    buf = (ctypes.c_double * 4)()
+    calls = ctypes.c_int()
+    _check(lib().ozgemm_phase_ms(buf, ctypes.byref(calls)), "ozgemm_phase_ms")
+    return list(buf), calls.value

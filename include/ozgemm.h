@@ -1,0 +1,177 @@
+/*
+ * ozgemm -- FP64 matrix multiplication C = A B emulated with exact
+ * INT8 x INT8 -> INT32 matrix products (Ozaki Scheme II), for AMD MI355X
+ * (gfx950).
+ *
+ * Method: the web page "Ozaki Scheme II：用 CRT 把高精度 GEMM 映射成少量 INT8
+ * GEMM" (chatdocs.ruinique.com/nla/ozaki-scheme-ii), cited below as
+ * "Ozaki II notes §n".  Its §7 lists the pipeline this library runs:
+ *   1. bit budget k from M = prod m_t and the inner dimension q (§5);
+ *   2. power-of-two row/column scalings D, E and truncation to integer
+ *      matrices A' = trunc(DA), B' = trunc(BE) (§3);
+ *   3. for each of s pairwise-coprime moduli m_t <= 256: symmetric int8
+ *      residues of A' and B', one exact int8 GEMM, product mod m_t (§4, §6);
+ *   4-5. CRT accumulation and reduction to the symmetric representative (§4, §5);
+ *   6. unscaling by D^-1 and E^-1 (§7).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are column-major (BLAS convention): A is m x q with leading
+ *    dimension lda >= max(1, m); B is q x n, ldb >= max(1, q); C is m x n,
+ *    ldc >= max(1, m).  No alpha/beta: C is overwritten.  A caller holding
+ *    row-major data passes (B^T, A^T) and receives C^T.
+ *  - Every pointer argument that names matrix data is DEVICE memory owned by
+ *    the caller; the library never allocates, frees or retains it.
+ *  - Work is enqueued on the configured HIP stream and the calls return
+ *    without synchronising (like BLAS on a GPU).  The caller synchronises.
+ *  - Return value: 0 on success.  -i means argument i (1-based) is invalid;
+ *    positive values are the OZGEMM_* codes below.  Arguments are checked
+ *    before anything is enqueued, so outputs are untouched on any error.
+ *  - The library keeps one global configuration; it is not thread-safe and
+ *    calls that overlap on one stream-set race on the workspace.
+ *  - s, the number of moduli, is 1..OZGEMM_S_MAX; the moduli are the first s
+ *    of the greedy pairwise-coprime sequence 256, 255, 253, 251, 247, 241,
+ *    239, 233, 229, 227, 223, 217, 211, 199, 197, 193, 191, 181, 179, 173.
+ *  - The inner dimension must satisfy q < 2^17 so that every int8 dot
+ *    product (|.| <= q * 2^14) is exact in int32 (Ozaki II notes §6), and s
+ *    must leave k >= 1 bits (§5); otherwise OZGEMM_RANGE.
+ *  - Numerics: the result equals X * 2^(e_i + f_j - 2k) rounded once to
+ *    nearest-even, where X = (A'B')_ij exactly.  Rows of A / columns of B that
+ *    hold Inf or NaN make the outputs they touch NaN; all-zero rows/columns
+ *    give +0; results beyond the double range round to +-Inf.
+ */
+#ifndef OZGEMM_H
+#define OZGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OZGEMM_OK                  0
+#define OZGEMM_NOT_CONFIGURED      1  /* ozgemm_config has not succeeded */
+#define OZGEMM_RANGE               2  /* q >= 2^17, or k(s, q) < 1, or size beyond the configured maximum */
+#define OZGEMM_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below ozgemm_workspace_bytes(...) */
+#define OZGEMM_HIP_ERROR           4  /* a HIP call failed; ozgemm_strerror(4) names it */
+
+#define OZGEMM_S_MAX 20               /* largest supported number of moduli */
+#define OZGEMM_Q_LIMIT (1 << 17)      /* q must be below this (Ozaki II notes §6) */
+#define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
+
+/* ---------------------------------------------------------------------- */
+/* Configuration                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace needed for problems up to max_m x max_n x max_q
+ * with up to s_max moduli (the per-modulus int8 residue planes of A and B,
+ * the uint8 product residues and small per-row/column arrays).  Returns 0
+ * for invalid arguments.  Host only. */
+size_t ozgemm_workspace_bytes(int max_m, int max_n, int max_q, int s_max);
+
+/* Record the maximum problem size, the HIP stream (a hipStream_t, may be
+ * NULL for the null stream) and a caller-owned device workspace of
+ * workspace_bytes bytes.  Nothing is allocated or launched.  Replaces any
+ * previous configuration.  Errors: -1..-4 bad sizes, -6 NULL workspace,
+ * OZGEMM_WORKSPACE_TOO_SMALL. */
+int ozgemm_config(int s_max, int max_m, int max_n, int max_q,
+                  void *hip_stream, void *workspace, size_t workspace_bytes);
+
+/* Change the stream used by later calls. */
+int ozgemm_set_stream(void *hip_stream);
+
+/* Forget the configuration (the workspace stays the caller's). */
+int ozgemm_free(void);
+
+/* Text for a status code; for OZGEMM_HIP_ERROR it includes the HIP error. */
+const char *ozgemm_strerror(int status);
+
+/* ---------------------------------------------------------------------- */
+/* The hot path                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* C <- A B by Ozaki Scheme II with s moduli (Ozaki II notes §7).
+ * m, n, q >= 0; m = 0 or n = 0 does nothing; q = 0 writes C = 0.
+ * C must not overlap A or B (-8).  Requires m <= max_m, n <= max_n,
+ * q <= max_q, s <= s_max of the configuration (OZGEMM_RANGE otherwise).
+ * Enqueues four kernels (scale, residue, int8 GEMM, CRT) on the stream. */
+int ozgemm_dgemm(int m, int n, int q,
+                 const double *A, int lda, const double *B, int ldb,
+                 double *C, int ldc, int s);
+
+/* ---------------------------------------------------------------------- */
+/* Host-only introspection (no device needed)                              */
+/* ---------------------------------------------------------------------- */
+
+/* Write the first s moduli to moduli_out[0..s-1].  Returns 0 or -1. */
+int ozgemm_moduli(int s, int *moduli_out);
+
+/* k = floor(1/2 log2((M/2 - 1)/q)) for the first s moduli, evaluated with
+ * exact integers (Ozaki II notes §5).  Returns k (>= 1) or a negative value
+ * when s and q leave no bits or q >= 2^17. */
+int ozgemm_kbits(int s, int q);
+
+/* Padded dimensions of the stage buffers below: rows of the residue planes
+ * are padded to *m_pad / *n_pad, the inner dimension to *q_pad. */
+int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
+
+/* ---------------------------------------------------------------------- */
+/* Stage entry points (the same kernels ozgemm_dgemm runs), for parity     */
+/* checks of each integer stage.  All buffers are caller-owned device      */
+/* memory; the configured workspace and stream are used.                   */
+/* ---------------------------------------------------------------------- */
+
+/* Exponents (Ozaki II notes §3, §5): e[i] for i < m with
+ * 2^(e_i - 1) <= max_l |a_il| < 2^e_i (0 for an all-zero row,
+ * OZGEMM_EXP_NONFINITE for a row holding Inf/NaN); f[j] likewise for the
+ * columns of B.  e has m entries, f has n. */
+int ozgemm_stage_scale(int m, int n, int q,
+                       const double *A, int lda, const double *B, int ldb,
+                       int32_t *e, int32_t *f);
+
+/* Truncation and residues (Ozaki II notes §3, §4, §6), with k = kbits(s, q):
+ *   A'_il = trunc(a_il 2^(k - e_i)),  B'_lj = trunc(b_lj 2^(k - f_j)),
+ *   Ares[t][i][l] = smod(A'_il, m_t),  Bres[t][j][l] = smod(B'_lj, m_t),
+ * smod(x, m) in [-floor(m/2), ceil(m/2) - 1].  Planes are int8, K-contiguous:
+ * Ares at t*m_pad*q_pad + i*q_pad + l, Bres at t*n_pad*q_pad + j*q_pad + l,
+ * zero in the padding.  Aprime (m x q, ld m) and Bprime (q x n, ld q) are
+ * optional (NULL to skip) float64 copies of A' and B'. */
+int ozgemm_stage_residue(int m, int n, int q, int s,
+                         const double *A, int lda, const double *B, int ldb,
+                         const int32_t *e, const int32_t *f,
+                         int8_t *Ares, int8_t *Bres,
+                         double *Aprime, double *Bprime);
+
+/* Per-modulus products (Ozaki II notes §4, §6): C_t = A_t B_t^T over q_pad,
+ * exact in int32.  Ct (optional, NULL to skip) receives int32 planes,
+ * column-major with ld m_pad: Ct[t*m_pad*n_pad + j*m_pad + i].  rt
+ * (optional) receives C_t mod m_t in [0, m_t) as uint8 in the same layout. */
+int ozgemm_stage_gemm(int m, int n, int q, int s,
+                      const int8_t *Ares, const int8_t *Bres,
+                      int32_t *Ct, uint8_t *rt);
+
+/* CRT reconstruction, range reduction and unscaling (Ozaki II notes §4, §5,
+ * §7): from rt (layout of ozgemm_stage_gemm), e and f, write the m x n result
+ * C (ld ldc). */
+int ozgemm_stage_crt(int m, int n, int q, int s,
+                     const uint8_t *rt, const int32_t *e, const int32_t *f,
+                     double *C, int ldc);
+
+/* ---------------------------------------------------------------------- */
+/* Phase timing                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* enable != 0: every later ozgemm_dgemm records HIP events on the stream
+ * around its four phases.  ozgemm_phase_ms adds, over the calls since timing
+ * was enabled, the milliseconds of [scale, residue, gemm, crt] into
+ * ms_out[0..3] (synchronising on the events) and the number of calls into
+ * *calls.  Disabling discards the events. */
+int ozgemm_timing(int enable);
+int ozgemm_phase_ms(double *ms_out, int *calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OZGEMM_H */

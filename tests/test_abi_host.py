@@ -1,0 +1,148 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load and export every function ``include/ozgemm.h``
+declares; the host-only entry points (moduli, bit budget, workspace and
+plane sizes, argument validation) must agree with the oracle and the header.
+No call here reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import ozaki2 as oz
+from fp64_gemm_emulation_ozii_amd import ozgemm as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ozgemm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libozgemm.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ozgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_lists():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("s", range(1, 21))
+def test_moduli_match_oracle(s):
+    assert L.ozgemm_moduli(s) == oz.greedy_moduli(s)
+
+
+def test_moduli_rejects_bad_s():
+    with pytest.raises(L.OzgemmError):
+        L.ozgemm_moduli(0)
+    with pytest.raises(L.OzgemmError):
+        L.ozgemm_moduli(21)
+
+
+@pytest.mark.parametrize("q", [1, 2, 3, 63, 64, 65, 127, 1000, 1024, 4096, 8192, 16384, 65536, 2**17 - 1])
+def test_kbits_match_oracle(q):
+    for s in range(1, 21):
+        M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+        want = oz.kbits(M, q)
+        got = L.ozgemm_kbits(s, q)
+        if want < 0:
+            assert got < 0
+        else:
+            assert got == want, (s, q)
+
+
+def test_kbits_rejects_q_limit():
+    assert L.ozgemm_kbits(14, 2**17) < 0
+
+
+def test_workspace_and_plane_dims():
+    mp, np_, qp = L.ozgemm_plane_dims(300, 257, 1000)
+    assert mp % 256 == 0 and mp >= 300 and np_ % 256 == 0 and np_ >= 257 and qp % 128 == 0 and qp >= 1000
+    small = L.ozgemm_workspace_bytes(64, 64, 64, 14)
+    big = L.ozgemm_workspace_bytes(8192, 8192, 8192, 14)
+    assert 0 < small < big
+    # the residue planes alone: s (m_pad + n_pad) q_pad, plus s m_pad n_pad product residues
+    assert big >= 14 * (8192 + 8192) * 8192 + 14 * 8192 * 8192
+    assert L.ozgemm_workspace_bytes(64, 64, 64, 0) == 0
+    assert L.ozgemm_workspace_bytes(64, 64, 64, 21) == 0
+
+
+def test_strerror_texts():
+    assert "argument 3" in L.ozgemm_strerror(-3)
+    assert "config" in L.ozgemm_strerror(L.OZGEMM_NOT_CONFIGURED)
+    assert "2^17" in L.ozgemm_strerror(L.OZGEMM_RANGE)
+
+
+FAKE = 1 << 40  # a non-NULL address that no validation path dereferences
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# Every call below must return from argument validation.  As a guard against a
+# regression that would let one reach a kernel launch with these fake
+# addresses, the validation tests only run where no GPU is visible.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation runs only without a GPU")
+
+
+@no_gpu_only
+def test_validation_before_any_launch():
+    lib = L.lib()
+    lib.ozgemm_free()
+    assert lib.ozgemm_dgemm(8, 8, 8, FAKE, 8, FAKE, 8, FAKE + (1 << 30), 8, 14) == L.OZGEMM_NOT_CONFIGURED
+    ws = L.ozgemm_workspace_bytes(512, 512, 512, 16)
+    assert lib.ozgemm_config(16, 512, 512, 512, None, FAKE, ws - 1) == L.OZGEMM_WORKSPACE_TOO_SMALL
+    assert lib.ozgemm_config(0, 512, 512, 512, None, FAKE, ws) == -1
+    assert lib.ozgemm_config(16, -1, 512, 512, None, FAKE, ws) == -2
+    assert lib.ozgemm_config(16, 512, 512, 2**17, None, FAKE, ws) == -4
+    assert lib.ozgemm_config(16, 512, 512, 512, None, None, ws) == -6
+    assert lib.ozgemm_config(16, 512, 512, 512, None, FAKE, ws) == 0
+    Cp = FAKE + (1 << 30)
+    d = lib.ozgemm_dgemm
+    assert d(-1, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 14) == -1
+    assert d(8, -1, 8, FAKE, 8, FAKE, 8, Cp, 8, 14) == -2
+    assert d(8, 8, -1, FAKE, 8, FAKE, 8, Cp, 8, 14) == -3
+    assert d(8, 8, 8, None, 8, FAKE, 8, Cp, 8, 14) == -4
+    assert d(8, 8, 8, FAKE, 7, FAKE, 8, Cp, 8, 14) == -5
+    assert d(8, 8, 8, FAKE, 8, None, 8, Cp, 8, 14) == -6
+    assert d(8, 8, 8, FAKE, 8, FAKE, 7, Cp, 8, 14) == -7
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, None, 8, 14) == -8
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 7, 14) == -9
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 0) == -10
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 21) == -10
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 17) == L.OZGEMM_RANGE        # s above s_max
+    assert d(513, 8, 8, FAKE, 513, FAKE, 8, Cp, 513, 14) == L.OZGEMM_RANGE  # m above max_m
+    assert d(8, 8, 600, FAKE, 8, FAKE, 600, Cp, 8, 14) == L.OZGEMM_RANGE    # q above max_q
+    assert d(8, 8, 64, FAKE, 8, FAKE, 64, Cp, 8, 1) == L.OZGEMM_RANGE       # s = 1 leaves k < 1
+    # C overlapping A
+    assert d(8, 8, 8, FAKE, 8, FAKE + (1 << 20), 8, FAKE + 64, 8, 14) == -8
+    # empty problems return before touching memory
+    assert d(0, 8, 8, FAKE, 1, FAKE, 8, Cp, 1, 14) == 0
+    assert d(8, 0, 8, FAKE, 8, FAKE, 8, Cp, 8, 14) == 0
+    lib.ozgemm_free()
+
+
+@no_gpu_only
+def test_config_rejects_q_limit_and_stage_checks():
+    lib = L.lib()
+    ws = L.ozgemm_workspace_bytes(256, 256, 256, 14)
+    assert lib.ozgemm_config(14, 256, 256, 256, None, FAKE, ws) == 0
+    assert lib.ozgemm_stage_gemm(8, 8, 0, 14, FAKE, FAKE, None, None) == -3
+    assert lib.ozgemm_stage_gemm(8, 8, 8, 15, FAKE, FAKE, None, None) == L.OZGEMM_RANGE
+    assert lib.ozgemm_stage_crt(8, 8, 8, 14, None, FAKE, FAKE, FAKE, 8) == -5
+    assert lib.ozgemm_stage_residue(8, 8, 8, 14, FAKE, 8, FAKE, 8, FAKE, FAKE, None, FAKE, None, None) == -11
+    lib.ozgemm_free()

@@ -1,0 +1,67 @@
+"""GPU parity at full problem sizes, in the launch configuration the
+benchmark times (ozgemm_dgemm with s = 14).
+
+The oracle cannot run these whole, so each test checks (a) every row and
+column exponent against the oracle, and (b) a block of output entries --
+random rows and columns plus the first/last rows and columns and rows/columns
+of the last output tile -- against the oracle evaluated on exactly those rows
+of A and columns of B (the entries only depend on them).
+"""
+import numpy as np
+import pytest
+
+from oracle import ozaki2 as oz
+from fp64_gemm_emulation_ozii_amd import ozgemm as L
+from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
+
+from gpu_util import dev_colmajor, log, same_doubles, within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_lines(size: int, count: int, seed: int, tile: int = 256):
+    rng = np.random.default_rng(seed)
+    picks = set(int(v) for v in rng.integers(0, size, size=count))
+    last0 = (size - 1) // tile * tile
+    picks |= {0, size - 1, last0, min(size - 1, last0 + 1)}
+    picks |= set(int(v) for v in rng.integers(last0, size, size=4))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+@pytest.mark.parametrize("m,q,n,phi", [
+    (4096, 4096, 4096, 1.0),
+    (8192, 8192, 8192, 1.0),
+    (16384, 1024, 16384, 1.0),
+    (1024, 65536, 1024, 1.0),
+    (16384, 16384, 16384, 4.0),
+])
+def test_sampled_block_and_exponents(m, q, n, phi):
+    import torch
+    s = 14
+    log(f"large m={m} q={q} n={n} phi={phi}: generate")
+    A, B = hpl_like(m, q, n, phi, seed=0)
+    L.ozgemm_config(s, m, n, q)
+    Ad = dev_colmajor(A)
+    Bd = dev_colmajor(B)
+    Cd = torch.empty((n, m), dtype=torch.float64, device="cuda")
+    log("  ozgemm_dgemm")
+    L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+    e = torch.empty(m, dtype=torch.int32, device="cuda")
+    f = torch.empty(n, dtype=torch.int32, device="cuda")
+    L.ozgemm_stage_scale(m, n, q, Ad, m, Bd, q, e, f)
+    torch.cuda.synchronize()
+    rows = sample_lines(m, 56, seed=1)
+    cols = sample_lines(n, 56, seed=2)
+    Cg = Cd[torch.from_numpy(cols).cuda()][:, torch.from_numpy(rows).cuda()].cpu().numpy().T
+    eg = e.cpu().numpy()
+    fg = f.cpu().numpy()
+    del Ad, Bd, Cd
+    L.ozgemm_free()
+    torch.cuda.empty_cache()
+    log("  oracle exponents")
+    assert np.array_equal(eg, oz.row_exponents(A))
+    assert np.array_equal(fg, oz.col_exponents(B))
+    log(f"  oracle block {len(rows)}x{len(cols)}")
+    ref = oz.dgemm_block(A, B, s, rows, cols)
+    assert within_tolerance(Cg, ref, A[rows, :], B[:, cols])
+    assert same_doubles(Cg, ref)

@@ -1,0 +1,173 @@
+"""GPU parity: every stage of the HIP path against the oracle.
+
+Integer stages (exponents, A', B', int8 residue planes, int32 products,
+product residues) must match bit for bit; the FP64 result must lie within
+2^-50 (|A||B|)_ij of the oracle's correctly rounded value (the north-star
+tolerance) and, because the CRT kernel also rounds once to nearest, is
+expected to match it bit for bit as well.
+"""
+import numpy as np
+import pytest
+
+from oracle import ozaki2 as oz
+from fp64_gemm_emulation_ozii_amd import ozgemm as L
+from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like, integer_valued
+
+from gpu_util import configure, first_diff, log, run_dgemm, run_stages, same_doubles, within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def small_config():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    configure(1536, 1536, 1536, 20)
+    yield
+    L.ozgemm_free()
+
+
+def check_all_stages(A, B, s, g, ref=None):
+    """Compare every stage of run_stages output g with the oracle."""
+    C_ref, st = ref if ref is not None else oz.dgemm(A, B, s, stages=True)
+    m, q = A.shape
+    n = B.shape[1]
+    assert np.array_equal(g["e"], st["e"]), first_diff(g["e"], st["e"])
+    assert np.array_equal(g["f"], st["f"]), first_diff(g["f"], st["f"])
+    if "Ap" in g:
+        assert np.array_equal(g["Ap"], st["Ap"]), first_diff(g["Ap"], st["Ap"])
+        assert np.array_equal(g["Bp"], st["Bp"]), first_diff(g["Bp"], st["Bp"])
+    assert np.array_equal(g["Ares"], st["Ares"]), first_diff(g["Ares"], st["Ares"])
+    assert np.array_equal(g["Bres"], st["Bres"]), first_diff(g["Bres"], st["Bres"])
+    # the padding of the planes is zero
+    assert not g["Ares_full"][:, m:, :].any() and not g["Ares_full"][:, :, q:].any()
+    assert not g["Bres_full"][:, n:, :].any() and not g["Bres_full"][:, :, q:].any()
+    if "Ct" in g:
+        assert np.array_equal(g["Ct"], st["Ct"]), first_diff(g["Ct"], st["Ct"])
+    assert np.array_equal(g["rt"], st["rt"]), first_diff(g["rt"], st["rt"])
+    assert within_tolerance(g["C"], C_ref, A, B)
+    assert same_doubles(g["C"], C_ref), first_diff(g["C"], C_ref)
+
+
+def test_tiny_64_cube_s14_all_stages():
+    """64 x 64 x 64, HPL-like phi = 0.5, seed 0, s = 14."""
+    A, B = hpl_like(64, 64, 64, 0.5, seed=0)
+    log("tiny 64^3 s=14")
+    check_all_stages(A, B, 14, run_stages(A, B, 14))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (7, 13, 5), (65, 127, 129), (129, 65, 1280), (300, 257, 1000),
+                                   (33, 500, 2), (256, 256, 128), (257, 255, 129)])
+@pytest.mark.parametrize("s", [8, 14])
+def test_ragged_shapes(shape, s):
+    m, q, n = shape
+    M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+    if oz.kbits(M, q) < 1:
+        pytest.skip("no bits left")
+    A, B = hpl_like(m, q, n, 1.0, seed=m + q + n)
+    log(f"ragged m={m} q={q} n={n} s={s}")
+    check_all_stages(A, B, s, run_stages(A, B, s))
+
+
+@pytest.mark.parametrize("s,q", [(16, 64), (18, 64), (18, 1000), (20, 3), (20, 200)])
+def test_k_above_53(s, q):
+    """k > 53: A' no longer fits the 53-bit significand (residues via u 2^sh)."""
+    M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+    assert oz.kbits(M, q) > 53
+    A, B = hpl_like(40, q, 33, 0.5, seed=s)
+    log(f"k>53 s={s} q={q}")
+    check_all_stages(A, B, s, run_stages(A, B, s))
+
+
+def special_inputs():
+    rng = np.random.default_rng(21)
+    A, B = hpl_like(70, 90, 66, 2.0, seed=5)
+    A[0, :] = 0.0                          # zero row -> +0
+    B[:, 1] = 0.0                          # zero column
+    A[2, 17] = np.inf                      # non-finite row -> NaN row
+    B[30, 3] = np.nan                      # non-finite column
+    A[4, :] = rng.standard_normal(90) * 1e-310   # subnormal-ish row
+    A[5, :] = rng.standard_normal(90) * 1e300    # near-overflow row
+    B[:, 6] = rng.standard_normal(90) * 1e300    # overflow products -> +-Inf
+    A[7, :] = rng.standard_normal(90) * 1e-300
+    B[:, 8] = rng.standard_normal(90) * 1e-300   # underflow products -> subnormal / 0
+    A[9, :] = 2.0 ** 40                    # exact powers of two
+    A[10, 3] = -5e-324                     # lone smallest subnormal in a normal row
+    return A, B
+
+
+@pytest.mark.parametrize("s", [10, 14, 18])
+def test_special_values(s):
+    A, B = special_inputs()
+    log(f"special values s={s}")
+    check_all_stages(A, B, s, run_stages(A, B, s))
+
+
+def test_integer_inputs_exact():
+    A, B = integer_valued(100, 64, 90, 2**10, seed=2)
+    C, _ = run_dgemm(A, B, 14)
+    assert np.array_equal(C, A @ B)
+
+
+def test_leading_dimension_padding():
+    A, B = hpl_like(45, 77, 31, 1.0, seed=3)
+    C0, _ = run_dgemm(A, B, 14)
+    C1, buf = run_dgemm(A, B, 14, lda=50, ldb=80, ldc=47)
+    assert same_doubles(C0, C1)
+    # entries of C's padding rows are untouched
+    assert np.all(buf[:31, 45:47] == 12345.0)
+    g = run_stages(A, B, 14, lda=64, ldb=128, ldc=64)
+    assert same_doubles(g["C"], C0)
+
+
+def test_dgemm_matches_stages_and_oracle():
+    A, B = hpl_like(200, 333, 150, 0.5, seed=4)
+    C, _ = run_dgemm(A, B, 14)
+    g = run_stages(A, B, 14, want_ct=False, want_prime=False)
+    assert same_doubles(C, g["C"])
+    assert same_doubles(C, oz.dgemm(A, B, 14))
+
+
+def test_q_zero_writes_zero_and_empty_shapes():
+    import torch
+    Cd = torch.full((5, 4), 3.0, dtype=torch.float64, device="cuda")
+    dummy = torch.zeros(8, dtype=torch.float64, device="cuda")
+    L.ozgemm_dgemm(4, 5, 0, dummy, 4, dummy, 1, Cd, 4, 14)
+    torch.cuda.synchronize()
+    assert torch.all(Cd == 0).item()
+    L.ozgemm_dgemm(0, 5, 3, dummy, 1, dummy, 3, Cd, 1, 14)
+    L.ozgemm_dgemm(4, 0, 3, dummy, 4, dummy, 3, Cd, 4, 14)
+
+
+def test_invariants_on_gpu():
+    A, B = hpl_like(60, 70, 50, 1.0, seed=8)
+    C, _ = run_dgemm(A, B, 14)
+    C2, _ = run_dgemm(A * 2.0**-30, B, 14)
+    assert same_doubles(C2, C * 2.0**-30)
+    Cn, _ = run_dgemm(-A, B, 14)
+    assert same_doubles(Cn, -C)
+    Ct, _ = run_dgemm(B.T.copy(), A.T.copy(), 14)
+    assert same_doubles(Ct, C.T)
+
+
+def test_phase_timing():
+    import torch
+    A, B = hpl_like(128, 128, 128, 0.5, seed=1)
+    L.ozgemm_timing(True)
+    for _ in range(3):
+        run_dgemm(A, B, 14)
+    ms, calls = L.ozgemm_phase_ms()
+    L.ozgemm_timing(False)
+    assert calls == 3 and all(x > 0 for x in ms)
+
+
+@pytest.mark.parametrize("s", [8, 14, 18])
+def test_1024_cube_full_oracle(s):
+    """1024^3, phi = 0.5: integer stages (s = 14) and the full result bit-exact."""
+    A, B = hpl_like(1024, 1024, 1024, 0.5, seed=0)
+    log(f"1024^3 s={s}: GPU")
+    g = run_stages(A, B, s, want_ct=(s == 14), want_prime=(s == 14))
+    log(f"1024^3 s={s}: oracle")
+    ref = oz.dgemm(A, B, s, stages=True)
+    log(f"1024^3 s={s}: compare")
+    check_all_stages(A, B, s, g, ref=ref)
