@@ -31,147 +31,232 @@ namespace oz {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Physical 16-byte chunk of logical chunk kc in tile row `row` is kc ^ swz(row).
+// A wavefront's 16-byte LDS reads are served 16 lanes at a time from 64
+// four-byte banks (256 bytes); an MFMA operand load sends 16 consecutive tile
+// rows to one group, so the 16 chunks must land in 16 different 16-byte bank
+// slots.  With 128-byte rows the slot is 8 (row & 1) + physical chunk, and
+// ((row >> 1) ^ (row << 2)) & 7 takes 8 distinct values on the even and on
+// the odd rows of every 16-row window (it also keeps 8-row groups distinct).
+// It depends on row mod 16 only, so a lane's source offset for the direct
+// LDS loads takes one of two values (even / odd 1 KB block).
 template <int BK>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 64) return ((row >> 1) ^ (row >> 3)) & 3;
-  else return ((row >> 1) ^ (row << 2)) & 7;
+__host__ __device__ __forceinline__ int swz(int row) {
+  static_assert(BK == 128, "the swizzle is laid out for 128-byte rows");
+  return ((row >> 1) ^ (row << 2)) & 7;  // always < 8: stays inside the row
 }
 
-template <int BM, int BN, int BK>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t* __restrict__ Ares,
-                                                       const int8_t* __restrict__ Bres, int m_pad, int n_pad,
-                                                       int q_pad, GemmConsts c, int32_t* __restrict__ Ct,
-                                                       uint8_t* __restrict__ rt) {
-  constexpr int CPR = BK / 16;                 // 16-byte chunks per tile row
-  constexpr int A_CHUNKS = BM * CPR / 256;     // chunk loads per thread
-  constexpr int B_CHUNKS = BN * CPR / 256;
-  constexpr int WTM = BM / 2, WTN = BN / 2;    // wave tile
-  constexpr int FM = WTM / 16, FN = WTN / 16;  // 16x16 MFMA tiles per wave
-  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+// Map the linear block id to (modulus, tile row, tile column).
+//
+// Blocks go to the 8 XCDs round-robin (block b runs on XCD b mod 8) and each
+// XCD has its own L2.  The moduli planes are walked one at a time, so all
+// XCDs work on the same plane and its operands stay in the shared
+// last-level cache; inside a plane each XCD takes a contiguous eighth of the
+// tiles, walked in groups of GROUP_M tile rows, so the blocks running on one
+// XCD at a time share A row panels and B column panels in its L2.
+template <int GROUP_M>
+__host__ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int& t, int& mi, int& nj) {
+  const int per_plane = tiles_m * tiles_n;
+  t = b / per_plane;
+  const int w = b % per_plane;
+  const int tile = (per_plane % 8 == 0) ? (w % 8) * (per_plane / 8) + w / 8 : w;
+  const int group = tile / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = tile % (GROUP_M * tiles_n);
+  mi = first_m + in_group % gm;
+  nj = in_group / gm;
+}
 
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
+// C mod m for an int32 C, as a value in [0, m).  C = h 2^16 + l with
+// |h| <= 2^15 and 0 <= l < 2^16, so x = h (2^16 mod m) + l satisfies
+// |x| < 2^24 and is exact in FP32; x - m floor(x / m) computed with an FP32
+// reciprocal is then exact and off by at most one multiple of m.
+__device__ __forceinline__ uint32_t mod_small(int v, int m, int c16, float invf) {
+  const int x = (v >> 16) * c16 + (v & 0xffff);
+  const float xf = (float)x;
+  const float qf = __builtin_floorf(xf * invf);
+  int r = (int)__builtin_fmaf(-qf, (float)m, xf);
+  r = r < 0 ? r + m : r;
+  r = r >= m ? r - m : r;
+  return (uint32_t)r;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int t = blockIdx.z;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+// s_waitcnt with only the vector-memory counter constrained to <= N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// BM x BN output tile per block of WM x WN wavefronts; each wavefront owns a
+// (BM/WM) x (BN/WN) sub-tile of 32x32 tiles of v_mfma_i32_32x32x32_i8.  Lane
+// l of that instruction supplies 16 bytes of row (l mod 32) of A (column
+// (l mod 32) of B) from K chunk l / 32 of the 32-wide K step; both operands
+// use the same lane -> K mapping, so the product is the dot product over the
+// step whatever order the hardware takes the bytes in.  Lane l receives rows
+// 8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
+//
+// Data movement:
+//  * K slices of BK bytes go from HBM straight into LDS (global_load_lds, 16
+//    bytes per lane, no register staging) through STAGES buffers; the slice
+//    STAGES-1 ahead is requested as soon as its buffer is free.  Past the
+//    last slice the last one is re-requested, so every iteration has the same
+//    number of loads in flight and the loop needs no branches.
+//  * Inside a slice the operand fragments of the next 32-wide step are read
+//    from LDS into a second register set while the current step's MFMAs run
+//    (one read issued after each MFMA), so LDS latency stays hidden.
+//  * One barrier per slice, placed before the last step's MFMAs: it publishes
+//    the next slice (after this wave's loads for it have landed) and retires
+//    the current buffer (after this wave's reads of it are in registers).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT>
+__global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
+    const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
+    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt) {
+  constexpr int NW = WM * WN;
+  constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
+  constexpr int ROWS_PER_KB = 1024 / BK;        // tile rows filled by one wavefront load
+  constexpr int A_LOADS = BM * BK / 1024 / NW;  // wavefront loads per slice
+  constexpr int B_LOADS = BN * BK / 1024 / NW;
+  constexpr int LPW = A_LOADS + B_LOADS;        // loads per wavefront per slice
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int NKS = BK / 32;                  // 32-wide MFMA steps per slice
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LPW < 64, "pipeline depth");
+  static_assert(FM * FN >= FM + FN, "interleave pattern");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * (BM + BN) * BK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int t, mi, nj;
+  tile_of_block<4>(blockIdx.x, m_pad / BM, n_pad / BN, t, mi, nj);
+  const int m0 = mi * BM, n0 = nj * BN;
 
   const int8_t* Ag = Ares + (long)t * m_pad * q_pad + (long)m0 * q_pad;
   const int8_t* Bg = Bres + (long)t * n_pad * q_pad + (long)n0 * q_pad;
 
-  // global -> register chunk coordinates (fixed per thread)
-  int a_off[A_CHUNKS], a_lds[A_CHUNKS], b_off[B_CHUNKS], b_lds[B_CHUNKS];
-#pragma unroll
-  for (int p = 0; p < A_CHUNKS; ++p) {
-    const int cidx = tid + 256 * p;
-    const int row = cidx / CPR, kc = cidx % CPR;
-    a_off[p] = row * q_pad + kc * 16;
-    a_lds[p] = row * BK + ((kc ^ swz<BK>(row)) * 16);
-  }
-#pragma unroll
-  for (int p = 0; p < B_CHUNKS; ++p) {
-    const int cidx = tid + 256 * p;
-    const int row = cidx / CPR, kc = cidx % CPR;
-    b_off[p] = row * q_pad + kc * 16;
-    b_lds[p] = row * BK + ((kc ^ swz<BK>(row)) * 16);
-  }
+  // A wavefront load fills 1 KB of LDS = ROWS_PER_KB whole tile rows, lane l
+  // landing in row l / CPR, physical chunk l mod CPR.  The swizzle depends on
+  // row mod 16, so the source offset differs between even and odd 1 KB blocks.
+  const int lrow_in_kb = lane / CPR;
+  const int lane_src0 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb)) * 16);
+  const int lane_src1 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb + ROWS_PER_KB)) * 16);
+  const long kb_stride = (long)ROWS_PER_KB * q_pad;  // source distance of consecutive 1 KB loads
 
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+  auto issue = [&](int buf, int k0) {
+    int8_t* As = smem + buf * (BM + BN) * BK;
+    int8_t* Bs = As + BM * BK;
+    const int8_t* ga = Ag + (long)(wave * A_LOADS) * kb_stride + k0;
+    const int8_t* gb = Bg + (long)(wave * B_LOADS) * kb_stride + k0;
 #pragma unroll
-  for (int p = 0; p < A_CHUNKS; ++p) ra[p] = *reinterpret_cast<const uint4*>(Ag + a_off[p]);
+    for (int p = 0; p < A_LOADS; ++p)
+      __builtin_amdgcn_global_load_lds(ga + p * kb_stride + (((wave * A_LOADS + p) & 1) ? lane_src1 : lane_src0),
+                                       As + (wave * A_LOADS + p) * 1024, 16, 0, 0);
 #pragma unroll
-  for (int p = 0; p < B_CHUNKS; ++p) rb[p] = *reinterpret_cast<const uint4*>(Bg + b_off[p]);
-#pragma unroll
-  for (int p = 0; p < A_CHUNKS; ++p) *reinterpret_cast<uint4*>(&As[0][a_lds[p]]) = ra[p];
-#pragma unroll
-  for (int p = 0; p < B_CHUNKS; ++p) *reinterpret_cast<uint4*>(&Bs[0][b_lds[p]]) = rb[p];
-  __syncthreads();
+    for (int p = 0; p < B_LOADS; ++p)
+      __builtin_amdgcn_global_load_lds(gb + p * kb_stride + (((wave * B_LOADS + p) & 1) ? lane_src1 : lane_src0),
+                                       Bs + (wave * B_LOADS + p) * 1024, 16, 0, 0);
+  };
 
-  v4i acc[FM][FN];
+  const int lrow = lane & 31;
+  const int lkc = lane >> 5;  // K chunk (of 2) within a 32-wide step
+  auto read = [&](int buf, int ks, v4i* af, v4i* bf) {
+    const int8_t* As = smem + buf * (BM + BN) * BK;
+    const int8_t* Bs = As + BM * BK;
+    const int kc = ks * 2 + lkc;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WTN + j * 32 + lrow;
+      bf[j] = *reinterpret_cast<const v4i*>(&Bs[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WTM + i * 32 + lrow;
+      af[i] = *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
+    }
+  };
+
+  v16i acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
   const int nk = q_pad / BK;
-  const int lrow = lane & 15;
-  const int lkc = lane >> 4;  // 0..3: K chunk within a 64-wide slice
+#pragma unroll
+  for (int sidx = 0; sidx < STAGES - 1; ++sidx) issue(sidx, min(sidx, nk - 1) * BK);
+  wait_vmcnt<(STAGES - 2) * LPW>();
+  __builtin_amdgcn_s_barrier();
 
+  v4i acur[FM], bcur[FN], anxt[FM], bnxt[FN];
+  read(0, 0, acur, bcur);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // prefetch the next slice (the last iteration re-reads its own slice
-    // into the idle buffer, which keeps the loop free of branches)
-    const int kn = min(kt + 1, nk - 1) * BK;
+    issue((kt + STAGES - 1) % STAGES, min(kt + STAGES - 1, nk - 1) * BK);
 #pragma unroll
-    for (int p = 0; p < A_CHUNKS; ++p) ra[p] = *reinterpret_cast<const uint4*>(Ag + a_off[p] + kn);
-#pragma unroll
-    for (int p = 0; p < B_CHUNKS; ++p) rb[p] = *reinterpret_cast<const uint4*>(Bg + b_off[p] + kn);
-#pragma unroll
-    for (int ks = 0; ks < BK / 64; ++ks) {
-      v4i af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WTM + i * 16 + lrow;
-        const int kc = ks * 4 + lkc;
-        af[i] = *reinterpret_cast<const v4i*>(&As[cur][row * BK + ((kc ^ swz<BK>(row)) * 16)]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WTN + j * 16 + lrow;
-        const int kc = ks * 4 + lkc;
-        bf[j] = *reinterpret_cast<const v4i*>(&Bs[cur][row * BK + ((kc ^ swz<BK>(row)) * 16)]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) {
+        read(kt % STAGES, ks + 1, anxt, bnxt);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slice kt are done
+        wait_vmcnt<(STAGES - 2) * LPW>();    // this wave's loads of slice kt + 1 have landed
+        __builtin_amdgcn_s_barrier();
+        read((kt + 1) % STAGES, 0, anxt, bnxt);  // (past the end: unused)
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[i], bcur[j], acc[i][j], 0, 0, 0);
+      // one LDS read after each MFMA while the reads last
+#pragma unroll
+      for (int r = 0; r < FM + FN; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acur[i] = anxt[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
     }
-#pragma unroll
-    for (int p = 0; p < A_CHUNKS; ++p) *reinterpret_cast<uint4*>(&As[cur ^ 1][a_lds[p]]) = ra[p];
-#pragma unroll
-    for (int p = 0; p < B_CHUNKS; ++p) *reinterpret_cast<uint4*>(&Bs[cur ^ 1][b_lds[p]]) = rb[p];
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // no load into LDS may outlive the block
 
   // ---- epilogue: int32 planes and/or residues mod m_t ----
   const long plane = (long)m_pad * n_pad;
   // select this plane's modulus without indexing the by-value argument
   // dynamically (which would copy it to scratch)
   int mt = c.m[0];
-  double inv = c.inv[0];
 #pragma unroll
-  for (int u = 1; u < OZGEMM_S_MAX; ++u) {
-    mt = (u == t) ? c.m[u] : mt;
-    inv = (u == t) ? c.inv[u] : inv;
-  }
+  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+  const int c16 = (1 << 16) % mt;
+  const float invf = 1.0f / (float)mt;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4);
-      const int col = n0 + wn * WTN + j * 16 + (lane & 15);
-      const long off = (long)t * plane + (long)col * m_pad + row;
-      const v4i v = acc[i][j];
-      if (Ct != nullptr) *reinterpret_cast<v4i*>(Ct + off) = v;
-      if (rt != nullptr) {
-        uint32_t packed = 0;
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const double d = (double)v[r];
-          const double qf = __builtin_floor(d * inv);
-          int ri = (int)__builtin_fma(-qf, (double)mt, d);
-          ri = ri < 0 ? ri + mt : ri;
-          ri = ri >= mt ? ri - mt : ri;
-          packed |= (uint32_t)ri << (8 * r);
+      for (int g = 0; g < 4; ++g) {
+        const int row = m0 + wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
+        const long off = (long)t * plane + (long)col * m_pad + row;
+        const v16i& v = acc[i][j];
+        if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+        if (WRITE_RT) {
+          const uint32_t packed = mod_small(v[4 * g], mt, c16, invf) | (mod_small(v[4 * g + 1], mt, c16, invf) << 8) |
+                                  (mod_small(v[4 * g + 2], mt, c16, invf) << 16) |
+                                  (mod_small(v[4 * g + 3], mt, c16, invf) << 24);
+          *reinterpret_cast<uint32_t*>(rt + off) = packed;
         }
-        *reinterpret_cast<uint32_t*>(rt + off) = packed;
       }
+      // keep the scheduler from hoisting every accumulator out of AGPRs at once
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -180,11 +265,19 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t* __restrict__
 
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad, const GemmConsts& c,
                        int32_t* Ct, uint8_t* rt, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, STAGES = 2;
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
-  dim3 grid(n_pad / BN, m_pad / BM, c.s);
-  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK>), grid, dim3(256), 0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct,
-                     rt);
+  const int nblocks = (n_pad / BN) * (m_pad / BM) * c.s;
+  const dim3 grid(nblocks), block(WM * WN * 64);
+  if (Ct != nullptr && rt != nullptr)
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, true>), grid, block, 0, st, Ares, Bres, m_pad,
+                       n_pad, q_pad, c, Ct, rt);
+  else if (Ct != nullptr)
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false>), grid, block, 0, st, Ares, Bres,
+                       m_pad, n_pad, q_pad, c, Ct, rt);
+  else if (rt != nullptr)
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true>), grid, block, 0, st, Ares, Bres,
+                       m_pad, n_pad, q_pad, c, Ct, rt);
   return hipGetLastError();
 }
 
