@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-accuracy", action="store_true")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="also run one plain device copy of this many bytes (calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -49,9 +51,10 @@ def kernel_hash(name: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(workload: str, launches_per_step: float):
-    """HBM bytes per GEMM launch from the committed counter summary, or None
-    when it is absent or was taken on a different kernel source."""
+def traffic_record(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary
+    (profiles/traffic.json), or None when it is absent or was taken on a
+    different GEMM kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -60,7 +63,8 @@ def traffic_record(workload: str, launches_per_step: float):
         ent = rec.get(workload)
         if not ent or ent.get("kernel_sha") != kernel_hash("gemm_i8.hip"):
             return None
-        return ent.get("gemm_hbm_bytes_per_launch")
+        v = ent.get("gemm_hbm_bytes_per_launch")
+        return None if v is None else int(v)
     except Exception:
         return None
 
@@ -76,13 +80,12 @@ def cpu_baseline(A, B, s, q, target_s, Cg_full_getter):
         blas_threads = 1
     m, n = A.shape[0], B.shape[1]
     rng = np.random.default_rng(7)
-    side = 16
-    # calibrate on a small block, then size the block for ~target_s seconds
+    # calibrate on a 32x32 block, then size the block for about target_s
+    # seconds (cost grows between linearly and quadratically with the side)
     t0 = time.perf_counter()
-    oz.dgemm_block(A, B, s, np.arange(side), np.arange(side))
+    oz.dgemm_block(A, B, s, np.arange(min(32, m)), np.arange(min(32, n)))
     t_small = time.perf_counter() - t0
-    per_entry = t_small / (side * side)
-    side = int(max(16, min(512, (target_s / max(per_entry, 1e-9)) ** 0.5)))
+    side = int(max(32, min(1024, 32 * (target_s / max(t_small, 1e-6)) ** (1 / 1.6))))
     rows = np.sort(rng.choice(m, size=min(side, m), replace=False))
     cols = np.sort(rng.choice(n, size=min(side, n), replace=False))
     t0 = time.perf_counter()
@@ -131,6 +134,12 @@ def main():
     for _ in range(args.warmup):
         L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
     torch.cuda.synchronize()
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 8, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     L.ozgemm_timing(True)
     torch.cuda.synchronize()
@@ -172,7 +181,7 @@ def main():
             "peak": INT8_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / INT8_PEAK_TOPS, 4),
-            "traffic": traffic_record(workload, 1.0),
+            "traffic": traffic_record(workload),
             "algorithmic_ops_per_launch": int8_ops,
         },
         "phases_ms": {"scale": round(per[0], 4), "residue": round(per[1], 4), "gemm": round(per[2], 4),

@@ -43,33 +43,10 @@ __device__ __forceinline__ double round_window(uint64_t T, bool sticky, int E) {
   return __builtin_ldexp((double)(mant + (up ? 1 : 0)), E - keep + 1);
 }
 
+// X * 2^(ei + fj - 2k) rounded once, from the exact limb sums S[0..L-1] of
+// Z = sum_t r_t W_t (steps 2-4 above).
 template <int L>
-__global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt, int m, int n, int m_pad,
-                                                   long plane, const int32_t* __restrict__ e,
-                                                   const int32_t* __restrict__ f, CrtConsts c,
-                                                   double* __restrict__ C, long ldc) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= m) return;
-  const int ei = e[i];
-  for (int j = blockIdx.y; j < n; j += gridDim.y) {
-  const int fj = f[j];
-  double* out = C + (long)j * ldc + i;
-  if (ei == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) {
-    *out = __builtin_nan("");
-    continue;
-  }
-
-  // 1. exact FP64 limb sums
-  double S[L];
-#pragma unroll
-  for (int l = 0; l < L; ++l) S[l] = 0.0;
-  const uint8_t* p = rt + (long)j * m_pad + i;
-  for (int t = 0; t < c.s; ++t) {
-    const double r = (double)p[(long)t * plane];
-#pragma unroll
-    for (int l = 0; l < L; ++l) S[l] = __builtin_fma(r, c.w[t][l], S[l]);
-  }
-
+__device__ __forceinline__ double reconstruct(const double* S, const CrtConsts& c, int scale) {
   // 2. carries -> Z[0..L]
   uint32_t Z[L + 1];
   uint64_t carry = 0;
@@ -89,8 +66,8 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
   const uint32_t Q = (uint32_t)__builtin_rint(zf * c.invM);
   uint32_t X[L + 1];
   {
-    uint64_t pc = 0;      // carry of Q*M
-    int64_t borrow = 0;   // 0 or -1
+    uint64_t pc = 0;     // carry of Q*M
+    int64_t borrow = 0;  // 0 or -1
 #pragma unroll
     for (int l = 0; l <= L; ++l) {
       const uint64_t pm = (uint64_t)Q * c.M[l] + pc;
@@ -103,15 +80,15 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
   const bool neg0 = (X[L] >> 31) != 0;
   {
     // D = X - M/2 (if X >= 0) or X + M/2 (if X < 0); fix when D has X's sign
-    uint32_t D[L + 1];
+    uint32_t Dtop = 0;
     int64_t cb = 0;
 #pragma unroll
     for (int l = 0; l <= L; ++l) {
       const int64_t d = neg0 ? (int64_t)X[l] + (int64_t)c.half[l] + cb : (int64_t)X[l] - (int64_t)c.half[l] + cb;
-      D[l] = (uint32_t)d;
+      Dtop = (uint32_t)d;
       cb = d >> 32;  // arithmetic: carry 1, borrow -1, or 0
     }
-    const bool dneg = (D[L] >> 31) != 0;
+    const bool dneg = (Dtop >> 31) != 0;
     // X >= 0 and X - M/2 >= 0 (never == 0): X -= M;  X < 0 and X + M/2 < 0: X += M
     const bool fix = neg0 ? dneg : !dneg;
     if (fix) {
@@ -135,7 +112,7 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
     }
   }
 
-  // 4. normalise so that X[L] holds the leading nonzero limb
+  // 4. normalise so that X[L] holds the leading nonzero limb, then round
   int h = L;
 #pragma unroll
   for (int it = 0; it < L; ++it) {
@@ -146,28 +123,66 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
       --h;
     }
   }
-  double res;
-  if (X[L] == 0) {
-    res = 0.0;
-  } else {
-    const int lz = __clz(X[L]);
-    const uint64_t hi64 = ((uint64_t)X[L] << 32) | (uint64_t)X[L - 1];
-    const uint32_t lo32 = (L >= 2) ? X[L - 2] : 0u;
-    uint64_t T = hi64;
-    uint32_t rest = lo32;
-    if (lz > 0) {
-      T = (hi64 << lz) | (uint64_t)(lo32 >> (32 - lz));
-      rest = lo32 << lz;
-    }
-    bool sticky = rest != 0;
-#pragma unroll
-    for (int l = 0; l + 3 <= L; ++l) sticky = sticky || (X[l] != 0);
-    const int Ebit = 32 * h + 31 - lz;  // position of the leading bit of |X|
-    const int E = Ebit + ei + fj - 2 * c.k;
-    res = round_window(T, sticky, E);
-    if (neg) res = -res;
+  if (X[L] == 0) return 0.0;
+  const int lz = __clz(X[L]);
+  const uint64_t hi64 = ((uint64_t)X[L] << 32) | (uint64_t)X[L - 1];
+  const uint32_t lo32 = (L >= 2) ? X[L - 2] : 0u;
+  uint64_t T = hi64;
+  uint32_t rest = lo32;
+  if (lz > 0) {
+    T = (hi64 << lz) | (uint64_t)(lo32 >> (32 - lz));
+    rest = lo32 << lz;
   }
-  *out = res;
+  bool sticky = rest != 0;
+#pragma unroll
+  for (int l = 0; l + 3 <= L; ++l) sticky = sticky || (X[l] != 0);
+  const int E = 32 * h + 31 - lz + scale;  // exponent of the leading bit of |X| 2^scale
+  const double res = round_window(T, sticky, E);
+  return neg ? -res : res;
+}
+
+// Thread = 4 consecutive rows of one output column: the product residues of
+// each modulus come in as one 32-bit load (the planes are padded to whole
+// tiles, so rows up to the padded height are always readable).
+template <int L>
+__global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt, int m, int n, int m_pad,
+                                                   long plane, const int32_t* __restrict__ e,
+                                                   const int32_t* __restrict__ f, CrtConsts c,
+                                                   double* __restrict__ C, long ldc) {
+  const int i0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= m) return;
+  int ei[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) ei[u] = (i0 + u < m) ? e[i0 + u] : 0;
+  for (int j = blockIdx.y; j < n; j += gridDim.y) {
+    const int fj = f[j];
+    const uint8_t* p = rt + (long)j * m_pad + i0;
+    uint32_t rr[OZGEMM_S_MAX];
+#pragma unroll
+    for (int t = 0; t < OZGEMM_S_MAX; ++t)
+      rr[t] = (t < c.s) ? *reinterpret_cast<const uint32_t*>(p + (long)t * plane) : 0u;
+    double* out = C + (long)j * ldc + i0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u >= m) break;
+      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) {
+        out[u] = __builtin_nan("");
+        continue;
+      }
+      // 1. exact FP64 limb sums
+      double S[L];
+#pragma unroll
+      for (int l = 0; l < L; ++l) S[l] = 0.0;
+#pragma unroll
+      for (int t = 0; t < OZGEMM_S_MAX; ++t) {
+        if (t < c.s) {
+          const double r = (double)((rr[t] >> (8 * u)) & 0xffu);
+#pragma unroll
+          for (int l = 0; l < L; ++l) S[l] = __builtin_fma(r, c.w[t][l], S[l]);
+        }
+      }
+      out[u] = reconstruct<L>(S, c, ei[u] + fj - 2 * c.k);
+    }
   }
 }
 
@@ -181,7 +196,7 @@ __global__ void fill_zero_kernel(double* C, int m, int n, long ldc) {
 
 hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e, const int32_t* f,
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
-  dim3 grid((m + 255) / 256, std::min(n, 65535));
+  dim3 grid((m + 1023) / 1024, std::min(n, 65535));
   const long plane = (long)m_pad * n_pad;
   switch (c.L) {
 #define OZ_CRT_CASE(LL)                                                                                      \

@@ -23,7 +23,6 @@ inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
 struct ResidueConsts {
   int s;
   int k;                        // bits kept: |A'| <= 2^k - 1
-  int big;                      // k > 53: A' may exceed the 53-bit significand
   int m[OZGEMM_S_MAX];          // moduli
   int lo[OZGEMM_S_MAX];         // -floor(m/2)
   int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1

@@ -139,7 +139,6 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
   std::memset(cc, 0, sizeof(*cc));
   rc->s = gc->s = cc->s = s;
   rc->k = cc->k = k;
-  rc->big = k > 53 ? 1 : 0;
   for (int t = 0; t < s; ++t) {
     const int m = mods[t];
     rc->m[t] = gc->m[t] = m;

@@ -13,12 +13,17 @@
 // 16-byte store per modulus into the K-contiguous plane the GEMM reads.
 //
 // Exactness.  a * 2^(k - e) is exact (a power-of-two scaling) unless it
-// falls below 2^-1022, where it is below 1 and truncates to 0 anyway.  For
-// |A'| < 2^53, q = rint(A' * RN(1/m)) is within one of the nearest-integer
-// quotient (relative error <= 2^-52, quotient < 2^53/173), so
-// r = fma(-q, m, A') is the exact small remainder and one +-m correction
-// lands it in the symmetric range.  When k > 53, A' = u * 2^sh with
-// u < 2^53 and A' mod m = (u mod m)(2^sh mod m) mod m.
+// falls below 2^-1022, where it is below 1 and truncates to 0 anyway.
+// The symmetric residue is r = A' - m floor(A'/m + 1/2), which lies in
+// [-floor(m/2), ceil(m/2) - 1] for odd and even m alike.  The quotient is
+// taken as q = floor(fma(A', RN(1/m), 1/2)); the fma result is within
+// 2^(k-52) 1.01 / m of A'/m + 1/2.  For odd m, A'/m + 1/2 = (2A' + m) / 2m has
+// an odd numerator, so it is at least 1/2m away from every integer, and for
+// m = 256 every step is exact: with k <= 50 the floor is therefore always
+// the exact one and r = fma(-q, m, A') needs no correction.  For
+// 50 < k <= 53 the quotient can be off by one and one +-m correction is
+// applied.  When k > 53, A' = u * 2^sh with u < 2^53 and
+// A' mod m = (u mod m)(2^sh mod m) mod m.
 #include "oz_internal.h"
 
 namespace oz {
@@ -29,16 +34,18 @@ constexpr int TR = 32;           // rows per tile
 constexpr int TK = 128;          // inner-dimension entries per tile
 constexpr int LDS_STRIDE = TK + 1;  // doubles; odd stride spreads banks
 
+template <bool FIX>
 __device__ __forceinline__ int smod_small(double a, int m, double inv, int lo, int hi) {
-  double qf = __builtin_rint(a * inv);
-  double r = __builtin_fma(-qf, (double)m, a);
-  int ri = (int)r;
-  ri = ri > hi ? ri - m : ri;
-  ri = ri < lo ? ri + m : ri;
+  const double qf = __builtin_floor(__builtin_fma(a, inv, 0.5));
+  int ri = (int)__builtin_fma(-qf, (double)m, a);
+  if (FIX) {
+    ri = ri > hi ? ri - m : ri;
+    ri = ri < lo ? ri + m : ri;
+  }
   return ri;
 }
 
-template <bool ROWS_CONTIG, bool BIG>
+template <bool ROWS_CONTIG, int MODE>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
 __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
                                                        long ls, const int32_t* __restrict__ ex, ResidueConsts c,
                                                        int8_t* __restrict__ planes, long plane_stride, int q_pad,
@@ -104,6 +111,7 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
     }
   }
 
+  constexpr bool BIG = MODE == 2;
   int sh[16];
   if (BIG) {
     // A' = u * 2^sh with |u| < 2^53 (sh = 0 when |A'| < 2^53)
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      int ri = smod_small(a[j], m, inv, lo, hi);
+      int ri = smod_small<MODE != 0>(a[j], m, inv, lo, hi);
       if (BIG) {
         int v = ri * (int)c.pow2[t][sh[j]];
         v = v % m;  // in (-m, m)
@@ -150,21 +158,20 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
   dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
   const bool rows_contig = (rs == 1);
+  const int mode = c.k <= 50 ? 0 : (c.k <= 53 ? 1 : 2);
+#define OZ_RES_LAUNCH(RC, MD)                                                                                \
+  hipLaunchKernelGGL((residue_kernel<RC, MD>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,     \
+                     plane_stride, q_pad, prime, prime_rs, prime_ls)
   if (rows_contig) {
-    if (c.big)
-      hipLaunchKernelGGL((residue_kernel<true, true>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
-                         plane_stride, q_pad, prime, prime_rs, prime_ls);
-    else
-      hipLaunchKernelGGL((residue_kernel<true, false>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
-                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+    if (mode == 0) OZ_RES_LAUNCH(true, 0);
+    else if (mode == 1) OZ_RES_LAUNCH(true, 1);
+    else OZ_RES_LAUNCH(true, 2);
   } else {
-    if (c.big)
-      hipLaunchKernelGGL((residue_kernel<false, true>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
-                         plane_stride, q_pad, prime, prime_rs, prime_ls);
-    else
-      hipLaunchKernelGGL((residue_kernel<false, false>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,
-                         plane_stride, q_pad, prime, prime_rs, prime_ls);
+    if (mode == 0) OZ_RES_LAUNCH(false, 0);
+    else if (mode == 1) OZ_RES_LAUNCH(false, 1);
+    else OZ_RES_LAUNCH(false, 2);
   }
+#undef OZ_RES_LAUNCH
   return hipGetLastError();
 }
 

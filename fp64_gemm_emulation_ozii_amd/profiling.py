@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 output for the committed performance records.
+
+Usage (after the profiler runs listed in the summaries themselves)::
+
+    python -m fp64_gemm_emulation_ozii_amd.profiling stats  <kernel_stats.csv> <out.txt> <command...>
+    python -m fp64_gemm_emulation_ozii_amd.profiling traffic <fetch counter_collection.csv>
+        <write counter_collection.csv> <copy bytes> <workload> <out.json> <command...>
+
+``stats`` turns rocprofv3's ``--stats`` kernel table into a short text
+table.  ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
+runs into HBM bytes per launch of each kernel.  Both counters report
+kilobytes per dispatch; a plain device copy of a known number of bytes in the
+same run calibrates them (bytes moved / bytes reported), and the GEMM
+kernel's source hash is stored so that a record taken on another kernel
+version is not reused.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_sha(name: str = "gemm_i8.hip") -> str:
+    return hashlib.sha256(open(os.path.join(PKG, "csrc", name), "rb").read()).hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    """Kernel name without namespaces and parameters (template arguments kept,
+    without spaces, so that instances stay apart)."""
+    k = kernel.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth, cut = 0, len(k)
+    for i, ch in enumerate(k):  # parameter list = first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    k = k[:cut]
+    base, _, targs = k.partition("<")
+    base = base.split("::")[-1].strip()
+    return base + (("<" + targs.replace(" ", "")) if targs else "")
+
+
+def read_stats(path: str):
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+            calls = int(float(r.get("Calls", 0)))
+            total = float(r.get("TotalDurationNs", 0))
+            avg = float(r.get("AverageNs", total / max(calls, 1)))
+            pct = float(r.get("Percentage", 0))
+            mn = float(r.get("MinNs", avg))
+            mx = float(r.get("MaxNs", avg))
+            rows.append((short_name(name), calls, total, avg, pct, mn, mx))
+    return rows
+
+
+def write_stats(stats_csv: str, out_txt: str, command: str) -> None:
+    rows = read_stats(stats_csv)
+    with open(out_txt, "w") as fh:
+        fh.write(f"# rocprofv3 kernel statistics\n# command: {command}\n")
+        fh.write(f"# {'kernel':<28} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}\n")
+        for name, calls, total, avg, pct, mn, mx in sorted(rows, key=lambda r: -r[2]):
+            fh.write(f"  {name:<28} {calls:>6} {avg / 1e3:>10.2f} {mn / 1e3:>10.2f} {mx / 1e3:>10.2f} {pct:>8.2f}\n")
+
+
+def read_counter(path: str):
+    """{kernel short name: [value per dispatch]} for a single-counter run."""
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = short_name(r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("kernel_name") or "")
+            val = float(r.get("Counter_Value") or r.get("Counter-Value") or r.get("value") or 0.0)
+            disp = r.get("Dispatch_Id") or r.get("Dispatch-Id") or r.get("dispatch_id") or len(per)
+            per.setdefault(name, {}).setdefault(disp, 0.0)
+            per[name][disp] += val
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, out_json: str,
+                  command: str) -> dict:
+    fetch = read_counter(fetch_csv)
+    write = read_counter(write_csv)
+    copy_names = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy_names:
+        raise RuntimeError(f"no copy kernel among {sorted(fetch)}")
+    copy_k = max(copy_names, key=lambda k: max(fetch[k]))
+    kb = copy_bytes / 1024.0
+    f_fetch = kb / max(fetch[copy_k])
+    f_write = kb / max(write.get(copy_k, [kb]))
+    rec = {}
+    if os.path.exists(out_json):
+        rec = json.load(open(out_json))
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        fb = statistics.median(fetch[k]) * 1024.0 * f_fetch
+        wb = statistics.median(write[k]) * 1024.0 * f_write
+        kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb, "dispatches": len(fetch[k])}
+    gemm_keys = [k for k in kernels if k.startswith("gemm_i8_kernel")]
+    gemm = kernels[gemm_keys[0]] if gemm_keys else None
+    rec[workload] = {
+        "kernel_sha": kernel_sha(),
+        "command": command,
+        "copy_kernel": copy_k,
+        "copy_bytes": copy_bytes,
+        "fetch_scale": f_fetch,
+        "write_scale": f_write,
+        "gemm_hbm_bytes_per_launch": gemm["hbm_bytes"] if gemm else None,
+        "kernels": kernels,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    return rec[workload]
+
+
+if __name__ == "__main__":
+    what = sys.argv[1]
+    if what == "stats":
+        write_stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif what == "traffic":
+        r = write_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6],
+                          " ".join(sys.argv[7:]))
+        print(json.dumps(r, indent=1))
+    else:
+        raise SystemExit(f"unknown mode {what}")
