@@ -5,7 +5,7 @@
 // §7 steps 4-6: accumulate, reduce, unscale by D^-1 and E^-1.
 //
 // 1. S_l = sum_t r_t w_{t,l}, where w_{t,l} < 2^32 are the 32-bit limbs of
-//    W_t = M_t y_t.  Each term is < 2^40 and there are at most 20, so every
+//    W_t = M_t y_t (a small device table, staged in LDS per block).  Each term is < 2^40 and there are at most 20, so every
 //    partial sum is an integer below 2^45 and FP64 fused multiply-adds are
 //    exact.
 // 2. Carry-propagate the S_l into 32-bit limbs Z_0..Z_L of Z = sum_t r_t W_t.
@@ -143,46 +143,67 @@ __device__ __forceinline__ double reconstruct(const double* S, const CrtConsts& 
 
 // Thread = 4 consecutive rows of one output column: the product residues of
 // each modulus come in as one 32-bit load (the planes are padded to whole
-// tiles, so rows up to the padded height are always readable).
+// tiles, so rows up to the padded height are always readable).  The limbs of
+// W_t sit in LDS, read once per modulus for all four rows.
 template <int L>
 __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt, int m, int n, int m_pad,
                                                    long plane, const int32_t* __restrict__ e,
                                                    const int32_t* __restrict__ f, CrtConsts c,
                                                    double* __restrict__ C, long ldc) {
+  __shared__ double wl[OZGEMM_S_MAX * MAX_LIMBS];
+  for (int idx = threadIdx.x; idx < OZGEMM_S_MAX * MAX_LIMBS; idx += 256)
+    wl[idx] = idx < c.s * MAX_LIMBS ? c.wtab[idx] : 0.0;
+  __syncthreads();
   const int i0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i0 >= m) return;
+  const int s = c.s;
   int ei[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ei[u] = (i0 + u < m) ? e[i0 + u] : 0;
+  for (int u = 0; u < 4; ++u) ei[u] = e[min(i0 + u, m - 1)];
   for (int j = blockIdx.y; j < n; j += gridDim.y) {
     const int fj = f[j];
     const uint8_t* p = rt + (long)j * m_pad + i0;
+    // residues of the four rows for every modulus (planes past s are never
+    // read: their slot loads plane s - 1 and is zeroed, as is its weight)
     uint32_t rr[OZGEMM_S_MAX];
 #pragma unroll
-    for (int t = 0; t < OZGEMM_S_MAX; ++t)
-      rr[t] = (t < c.s) ? *reinterpret_cast<const uint32_t*>(p + (long)t * plane) : 0u;
-    double* out = C + (long)j * ldc + i0;
+    for (int t = 0; t < OZGEMM_S_MAX; ++t) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(p + (long)min(t, s - 1) * plane);
+      rr[t] = (t < s) ? v : 0u;
+    }
+    // 1. exact FP64 limb sums for the four rows, moduli in groups of four
+    double S[4][L];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (i0 + u >= m) break;
-      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) {
-        out[u] = __builtin_nan("");
-        continue;
-      }
-      // 1. exact FP64 limb sums
-      double S[L];
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int l = 0; l < L; ++l) S[l] = 0.0;
+      for (int l = 0; l < L; ++l) S[u][l] = 0.0;
 #pragma unroll
-      for (int t = 0; t < OZGEMM_S_MAX; ++t) {
-        if (t < c.s) {
-          const double r = (double)((rr[t] >> (8 * u)) & 0xffu);
+    for (int tg = 0; tg < OZGEMM_S_MAX; tg += 4) {
+      if (tg < s) {
 #pragma unroll
-          for (int l = 0; l < L; ++l) S[l] = __builtin_fma(r, c.w[t][l], S[l]);
+        for (int t = tg; t < tg + 4; ++t) {
+          double w[L];
+#pragma unroll
+          for (int l = 0; l < L; ++l) w[l] = wl[t * MAX_LIMBS + l];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const double r = (double)((rr[t] >> (8 * u)) & 0xffu);
+#pragma unroll
+            for (int l = 0; l < L; ++l) S[u][l] = __builtin_fma(r, w[l], S[u][l]);
+          }
         }
       }
-      out[u] = reconstruct<L>(S, c, ei[u] + fj - 2 * c.k);
     }
+    double res[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      res[u] = reconstruct<L>(S[u], c, ei[u] + fj - 2 * c.k);
+      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res[u] = __builtin_nan("");
+    }
+    double* out = C + (long)j * ldc + i0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u < m) out[u] = res[u];
   }
 }
 

@@ -37,17 +37,21 @@ struct GemmConsts {
   double inv[OZGEMM_S_MAX];
 };
 
-// CRT constants (Ozaki II notes §4): W_t = M_t y_t < M split in 32-bit limbs,
-// stored as doubles so that sum_t r_t W_t accumulates exactly in FP64.
+// CRT constants (Ozaki II notes §4).  The 32-bit limbs of W_t = M_t y_t < M
+// are stored as doubles in a device table (wtab[t * MAX_LIMBS + l]) so that
+// sum_t r_t W_t accumulates exactly in FP64; the rest travels by value.
 struct CrtConsts {
   int s;
   int L;                             // limbs of M (top limb nonzero)
   int k;
-  double w[OZGEMM_S_MAX][MAX_LIMBS]; // limbs of W_t
+  const double* wtab;                // device: s x MAX_LIMBS limbs of W_t
   uint32_t M[MAX_LIMBS + 1];         // limbs of M (extra zero limb)
   uint32_t half[MAX_LIMBS + 1];      // limbs of M/2 (M is even: m_1 = 256)
   double invM;                       // RN(1/M)
 };
+
+// Host table of the W_t limbs for every s (wtab for s at (s - 1) * S_MAX * MAX_LIMBS).
+constexpr size_t CRT_TABLE_DOUBLES = (size_t)OZGEMM_S_MAX * OZGEMM_S_MAX * MAX_LIMBS;
 
 // Launchers (each enqueues on `st`).
 hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,

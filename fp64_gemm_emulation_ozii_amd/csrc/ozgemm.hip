@@ -159,6 +159,14 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
   big_divmod_small(M, 2, &half);
   for (int l = 0; l <= MAX_LIMBS; ++l) cc->half[l] = l < BIG_LIMBS ? half.w[l] : 0;
   cc->invM = 1.0 / big_to_double(M);
+}
+
+// W_t = M_t y_t limbs for s moduli, written to out[t * MAX_LIMBS + l].
+void crt_weights(int s, double* out) {
+  const auto& mods = moduli_list();
+  const Big M = product_M(s);
+  for (int t = 0; t < OZGEMM_S_MAX; ++t)
+    for (int l = 0; l < MAX_LIMBS; ++l) out[t * MAX_LIMBS + l] = 0.0;
   for (int t = 0; t < s; ++t) {
     Big Mt;
     const uint32_t mt = (uint32_t)mods[t];
@@ -167,7 +175,7 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
     const int y = modinv_small((int)Mt_mod, (int)mt);
     Big W = Mt;
     big_mul_small(W, (uint32_t)y);  // W_t = M_t y_t < M
-    for (int l = 0; l < MAX_LIMBS; ++l) cc->w[t][l] = (double)W.w[l];
+    for (int l = 0; l < MAX_LIMBS; ++l) out[t * MAX_LIMBS + l] = (double)W.w[l];
   }
 }
 
@@ -177,7 +185,7 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
 constexpr int NCH_MAX = 256;  // partial row-max chunks of A
 
 struct Layout {
-  size_t pmax, e, f, ares, bres, rt, total;
+  size_t consts, pmax, e, f, ares, bres, rt, total;
 };
 
 Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
@@ -191,6 +199,7 @@ Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
     off = round_up(off + bytes, 256);
     return o;
   };
+  L.consts = take(CRT_TABLE_DOUBLES * sizeof(double));
   L.pmax = take((size_t)NCH_MAX * mp * 8);
   L.e = take(mp * 4);
   L.f = take(np * 4);
@@ -208,6 +217,8 @@ struct State {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   Layout lay{};
+  bool consts_on_device = false;  // CRT weight table uploaded to the workspace
+  std::vector<double> consts_host;
   bool timing = false;
   std::vector<std::array<hipEvent_t, 5>> events;
   std::string hip_err;
@@ -228,6 +239,22 @@ int hip_fail(hipError_t err) {
     const hipError_t oz_err_ = (expr);             \
     if (oz_err_ != hipSuccess) return hip_fail(oz_err_); \
   } while (0)
+
+// The CRT weight table lives in the workspace; it is copied there once after
+// each configuration, at the first call that needs it (a blocking 16 KB copy).
+int ensure_crt_table() {
+  if (g.consts_on_device) return 0;
+  g.consts_host.assign(CRT_TABLE_DOUBLES, 0.0);
+  for (int s = 1; s <= OZGEMM_S_MAX; ++s) crt_weights(s, g.consts_host.data() + (size_t)(s - 1) * OZGEMM_S_MAX * MAX_LIMBS);
+  OZ_CHECK(hipMemcpy(g.ws + g.lay.consts, g.consts_host.data(), CRT_TABLE_DOUBLES * sizeof(double),
+                     hipMemcpyHostToDevice));
+  g.consts_on_device = true;
+  return 0;
+}
+
+const double* crt_table(int s) {
+  return reinterpret_cast<const double*>(g.ws + g.lay.consts) + (size_t)(s - 1) * OZGEMM_S_MAX * MAX_LIMBS;
+}
 
 void dims(int m, int n, int q, int* mp, int* np, int* qp) {
   *mp = (int)round_up((size_t)std::max(m, 1), ROW_PAD);
@@ -332,6 +359,7 @@ int ozgemm_config(int s_max, int max_m, int max_n, int max_q, void* hip_stream, 
   g.ws = (char*)workspace;
   g.ws_bytes = workspace_bytes;
   g.lay = lay;
+  g.consts_on_device = false;
   return OZGEMM_OK;
 }
 
@@ -409,6 +437,8 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   GemmConsts gc;
   CrtConsts cc;
   make_consts(s, q, &rc, &gc, &cc);
+  if ((st = ensure_crt_table())) return st;
+  cc.wtab = crt_table(s);
 
   std::array<hipEvent_t, 5> ev{};
   const bool timed = g.timing && g.events.size() < TIMING_MAX_CALLS;
@@ -502,6 +532,8 @@ int ozgemm_stage_crt(int m, int n, int q, int s, const uint8_t* rt, const int32_
   GemmConsts gc;
   CrtConsts cc;
   make_consts(s, q, &rc, &gc, &cc);
+  if ((st = ensure_crt_table())) return st;
+  cc.wtab = crt_table(s);
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
   return 0;
 }
