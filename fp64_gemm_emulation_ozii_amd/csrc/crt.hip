@@ -5,141 +5,18 @@
 // §7 steps 4-6: accumulate, reduce, unscale by D^-1 and E^-1.
 //
 // 1. S_l = sum_t r_t w_{t,l}, where w_{t,l} < 2^32 are the 32-bit limbs of
-//    W_t = M_t y_t (a small device table, staged in LDS per block).  Each term is < 2^40 and there are at most 20, so every
-//    partial sum is an integer below 2^45 and FP64 fused multiply-adds are
-//    exact.
-// 2. Carry-propagate the S_l into 32-bit limbs Z_0..Z_L of Z = sum_t r_t W_t.
-// 3. Q = rint(Z / M) from a double estimate (Z < 20*255*M, so the estimate
-//    is within 2^-38 of Z/M and Q is right or off by one); X = Z - Q M in
-//    two's complement limbs; one exact comparison against M/2 fixes an
-//    off-by-one Q, giving the unique X with |X| < M/2.
-// 4. C_ij = X * 2^(e_i + f_j - 2k) rounded once to nearest-even from a
-//    64-bit window of |X| plus a sticky bit, with the rounding position moved
-//    up for subnormal results and +-Inf past the double range.
+//    W_t = M_t y_t (a small device table, staged in LDS per block).  Each
+//    term is < 2^40 and there are at most 20, so every partial sum is an
+//    integer below 2^45 and FP64 fused multiply-adds are exact.
+// 2. The limb sums go to reconstruct_limbs (crt_reconstruct.h): balanced
+//    carries, X = Z - Q M with Q = rint(Z / M), one exact shift by M into
+//    (-M/2, M/2), and a single rounding of X * 2^(e_i + f_j - 2k) to
+//    nearest-even (subnormal and overflowing results included).
 #include "oz_internal.h"
 
 namespace oz {
 
 namespace {
-
-// Round |X| * 2^(E - 63) to the nearest double, where T holds the 64 leading
-// bits of |X| (bit 63 set) and `sticky` tells whether any lower bit is set.
-__device__ __forceinline__ double round_window(uint64_t T, bool sticky, int E) {
-  if (E >= 1024) return __builtin_inf();
-  const int keep = min(53, E + 1075);  // significant bits the result can hold
-  if (keep <= 0) {
-    if (keep == 0) {
-      // value in [2^-1075, 2^-1074): above the tie -> smallest subnormal
-      const bool above = ((T << 1) != 0) || sticky;
-      return above ? 4.9406564584124654e-324 : 0.0;
-    }
-    return 0.0;
-  }
-  const int drop = 64 - keep;  // 11..63
-  const uint64_t mant = T >> drop;
-  const uint64_t rem = T & ((1ull << drop) - 1);
-  const uint64_t halfv = 1ull << (drop - 1);
-  const bool up = (rem > halfv) || (rem == halfv && (sticky || (mant & 1)));
-  return __builtin_ldexp((double)(mant + (up ? 1 : 0)), E - keep + 1);
-}
-
-// X * 2^(ei + fj - 2k) rounded once, from the exact limb sums S[0..L-1] of
-// Z = sum_t r_t W_t (steps 2-4 above).
-template <int L>
-__device__ __forceinline__ double reconstruct(const double* S, const CrtConsts& c, int scale) {
-  // 2. carries -> Z[0..L]
-  uint32_t Z[L + 1];
-  uint64_t carry = 0;
-#pragma unroll
-  for (int l = 0; l < L; ++l) {
-    const uint32_t hi = (uint32_t)(S[l] * 0x1p-32);
-    const uint32_t lo = (uint32_t)(S[l] - (double)hi * 0x1p32);
-    const uint64_t v = (uint64_t)lo + carry;
-    Z[l] = (uint32_t)v;
-    carry = (v >> 32) + hi;
-  }
-  Z[L] = (uint32_t)carry;
-
-  // 3. X = Z - Q M, then exact fix-up into (-M/2, M/2)
-  double zf = (double)Z[L] * __builtin_ldexp(1.0, 32 * L) + (double)Z[L - 1] * __builtin_ldexp(1.0, 32 * (L - 1));
-  if (L >= 2) zf += (double)Z[L - 2] * __builtin_ldexp(1.0, 32 * (L - 2));
-  const uint32_t Q = (uint32_t)__builtin_rint(zf * c.invM);
-  uint32_t X[L + 1];
-  {
-    uint64_t pc = 0;     // carry of Q*M
-    int64_t borrow = 0;  // 0 or -1
-#pragma unroll
-    for (int l = 0; l <= L; ++l) {
-      const uint64_t pm = (uint64_t)Q * c.M[l] + pc;
-      pc = pm >> 32;
-      const int64_t d = (int64_t)Z[l] - (int64_t)(uint32_t)pm + borrow;
-      X[l] = (uint32_t)d;
-      borrow = d < 0 ? -1 : 0;
-    }
-  }
-  const bool neg0 = (X[L] >> 31) != 0;
-  {
-    // D = X - M/2 (if X >= 0) or X + M/2 (if X < 0); fix when D has X's sign
-    uint32_t Dtop = 0;
-    int64_t cb = 0;
-#pragma unroll
-    for (int l = 0; l <= L; ++l) {
-      const int64_t d = neg0 ? (int64_t)X[l] + (int64_t)c.half[l] + cb : (int64_t)X[l] - (int64_t)c.half[l] + cb;
-      Dtop = (uint32_t)d;
-      cb = d >> 32;  // arithmetic: carry 1, borrow -1, or 0
-    }
-    const bool dneg = (Dtop >> 31) != 0;
-    // X >= 0 and X - M/2 >= 0 (never == 0): X -= M;  X < 0 and X + M/2 < 0: X += M
-    const bool fix = neg0 ? dneg : !dneg;
-    if (fix) {
-      int64_t cc = 0;
-#pragma unroll
-      for (int l = 0; l <= L; ++l) {
-        const int64_t d = neg0 ? (int64_t)X[l] + (int64_t)c.M[l] + cc : (int64_t)X[l] - (int64_t)c.M[l] + cc;
-        X[l] = (uint32_t)d;
-        cc = d >> 32;
-      }
-    }
-  }
-  const bool neg = (X[L] >> 31) != 0;
-  if (neg) {  // magnitude
-    uint64_t cc = 1;
-#pragma unroll
-    for (int l = 0; l <= L; ++l) {
-      const uint64_t v = (uint64_t)(~X[l]) + cc;
-      X[l] = (uint32_t)v;
-      cc = v >> 32;
-    }
-  }
-
-  // 4. normalise so that X[L] holds the leading nonzero limb, then round
-  int h = L;
-#pragma unroll
-  for (int it = 0; it < L; ++it) {
-    if (X[L] == 0) {
-#pragma unroll
-      for (int l = L; l > 0; --l) X[l] = X[l - 1];
-      X[0] = 0;
-      --h;
-    }
-  }
-  if (X[L] == 0) return 0.0;
-  const int lz = __clz(X[L]);
-  const uint64_t hi64 = ((uint64_t)X[L] << 32) | (uint64_t)X[L - 1];
-  const uint32_t lo32 = (L >= 2) ? X[L - 2] : 0u;
-  uint64_t T = hi64;
-  uint32_t rest = lo32;
-  if (lz > 0) {
-    T = (hi64 << lz) | (uint64_t)(lo32 >> (32 - lz));
-    rest = lo32 << lz;
-  }
-  bool sticky = rest != 0;
-#pragma unroll
-  for (int l = 0; l + 3 <= L; ++l) sticky = sticky || (X[l] != 0);
-  const int E = 32 * h + 31 - lz + scale;  // exponent of the leading bit of |X| 2^scale
-  const double res = round_window(T, sticky, E);
-  return neg ? -res : res;
-}
 
 // Thread = 4 consecutive rows of one output column: the product residues of
 // each modulus come in as one 32-bit load (the planes are padded to whole
@@ -197,7 +74,7 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
     double res[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      res[u] = reconstruct<L>(S[u], c, ei[u] + fj - 2 * c.k);
+      res[u] = reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
       if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res[u] = __builtin_nan("");
     }
     double* out = C + (long)j * ldc + i0;

@@ -6,6 +6,7 @@
 #include <stddef.h>
 
 #include "../../include/ozgemm.h"
+#include "crt_reconstruct.h"
 
 namespace oz {
 
@@ -45,9 +46,7 @@ struct CrtConsts {
   int L;                             // limbs of M (top limb nonzero)
   int k;
   const double* wtab;                // device: s x MAX_LIMBS limbs of W_t
-  uint32_t M[MAX_LIMBS + 1];         // limbs of M (extra zero limb)
-  uint32_t half[MAX_LIMBS + 1];      // limbs of M/2 (M is even: m_1 = 256)
-  double invM;                       // RN(1/M)
+  CrtModulus K;                      // limbs of M and M/2, M/2, 1/M
 };
 
 // Host table of the W_t limbs for every s (wtab for s at (s - 1) * S_MAX * MAX_LIMBS).

@@ -154,11 +154,14 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
   const Big M = product_M(s);
   const int bits = big_bitlen(M);
   cc->L = (bits + 31) / 32;
-  for (int l = 0; l <= MAX_LIMBS; ++l) cc->M[l] = l < BIG_LIMBS ? M.w[l] : 0;
   Big half;
   big_divmod_small(M, 2, &half);
-  for (int l = 0; l <= MAX_LIMBS; ++l) cc->half[l] = l < BIG_LIMBS ? half.w[l] : 0;
-  cc->invM = 1.0 / big_to_double(M);
+  for (int l = 0; l < MAX_LIMBS; ++l) {
+    cc->K.Ml[l] = l < BIG_LIMBS ? (double)M.w[l] : 0.0;
+    cc->K.Hl[l] = l < BIG_LIMBS ? (double)half.w[l] : 0.0;
+  }
+  cc->K.halfM = big_to_double(half);
+  cc->K.invM = 1.0 / big_to_double(M);
 }
 
 // W_t = M_t y_t limbs for s moduli, written to out[t * MAX_LIMBS + l].
