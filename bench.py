@@ -201,18 +201,14 @@ def main():
         return Cd[c][:, r].cpu().numpy().T
 
     if not args.no_accuracy:
-        from oracle import ozaki2 as oz
+        from fp64_gemm_emulation_ozii_amd.accuracy import correct_bits
         rng = np.random.default_rng(3)
         ri = rng.integers(0, m, size=24)
         ci = rng.integers(0, n, size=24)
-        Cg = np.array([block_getter(np.array([i]), np.array([j]))[0, 0] for i, j in zip(ri, ci)])
-        Cfull = np.zeros((m, n))
-        Cfull[ri, ci] = Cg
-        out["correct_bits"] = round(oz.correct_bits(Cfull, A, B, ri, ci), 2)
+        Cg = Cd.T[torch.from_numpy(ri).to(dev), torch.from_numpy(ci).to(dev)].cpu().numpy()
+        out["correct_bits"] = round(correct_bits(Cg, A, B, ri, ci), 2)
         native = (torch.from_numpy(A[ri, :]).to(dev) * torch.from_numpy(B[:, ci].T.copy()).to(dev)).sum(1)
-        Cn = np.zeros((m, n))
-        Cn[ri, ci] = native.cpu().numpy()
-        out["correct_bits_native_fp64_dot"] = round(oz.correct_bits(Cn, A, B, ri, ci), 2)
+        out["correct_bits_native_fp64_dot"] = round(correct_bits(native.cpu().numpy(), A, B, ri, ci), 2)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter)

@@ -1,0 +1,147 @@
+"""Accuracy and phase-time measurement of the emulated DGEMM.
+
+Correct bits of an output entry are -log2(|C_ij - (AB)_ij| / (|A||B|)_ij),
+with (AB)_ij and (|A||B|)_ij formed exactly in integer arithmetic from the
+binary expansions of the doubles; over a set of entries the worst one
+counts.  This is the componentwise measure behind the error bound of the
+Ozaki II notes (§5: the truncation error of A' and B' relative to
+|A||B|), and 64 means exact everywhere.
+
+Command line (runs on the GPU)::
+
+    python -m fp64_gemm_emulation_ozii_amd.accuracy --m 1024 --n 1024 --q 1024 \
+        --s 8,10,12,14,16,18 --phi 0.5 [--entries 64] [--out table.json]
+
+prints one JSON object per (s, phi) with the correct bits of the emulation
+and of the native FP64 dot products on the same entries, and the time of
+each phase (scale, residue, GEMM, CRT) in milliseconds.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+from fractions import Fraction
+
+import numpy as np
+
+
+def _int_terms(v: np.ndarray):
+    """Each double as (integer mantissa, exponent): v = mant * 2^expo."""
+    mant, expo = np.frexp(np.asarray(v, dtype=np.float64))
+    return (mant * float(1 << 53)).astype(np.int64), expo.astype(np.int64) - 53
+
+
+def _exact_sum_products(a: np.ndarray, b: np.ndarray):
+    """sum_l a_l b_l exactly, as (N, p) meaning N * 2^p."""
+    ma, ea = _int_terms(a)
+    mb, eb = _int_terms(b)
+    nz = (ma != 0) & (mb != 0)
+    if not nz.any():
+        return 0, 0
+    ma, ea, mb, eb = ma[nz], ea[nz], mb[nz], eb[nz]
+    ex = ea + eb
+    p = int(ex.min())
+    total = 0
+    for x, y, e in zip(ma.tolist(), mb.tolist(), (ex - p).tolist()):
+        total += (x * y) << e
+    return total, p
+
+
+def entry_error(c: float, a: np.ndarray, b: np.ndarray):
+    """|c - a.b| / (|a|.|b|) as a Fraction (None when |a|.|b| = 0)."""
+    N, p = _exact_sum_products(a, b)
+    D, pd = _exact_sum_products(np.abs(a), np.abs(b))
+    if D == 0:
+        return None
+    exact = Fraction(N) * Fraction(2) ** p
+    denom = Fraction(D) * Fraction(2) ** pd
+    if not math.isfinite(c):
+        return Fraction(1 << 64)
+    return abs(Fraction(c) - exact) / denom
+
+
+def correct_bits(values, A: np.ndarray, B: np.ndarray, rows, cols) -> float:
+    """Worst-entry correct bits of values[k] = C[rows[k], cols[k]]."""
+    worst = Fraction(0)
+    for c, i, j in zip(values, rows, cols):
+        err = entry_error(float(c), A[i, :], B[:, j])
+        if err is not None and err > worst:
+            worst = err
+    return 64.0 if worst == 0 else -math.log2(float(worst))
+
+
+def _parse_list(text: str, conv):
+    return [conv(x) for x in text.split(",") if x.strip()]
+
+
+def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats):
+    import torch
+
+    from . import ozgemm as L
+    from .synthetic import hpl_like
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(12345)
+    rows = rng.integers(0, m, size=entries)
+    cols = rng.integers(0, n, size=entries)
+    results = []
+    for phi in phi_list:
+        A, B = hpl_like(m, q, n, phi, seed=seed)
+        Ad = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)
+        Bd = torch.from_numpy(np.ascontiguousarray(B.T)).to(dev)
+        Cd = torch.empty((n, m), dtype=torch.float64, device=dev)
+        native = (torch.from_numpy(A[rows, :]).to(dev) * torch.from_numpy(B[:, cols].T.copy()).to(dev)).sum(1)
+        native_bits = correct_bits(native.cpu().numpy(), A, B, rows, cols)
+        L.ozgemm_config(max(s_list), m, n, q, stream=torch.cuda.current_stream())
+        for s in s_list:
+            L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)  # warm-up
+            torch.cuda.synchronize()
+            L.ozgemm_timing(True)
+            for _ in range(repeats):
+                L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+            torch.cuda.synchronize()
+            phase_ms, calls = L.ozgemm_phase_ms()
+            L.ozgemm_timing(False)
+            per = [x / max(calls, 1) for x in phase_ms]
+            Cs = Cd.T[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)].cpu().numpy()
+            rec = {
+                "m": m, "n": n, "q": q, "s": s, "phi": phi, "k": L.ozgemm_kbits(s, q),
+                "correct_bits": round(correct_bits(Cs, A, B, rows, cols), 2),
+                "correct_bits_native_fp64": round(native_bits, 2),
+                "entries": int(entries),
+                "phases_ms": {"scale": round(per[0], 4), "residue": round(per[1], 4),
+                              "gemm": round(per[2], 4), "crt": round(per[3], 4)},
+                "total_ms": round(sum(per), 4),
+                "fp64_tflops": round(2.0 * m * n * q / (sum(per) * 1e-3) / 1e12, 2),
+            }
+            print(json.dumps(rec), flush=True)
+            results.append(rec)
+        L.ozgemm_free()
+        del Ad, Bd, Cd
+        torch.cuda.empty_cache()
+    return results
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--m", type=int, default=1024)
+    p.add_argument("--n", type=int, default=1024)
+    p.add_argument("--q", type=int, default=1024)
+    p.add_argument("--s", type=str, default="8,9,10,11,12,13,14,15,16,17,18")
+    p.add_argument("--phi", type=str, default="0.5")
+    p.add_argument("--entries", type=int, default=64)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--repeats", type=int, default=5)
+    p.add_argument("--out", type=str, default="")
+    a = p.parse_args(argv)
+    res = run_sweep(a.m, a.n, a.q, _parse_list(a.s, int), _parse_list(a.phi, float), a.entries, a.seed, a.repeats)
+    if a.out:
+        with open(a.out, "w") as fh:
+            json.dump(res, fh, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,7 +16,6 @@ constexpr int ROW_PAD = 256;
 constexpr int K_PAD = 128;
 constexpr int MAX_LIMBS = 5;      // 32-bit limbs of M: log2 M < 160 for s <= 20
 constexpr int SCALE_CHUNK = 128;  // columns of A per partial row-max block
-constexpr int MAX_SHIFT = 32;     // |A'| < 2^(53 + MAX_SHIFT); k <= 78 for s <= 20
 
 inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
 
@@ -28,7 +27,7 @@ struct ResidueConsts {
   int lo[OZGEMM_S_MAX];         // -floor(m/2)
   int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1
   double inv[OZGEMM_S_MAX];     // RN(1/m)
-  uint8_t pow2[OZGEMM_S_MAX][MAX_SHIFT];  // 2^sh mod m, sh < MAX_SHIFT
+  double c32[OZGEMM_S_MAX];     // 2^32 mod m
 };
 
 // Per-modulus constants for the GEMM epilogue.

@@ -145,11 +145,7 @@ void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc)
     rc->lo[t] = -(m / 2);
     rc->hi[t] = (m + 1) / 2 - 1;
     rc->inv[t] = gc->inv[t] = 1.0 / (double)m;
-    int p = 1 % m;
-    for (int sh = 0; sh < MAX_SHIFT; ++sh) {
-      rc->pow2[t][sh] = (uint8_t)p;
-      p = (p * 2) % m;
-    }
+    rc->c32[t] = (double)((1ull << 32) % (unsigned long long)m);
   }
   const Big M = product_M(s);
   const int bits = big_bitlen(M);

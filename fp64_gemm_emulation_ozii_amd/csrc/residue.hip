@@ -22,8 +22,11 @@
 // m = 256 every step is exact: with k <= 50 the floor is therefore always
 // the exact one and r = fma(-q, m, A') needs no correction.  For
 // 50 < k <= 53 the quotient can be off by one and one +-m correction is
-// applied.  When k > 53, A' = u * 2^sh with u < 2^53 and
-// A' mod m = (u mod m)(2^sh mod m) mod m.
+// applied.  When k > 53 (|A'| < 2^78 since k <= 77 for s <= 20), A' is split
+// once per element as A' = h 2^32 + l with h = floor(A' 2^-32) (|h| < 2^46)
+// and 0 <= l < 2^32, both exact; per modulus, r_h = smod(h) needs no
+// correction (|h| < 2^50), v = r_h (2^32 mod m) + l is an exact integer below
+// 2^34, and r = smod(v) again needs none.
 #include "oz_internal.h"
 
 namespace oz {
@@ -43,6 +46,12 @@ __device__ __forceinline__ int smod_small(double a, int m, double inv, int lo, i
     ri = ri < lo ? ri + m : ri;
   }
   return ri;
+}
+
+// Same without correction, kept in FP64 (|a| < 2^50).
+__device__ __forceinline__ double smod_exact_d(double a, double m, double inv) {
+  const double qf = __builtin_floor(__builtin_fma(a, inv, 0.5));
+  return __builtin_fma(-qf, m, a);
 }
 
 template <bool ROWS_CONTIG, int MODE>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
@@ -112,14 +121,12 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
   }
 
   constexpr bool BIG = MODE == 2;
-  int sh[16];
+  double ahi[BIG ? 16 : 1];
   if (BIG) {
-    // A' = u * 2^sh with |u| < 2^53 (sh = 0 when |A'| < 2^53)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int ebits = (int)(((uint64_t)__double_as_longlong(a[j]) >> 52) & 0x7ff) - 1023;
-      sh[j] = max(0, ebits - 52);
-      a[j] = __builtin_ldexp(a[j], -sh[j]);
+      ahi[j] = __builtin_floor(a[j] * 0x1p-32);
+      a[j] = __builtin_fma(ahi[j], -0x1p32, a[j]);  // low part, in [0, 2^32)
     }
   }
 
@@ -131,13 +138,12 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      int ri = smod_small<MODE != 0>(a[j], m, inv, lo, hi);
+      int ri;
       if (BIG) {
-        int v = ri * (int)c.pow2[t][sh[j]];
-        v = v % m;  // in (-m, m)
-        v = v > hi ? v - m : v;
-        v = v < lo ? v + m : v;
-        ri = v;
+        const double rh = smod_exact_d(ahi[j], (double)m, inv);
+        ri = smod_small<false>(__builtin_fma(rh, c.c32[t], a[j]), m, inv, lo, hi);
+      } else {
+        ri = smod_small<MODE != 0>(a[j], m, inv, lo, hi);
       }
       packed[j >> 2] |= ((uint32_t)ri & 0xffu) << (8 * (j & 3));
     }
