@@ -1,4 +1,5 @@
-"""CPU oracle for the Ozaki Scheme II FP64 GEMM emulation.
+"""CPU oracle for FP64 GEMM emulation by Ozaki Scheme II (``ozaki2``) and by
+the Scheme I slice split (``ozaki1``).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call, link
 or execute anything in this directory.  The only permitted users are the
