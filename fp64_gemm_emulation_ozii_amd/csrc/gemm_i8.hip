@@ -1,29 +1,27 @@
-// Per-modulus exact int8 GEMM on gfx950 matrix cores, with the product
-// re-reduction fused into the epilogue.
+// Exact int8 GEMMs on gfx950 matrix cores: one per modulus for Scheme II
+// (with the product re-reduction fused into the epilogue), and the slice
+// products of the Scheme I path.
 //
 // Ozaki II notes §4: one product C'_t = A'_t B'_t per modulus and no cross
 // terms; §6: int8 residues with int32 accumulation are exact while
 // q < 2^17 (|dot| <= q 2^14 < 2^31); §7 step 3: C''_t = C'_t mod m_t;
-// §15: the independent moduli are batched into one launch (grid z = t).
+// §15: the independent moduli are batched into one launch.  Ozaki I notes
+// (INT matrix multiplication algorithm, group-wise accumulation): slice
+// products A_s B_t, optionally several with the same s + t summed into one
+// int32 accumulator.
 //
-// Operands are the K-contiguous residue planes written by the residue step:
-// A_t is m_pad x q_pad (row i at i*q_pad), B_t is n_pad x q_pad (column j of
-// B at j*q_pad), so the product is A_t B_t^T.  A block computes a BM x BN
-// output tile with four wavefronts (2 x 2), each owning (BM/2) x (BN/2)
-// built from 16x16 int32 tiles of v_mfma_i32_16x16x64_i8.
-//
-// Per 64-wide K slice, lane l of an MFMA supplies 16 bytes of row (l mod 16)
-// of A and the same 16 K positions of column (l mod 16) of B, taken from
-// K chunk (l / 16).  Both operands use the same lane -> K mapping, so every
-// K index pairs with itself and the sum over the slice is the dot product
-// whatever order the hardware walks the bytes in.  The int32 result tile
-// holds rows 4*(l/16) + r, r = 0..3, of column (l mod 16) in lane l.
+// Operands are K-contiguous int8 planes: A_t is m_pad x q_pad (row i at
+// i*q_pad), B_t is n_pad x q_pad (column j of B at j*q_pad), so each product
+// is A_t B_t^T.  A block computes a BM x BN output tile with four wavefronts
+// (2 x 2), each owning (BM/2) x (BN/2) built from 32x32 int32 tiles of
+// v_mfma_i32_32x32x32_i8.  In the multi-product form an output plane is the
+// sum of `count` products (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one
+// long K loop.
 //
 // LDS: each tile row (BK bytes) is stored as 16-byte chunks whose position
-// is XOR-permuted by a function of the row, so that the 16 consecutive rows
-// an MFMA operand load touches fall in distinct bank groups.  Two buffers:
-// the next K slice is fetched from HBM into registers while the current
-// one feeds the matrix cores, then written to the other buffer.
+// is XOR-permuted by a function of the row, so that the rows an MFMA operand
+// load touches fall in distinct bank groups.  K slices move from HBM straight
+// into LDS through STAGES buffers.
 #include "oz_internal.h"
 
 namespace oz {
@@ -111,10 +109,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 //  * One barrier per slice, placed before the last step's MFMAs: it publishes
 //    the next slice (after this wave's loads for it have landed) and retires
 //    the current buffer (after this wave's reads of it are in registers).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT, bool MULTI>
 __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
     const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
-    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt) {
+    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
   constexpr int ROWS_PER_KB = 1024 / BK;        // tile rows filled by one wavefront load
@@ -138,8 +136,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   tile_of_block<4>(blockIdx.x, m_pad / BM, n_pad / BN, t, mi, nj);
   const int m0 = mi * BM, n0 = nj * BN;
 
-  const int8_t* Ag = Ares + (long)t * m_pad * q_pad + (long)m0 * q_pad;
-  const int8_t* Bg = Bres + (long)t * n_pad * q_pad + (long)n0 * q_pad;
+  // operand planes: (t, t) once, or (a0 + u, b0 - u) for u < count
+  const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad;
+  int a0 = t, b0 = t, count = 1, out_t = t;
+  if (MULTI) {
+    const int4 pl = plan[t];
+    a0 = pl.x;
+    b0 = pl.y;
+    count = pl.z;
+    out_t = pl.w;
+  }
+  const int8_t* Ag = Ares + (long)a0 * a_plane + (long)m0 * q_pad;
+  const int8_t* Bg = Bres + (long)b0 * b_plane + (long)n0 * q_pad;
 
   // A wavefront load fills 1 KB of LDS = ROWS_PER_KB whole tile rows, lane l
   // landing in row l / CPR, physical chunk l mod CPR.  The swizzle depends on
@@ -149,11 +157,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   const int lane_src1 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb + ROWS_PER_KB)) * 16);
   const long kb_stride = (long)ROWS_PER_KB * q_pad;  // source distance of consecutive 1 KB loads
 
-  auto issue = [&](int buf, int k0) {
+  const int nk = q_pad / BK;  // K slices per product
+  auto issue = [&](int buf, int kk) {
     int8_t* As = smem + buf * (BM + BN) * BK;
     int8_t* Bs = As + BM * BK;
-    const int8_t* ga = Ag + (long)(wave * A_LOADS) * kb_stride + k0;
-    const int8_t* gb = Bg + (long)(wave * B_LOADS) * kb_stride + k0;
+    const int8_t* ga = Ag;
+    const int8_t* gb = Bg;
+    int k0 = kk * BK;
+    if (MULTI) {
+      const int u = kk / nk;
+      k0 = (kk - u * nk) * BK;
+      ga += u * a_plane;
+      gb -= u * b_plane;
+    }
+    ga += (long)(wave * A_LOADS) * kb_stride + k0;
+    gb += (long)(wave * B_LOADS) * kb_stride + k0;
 #pragma unroll
     for (int p = 0; p < A_LOADS; ++p)
       __builtin_amdgcn_global_load_lds(ga + p * kb_stride + (((wave * A_LOADS + p) & 1) ? lane_src1 : lane_src0),
@@ -188,16 +206,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int nk = q_pad / BK;
+  const int nkt = nk * count;  // K slices of the whole output plane
 #pragma unroll
-  for (int sidx = 0; sidx < STAGES - 1; ++sidx) issue(sidx, min(sidx, nk - 1) * BK);
+  for (int sidx = 0; sidx < STAGES - 1; ++sidx) issue(sidx, min(sidx, nkt - 1));
   wait_vmcnt<(STAGES - 2) * LPW>();
   __builtin_amdgcn_s_barrier();
 
   v4i acur[FM], bcur[FN], anxt[FM], bnxt[FN];
   read(0, 0, acur, bcur);
-  for (int kt = 0; kt < nk; ++kt) {
-    issue((kt + STAGES - 1) % STAGES, min(kt + STAGES - 1, nk - 1) * BK);
+  for (int kt = 0; kt < nkt; ++kt) {
+    issue((kt + STAGES - 1) % STAGES, min(kt + STAGES - 1, nkt - 1));
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 1 < NKS) {
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = m0 + wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
-        const long off = (long)t * plane + (long)col * m_pad + row;
+        const long off = (long)out_t * plane + (long)col * m_pad + row;
         const v16i& v = acc[i][j];
         if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
         if (WRITE_RT) {
@@ -270,14 +288,27 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   const int nblocks = (n_pad / BN) * (m_pad / BM) * c.s;
   const dim3 grid(nblocks), block(WM * WN * 64);
   if (Ct != nullptr && rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, true>), grid, block, 0, st, Ares, Bres, m_pad,
-                       n_pad, q_pad, c, Ct, rt);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, true, false>), grid, block, 0, st, Ares, Bres,
+                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
   else if (Ct != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false>), grid, block, 0, st, Ares, Bres,
-                       m_pad, n_pad, q_pad, c, Ct, rt);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, false>), grid, block, 0, st, Ares,
+                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
   else if (rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true>), grid, block, 0, st, Ares, Bres,
-                       m_pad, n_pad, q_pad, c, Ct, rt);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false>), grid, block, 0, st, Ares,
+                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m_pad, int n_pad, int q_pad,
+                             const int4* plan, int nout, int32_t* P, hipStream_t st) {
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, STAGES = 2;
+  if (m_pad % BM || n_pad % BN || q_pad % BK || nout < 1) return hipErrorInvalidValue;
+  GemmConsts none{};
+  none.s = 1;
+  none.m[0] = 2;
+  const int nblocks = (n_pad / BN) * (m_pad / BM) * nout;
+  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, true>), dim3(nblocks),
+                     dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan);
   return hipGetLastError();
 }
 

@@ -67,6 +67,23 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad,
                        const GemmConsts& c, int32_t* Ct, uint8_t* rt, hipStream_t st);
 
+// Scheme I slice products: output plane plan[o].w (m_pad x n_pad int32, [j][i])
+// = sum over u < plan[o].z of A_{plan[o].x + u} B_{plan[o].y - u}^T.
+hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m_pad, int n_pad, int q_pad,
+                             const int4* plan, int nout, int32_t* P, hipStream_t st);
+
+// Scheme I split and accumulation (scheme1.hip).
+hipError_t launch_s1_rowmax(const double* X, int rows, int q, long rs, long ls, int rows_pad, int q_pad,
+                            uint64_t* pmax, hipStream_t st);
+hipError_t launch_s1_grid(const uint64_t* pmax, int rows_pad, int nchunks, int beta, int32_t* gout, hipStream_t st);
+hipError_t launch_s1_split(const double* X, int rows, int q, long rs, long ls, const int32_t* g, int rows_pad,
+                           int q_pad, int variant, int pass, int k, int beta, int8_t* planes, uint64_t* pmax,
+                           hipStream_t st);
+hipError_t launch_s1_plan(int variant, int k, int r, int beta, int4* gemm_plan, int4* acc_plan, hipStream_t st);
+hipError_t launch_s1_accum(const int32_t* P, int m, int n, int m_pad, int n_pad, int nout, const int4* acc,
+                           const int32_t* gA, int ma_pad, const int32_t* gB, int nb_pad, double* C, int ldc,
+                           hipStream_t st);
+
 hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e,
                       const int32_t* f, const CrtConsts& c, double* C, int ldc, hipStream_t st);
 

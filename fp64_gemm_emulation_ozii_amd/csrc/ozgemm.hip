@@ -327,6 +327,102 @@ int run_residue(int m, int n, int q, int s, const double* A, int lda, const doub
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Scheme I (slice split) helpers
+// ---------------------------------------------------------------------------
+
+// beta = min(7, floor((31 - log2 q) / 2)) as the largest b <= 7 with
+// q 4^b <= 2^31 (Ozaki I notes, RN split analysis); -1 when no b >= 1 fits.
+int s1_beta(int q) {
+  if (q < 1) return -1;
+  int b = 0;
+  while (b < 7 && (int64_t)q * ((int64_t)1 << (2 * (b + 1))) <= ((int64_t)1 << 31)) ++b;
+  return b >= 1 ? b : -1;
+}
+
+// r = max(1, 2^(31 - 2 beta - ceil(log2 q))) (Ozaki I notes, direction 2).
+int s1_group(int q, int beta) {
+  const int c = (q <= 1) ? 0 : 32 - __builtin_clz((unsigned)(q - 1));
+  const int e = 31 - 2 * beta - c;
+  return e >= 0 ? std::max(1, 1 << e) : 1;
+}
+
+int s1_nout(int k, int variant, int r) {
+  if (variant == OZGEMM_S1_RN) return k * (k + 1) / 2;
+  int total = 0;
+  for (int gg = 2; gg <= k + 1; ++gg) total += (gg - 1 + r - 1) / r;
+  return total;
+}
+
+struct S1Layout {
+  size_t plans, gA, gB, pmax, asl, bsl, P, total;  // offsets from the Scheme I base
+  int mp, np, qp, grid_rows, nout, nch, beta, r;
+};
+
+S1Layout s1_layout(int m, int n, int q, int k, int variant) {
+  S1Layout L{};
+  dims(m, n, q, &L.mp, &L.np, &L.qp);
+  L.beta = s1_beta(std::max(q, 1));
+  L.r = s1_group(std::max(q, 1), std::max(L.beta, 1));
+  L.grid_rows = variant == OZGEMM_S1_RN ? k : 1;
+  L.nout = s1_nout(k, variant, L.r);
+  L.nch = L.qp / 128;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L.plans = take(2 * OZGEMM_S1_MAX_OUT * sizeof(int4));
+  L.gA = take((size_t)L.grid_rows * L.mp * 4);
+  L.gB = take((size_t)L.grid_rows * L.np * 4);
+  L.pmax = take((size_t)L.nch * std::max(L.mp, L.np) * 8);
+  L.asl = take((size_t)k * L.mp * L.qp);
+  L.bsl = take((size_t)k * L.np * L.qp);
+  L.P = take((size_t)L.nout * L.mp * L.np * 4);
+  L.total = off;
+  return L;
+}
+
+// Scheme I scratch starts after the constant table shared with Scheme II.
+size_t s1_base() { return round_up(CRT_TABLE_DOUBLES * sizeof(double), 256); }
+
+int s1_check(int k, int variant, int q) {
+  if (k < 1 || k > OZGEMM_S1_K_MAX) return -1;
+  if (variant != OZGEMM_S1_RN && variant != OZGEMM_S1_HYBRID) return -2;
+  if (q > 0 && s1_beta(q) < 1) return OZGEMM_RANGE;
+  return 0;
+}
+
+// Split of A (rows) and B (columns) into slices and grid exponents.
+int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const double* A, int lda, const double* B,
+             int ldb, int8_t* Asl, int8_t* Bsl, int32_t* gA, int32_t* gB, uint64_t* pmax) {
+  struct Side {
+    const double* X;
+    int rows;
+    long rs, ls;
+    int rp;
+    int8_t* sl;
+    int32_t* gr;
+  } sides[2] = {{A, m, 1, (long)lda, L.mp, Asl, gA}, {B, n, (long)ldb, 1, L.np, Bsl, gB}};
+  for (const Side& sd : sides) {
+    OZ_CHECK(launch_s1_rowmax(sd.X, sd.rows, q, sd.rs, sd.ls, sd.rp, L.qp, pmax, g.stream));
+    OZ_CHECK(launch_s1_grid(pmax, sd.rp, L.nch, L.beta, sd.gr, g.stream));
+    if (variant == OZGEMM_S1_RN) {
+      for (int p = 0; p < k; ++p) {
+        const bool more = p + 1 < k;
+        OZ_CHECK(launch_s1_split(sd.X, sd.rows, q, sd.rs, sd.ls, sd.gr, sd.rp, L.qp, variant, p, k, L.beta, sd.sl,
+                                 more ? pmax : nullptr, g.stream));
+        if (more) OZ_CHECK(launch_s1_grid(pmax, sd.rp, L.nch, L.beta, sd.gr + (size_t)(p + 1) * sd.rp, g.stream));
+      }
+    } else {
+      OZ_CHECK(launch_s1_split(sd.X, sd.rows, q, sd.rs, sd.ls, sd.gr, sd.rp, L.qp, variant, 0, k, L.beta, sd.sl,
+                               nullptr, g.stream));
+    }
+  }
+  return 0;
+}
+
 }  // namespace
 }  // namespace oz
 
@@ -534,6 +630,133 @@ int ozgemm_stage_crt(int m, int n, int q, int s, const uint8_t* rt, const int32_
   if ((st = ensure_crt_table())) return st;
   cc.wtab = crt_table(s);
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
+  return 0;
+}
+
+int ozgemm_scheme1_beta(int q) { return s1_beta(q); }
+
+int ozgemm_scheme1_outputs(int k, int variant, int q) {
+  int st = s1_check(k, variant, q);
+  if (st) return st < 0 ? st : -3;
+  const int beta = s1_beta(std::max(q, 1));
+  return s1_nout(k, variant, s1_group(std::max(q, 1), beta));
+}
+
+size_t ozgemm_scheme1_workspace_bytes(int m, int n, int q, int k, int variant) {
+  if (m < 0 || n < 0 || q < 0 || s1_check(k, variant, q) != 0) return 0;
+  return s1_base() + s1_layout(m, n, q, k, variant).total;
+}
+
+int ozgemm_scheme1_dgemm(int m, int n, int q, const double* A, int lda, const double* B, int ldb, double* C,
+                         int ldc, int k, int variant) {
+  int st = check_common(m, n, q, A, lda, B, ldb);
+  if (st) return st;
+  if (C == nullptr && m > 0 && n > 0) return -8;
+  if (ldc < std::max(1, m)) return -9;
+  if (k < 1 || k > OZGEMM_S1_K_MAX) return -10;
+  if (variant != OZGEMM_S1_RN && variant != OZGEMM_S1_HYBRID) return -11;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > OZ_MAX_ROWS || n > OZ_MAX_ROWS || (q > 0 && s1_beta(q) < 1)) return OZGEMM_RANGE;
+  if (m == 0 || n == 0) return OZGEMM_OK;
+  const size_t cb = mat_bytes(m, n, ldc);
+  if (overlaps(C, cb, A, mat_bytes(m, q, lda)) || overlaps(C, cb, B, mat_bytes(q, n, ldb))) return -8;
+  if (q == 0) {
+    OZ_CHECK(launch_fill_zero(C, m, n, ldc, g.stream));
+    return OZGEMM_OK;
+  }
+  const S1Layout L = s1_layout(m, n, q, k, variant);
+  if (g.ws_bytes < s1_base() + L.total) return OZGEMM_WORKSPACE_TOO_SMALL;
+  char* base = g.ws + s1_base();
+  int4* gemm_plan = reinterpret_cast<int4*>(base + L.plans);
+  int4* acc_plan = gemm_plan + OZGEMM_S1_MAX_OUT;
+  int32_t* gA = reinterpret_cast<int32_t*>(base + L.gA);
+  int32_t* gB = reinterpret_cast<int32_t*>(base + L.gB);
+  uint64_t* pmax = reinterpret_cast<uint64_t*>(base + L.pmax);
+  int8_t* Asl = reinterpret_cast<int8_t*>(base + L.asl);
+  int8_t* Bsl = reinterpret_cast<int8_t*>(base + L.bsl);
+  int32_t* P = reinterpret_cast<int32_t*>(base + L.P);
+  // Scheme II keeps its constant table below this region; it stays valid.
+
+  std::array<hipEvent_t, 5> ev{};
+  const bool timed = g.timing && g.events.size() < TIMING_MAX_CALLS;
+  if (timed) {
+    for (auto& x : ev) OZ_CHECK(hipEventCreate(&x));
+    OZ_CHECK(hipEventRecord(ev[0], g.stream));
+    OZ_CHECK(hipEventRecord(ev[1], g.stream));
+  }
+  if ((st = s1_split(L, m, n, q, k, variant, A, lda, B, ldb, Asl, Bsl, gA, gB, pmax))) return st;
+  if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
+  OZ_CHECK(launch_s1_plan(variant, k, L.r, L.beta, gemm_plan, acc_plan, g.stream));
+  OZ_CHECK(launch_gemm_multi(Asl, Bsl, L.mp, L.np, L.qp, gemm_plan, L.nout, P, g.stream));
+  if (timed) OZ_CHECK(hipEventRecord(ev[3], g.stream));
+  OZ_CHECK(launch_s1_accum(P, m, n, L.mp, L.np, L.nout, acc_plan, gA, L.mp, gB, L.np, C, ldc, g.stream));
+  if (timed) {
+    OZ_CHECK(hipEventRecord(ev[4], g.stream));
+    g.events.push_back(ev);
+  }
+  return OZGEMM_OK;
+}
+
+int ozgemm_scheme1_stage_split(int m, int n, int q, int k, int variant, const double* A, int lda, const double* B,
+                               int ldb, int8_t* Aslices, int8_t* Bslices, int32_t* gA, int32_t* gB) {
+  int st = check_common(m, n, q, A, lda, B, ldb);
+  if (st) return st;
+  if (q < 1) return -3;
+  if (k < 1 || k > OZGEMM_S1_K_MAX) return -8;
+  if (variant != OZGEMM_S1_RN && variant != OZGEMM_S1_HYBRID) return -9;
+  if (Aslices == nullptr) return -10;
+  if (Bslices == nullptr) return -11;
+  if (gA == nullptr) return -12;
+  if (gB == nullptr) return -13;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > OZ_MAX_ROWS || n > OZ_MAX_ROWS || s1_beta(q) < 1) return OZGEMM_RANGE;
+  const S1Layout L = s1_layout(m, n, q, k, variant);
+  if (g.ws_bytes < s1_base() + L.pmax + (size_t)L.nch * std::max(L.mp, L.np) * 8) return OZGEMM_WORKSPACE_TOO_SMALL;
+  uint64_t* pmax = reinterpret_cast<uint64_t*>(g.ws + s1_base() + L.pmax);
+  return s1_split(L, m, n, q, k, variant, A, lda, B, ldb, Aslices, Bslices, gA, gB, pmax);
+}
+
+int ozgemm_scheme1_stage_products(int m, int n, int q, int k, int variant, const int8_t* Aslices,
+                                  const int8_t* Bslices, int32_t* P) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 1) return -3;
+  if (k < 1 || k > OZGEMM_S1_K_MAX) return -4;
+  if (variant != OZGEMM_S1_RN && variant != OZGEMM_S1_HYBRID) return -5;
+  if (Aslices == nullptr) return -6;
+  if (Bslices == nullptr) return -7;
+  if (P == nullptr) return -8;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > OZ_MAX_ROWS || n > OZ_MAX_ROWS || s1_beta(q) < 1) return OZGEMM_RANGE;
+  const S1Layout L = s1_layout(m, n, q, k, variant);
+  if (g.ws_bytes < s1_base() + L.plans + 2 * OZGEMM_S1_MAX_OUT * sizeof(int4)) return OZGEMM_WORKSPACE_TOO_SMALL;
+  int4* gemm_plan = reinterpret_cast<int4*>(g.ws + s1_base() + L.plans);
+  OZ_CHECK(launch_s1_plan(variant, k, L.r, L.beta, gemm_plan, gemm_plan + OZGEMM_S1_MAX_OUT, g.stream));
+  OZ_CHECK(launch_gemm_multi(Aslices, Bslices, L.mp, L.np, L.qp, gemm_plan, L.nout, P, g.stream));
+  return 0;
+}
+
+int ozgemm_scheme1_stage_accumulate(int m, int n, int q, int k, int variant, const int32_t* P, const int32_t* gA,
+                                    const int32_t* gB, double* C, int ldc) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 1) return -3;
+  if (k < 1 || k > OZGEMM_S1_K_MAX) return -4;
+  if (variant != OZGEMM_S1_RN && variant != OZGEMM_S1_HYBRID) return -5;
+  if (P == nullptr) return -6;
+  if (gA == nullptr) return -7;
+  if (gB == nullptr) return -8;
+  if (C == nullptr && m > 0 && n > 0) return -9;
+  if (ldc < std::max(1, m)) return -10;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > OZ_MAX_ROWS || n > OZ_MAX_ROWS || s1_beta(q) < 1) return OZGEMM_RANGE;
+  if (m == 0 || n == 0) return 0;
+  const S1Layout L = s1_layout(m, n, q, k, variant);
+  if (g.ws_bytes < s1_base() + L.plans + 2 * OZGEMM_S1_MAX_OUT * sizeof(int4)) return OZGEMM_WORKSPACE_TOO_SMALL;
+  int4* gemm_plan = reinterpret_cast<int4*>(g.ws + s1_base() + L.plans);
+  int4* acc_plan = gemm_plan + OZGEMM_S1_MAX_OUT;
+  OZ_CHECK(launch_s1_plan(variant, k, L.r, L.beta, gemm_plan, acc_plan, g.stream));
+  OZ_CHECK(launch_s1_accum(P, m, n, L.mp, L.np, L.nout, acc_plan, gA, L.mp, gB, L.np, C, ldc, g.stream));
   return 0;
 }
 

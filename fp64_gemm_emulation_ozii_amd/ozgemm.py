@@ -24,12 +24,18 @@ OZGEMM_HIP_ERROR = 4
 OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
+OZGEMM_S1_RN = 0
+OZGEMM_S1_HYBRID = 1
+OZGEMM_S1_K_MAX = 16
+OZGEMM_S1_MAX_OUT = 136
 
 #: every symbol the header declares
 EXPORTS = (
     "ozgemm_workspace_bytes", "ozgemm_config", "ozgemm_set_stream", "ozgemm_free", "ozgemm_strerror",
     "ozgemm_dgemm", "ozgemm_moduli", "ozgemm_kbits", "ozgemm_plane_dims", "ozgemm_stage_scale",
     "ozgemm_stage_residue", "ozgemm_stage_gemm", "ozgemm_stage_crt", "ozgemm_timing", "ozgemm_phase_ms",
+    "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
+    "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
 )
 
 _lib = None
@@ -68,6 +74,14 @@ def lib():
         "ozgemm_stage_crt": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_int]),
         "ozgemm_timing": (c_int, [c_int]),
         "ozgemm_phase_ms": (c_int, [ctypes.POINTER(ctypes.c_double), ip]),
+        "ozgemm_scheme1_beta": (c_int, [c_int]),
+        "ozgemm_scheme1_outputs": (c_int, [c_int, c_int, c_int]),
+        "ozgemm_scheme1_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
+        "ozgemm_scheme1_dgemm": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, c_int, c_int, c_int]),
+        "ozgemm_scheme1_stage_split": (c_int, [c_int, c_int, c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp, vp,
+                                               vp]),
+        "ozgemm_scheme1_stage_products": (c_int, [c_int, c_int, c_int, c_int, c_int, vp, vp, vp]),
+        "ozgemm_scheme1_stage_accumulate": (c_int, [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -135,12 +149,16 @@ def ozgemm_plane_dims(m: int, n: int, q: int):
 # --------------------------------------------------------------------------
 
 def ozgemm_config(s_max: int, max_m: int, max_n: int, max_q: int, stream=None, workspace=None,
-                  workspace_bytes: int | None = None) -> int:
+                  workspace_bytes: int | None = None, scheme1_k: int = 0, scheme1_variant: int = OZGEMM_S1_RN) -> int:
     """Configure the library.  With ``workspace=None`` a torch uint8 device
     tensor of ``ozgemm_workspace_bytes(...)`` bytes is allocated and kept
-    alive here."""
+    alive here -- or of ``ozgemm_scheme1_workspace_bytes(max_m, max_n, max_q,
+    scheme1_k, scheme1_variant)`` bytes when ``scheme1_k`` > 0 and that is
+    larger."""
     global _workspace
     need = ozgemm_workspace_bytes(max_m, max_n, max_q, s_max)
+    if scheme1_k > 0:
+        need = max(need, ozgemm_scheme1_workspace_bytes(max_m, max_n, max_q, scheme1_k, scheme1_variant))
     if workspace is None:
         import torch
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
@@ -193,6 +211,40 @@ def ozgemm_stage_gemm(m, n, q, s, Ares, Bres, Ct=None, rt=None, check: bool = Tr
 def ozgemm_stage_crt(m, n, q, s, rt, e, f, C, ldc, check: bool = True) -> int:
     st = lib().ozgemm_stage_crt(m, n, q, s, _ptr(rt), _ptr(e), _ptr(f), _ptr(C), ldc)
     return _check(st, "ozgemm_stage_crt") if check else st
+
+
+def ozgemm_scheme1_beta(q: int) -> int:
+    return lib().ozgemm_scheme1_beta(q)
+
+
+def ozgemm_scheme1_outputs(k: int, variant: int, q: int) -> int:
+    return lib().ozgemm_scheme1_outputs(k, variant, q)
+
+
+def ozgemm_scheme1_workspace_bytes(m: int, n: int, q: int, k: int, variant: int) -> int:
+    return lib().ozgemm_scheme1_workspace_bytes(m, n, q, k, variant)
+
+
+def ozgemm_scheme1_dgemm(m, n, q, A, lda, B, ldb, C, ldc, k, variant=OZGEMM_S1_RN, check: bool = True) -> int:
+    st = lib().ozgemm_scheme1_dgemm(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, k, variant)
+    return _check(st, "ozgemm_scheme1_dgemm") if check else st
+
+
+def ozgemm_scheme1_stage_split(m, n, q, k, variant, A, lda, B, ldb, Aslices, Bslices, gA, gB,
+                               check: bool = True) -> int:
+    st = lib().ozgemm_scheme1_stage_split(m, n, q, k, variant, _ptr(A), lda, _ptr(B), ldb, _ptr(Aslices),
+                                          _ptr(Bslices), _ptr(gA), _ptr(gB))
+    return _check(st, "ozgemm_scheme1_stage_split") if check else st
+
+
+def ozgemm_scheme1_stage_products(m, n, q, k, variant, Aslices, Bslices, P, check: bool = True) -> int:
+    st = lib().ozgemm_scheme1_stage_products(m, n, q, k, variant, _ptr(Aslices), _ptr(Bslices), _ptr(P))
+    return _check(st, "ozgemm_scheme1_stage_products") if check else st
+
+
+def ozgemm_scheme1_stage_accumulate(m, n, q, k, variant, P, gA, gB, C, ldc, check: bool = True) -> int:
+    st = lib().ozgemm_scheme1_stage_accumulate(m, n, q, k, variant, _ptr(P), _ptr(gA), _ptr(gB), _ptr(C), ldc)
+    return _check(st, "ozgemm_scheme1_stage_accumulate") if check else st
 
 
 def ozgemm_timing(enable: bool) -> int:

@@ -60,6 +60,12 @@ extern "C" {
 #define OZGEMM_Q_LIMIT (1 << 17)      /* q must be below this (Ozaki II notes §6) */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
 
+/* Scheme I variants (Ozaki I notes, optimized algorithm) */
+#define OZGEMM_S1_RN      0  /* RN split, per-product FP64 accumulation (direction 1) */
+#define OZGEMM_S1_HYBRID  1  /* Hybrid split, group-wise INT32 accumulation (directions 2, 3) */
+#define OZGEMM_S1_K_MAX   16 /* largest number of slices */
+#define OZGEMM_S1_MAX_OUT 136 /* k (k + 1) / 2 at k = OZGEMM_S1_K_MAX */
+
 /* ---------------------------------------------------------------------- */
 /* Configuration                                                          */
 /* ---------------------------------------------------------------------- */
@@ -157,6 +163,78 @@ int ozgemm_stage_gemm(int m, int n, int q, int s,
 int ozgemm_stage_crt(int m, int n, int q, int s,
                      const uint8_t *rt, const int32_t *e, const int32_t *f,
                      double *C, int ldc);
+
+/* ---------------------------------------------------------------------- */
+/* Scheme I: FP64 GEMM from int8 slices (secondary path)                   */
+/*                                                                        */
+/* Method: the course page "Ozaki Scheme" (zsc0tt.pages.dev/courses/      */
+/* hpc-summer/ozaki-scheme), cited as "Ozaki I notes": its optimized      */
+/* algorithm after Uchino, Ozaki and Imamura.  Each row of A and column  */
+/* of B is split into k signed slices of beta bits,                       */
+/* beta = min(7, floor((31 - log2 q) / 2)); slice p of a row is the       */
+/* row's remaining residual rounded to nearest-even on a power-of-two     */
+/* grid 2^g (|slice / 2^g| <= 2^(beta-1)).  The products A_i B_j with     */
+/* i + j <= k + 1 (k (k + 1) / 2 of them) are exact int8 GEMMs and are    */
+/* added up in FP64 in a fixed order, so results are reproducible.        */
+/*   OZGEMM_S1_RN:     grid of slice p from the max of the row's residual */
+/*                     (RN split); each product converted and added,      */
+/*                     i-major, j-minor.                                  */
+/*   OZGEMM_S1_HYBRID: grid of slice p = g0 - beta (p - 1), g0 from the   */
+/*                     original row max (Hybrid split); products with the */
+/*                     same i + j summed in int32, at most                */
+/*                     r = max(1, 2^(31 - 2 beta - ceil(log2 q))) at a    */
+/*                     time, then added in increasing i + j.              */
+/* Grid exponents: g = ceil(log2 max|row|) + 1 - beta; 0 for an all-zero  */
+/* row; OZGEMM_EXP_NONFINITE (first grid row only) for a row holding      */
+/* Inf/NaN, whose slices are zero and whose outputs are NaN.              */
+/* These calls use the configured stream and workspace; the workspace     */
+/* must hold ozgemm_scheme1_workspace_bytes(m, n, q, k, variant) bytes    */
+/* (else OZGEMM_WORKSPACE_TOO_SMALL).  q may exceed 2^17 (beta shrinks);  */
+/* beta < 1 (q > 2^29) gives OZGEMM_RANGE.                                */
+/* ---------------------------------------------------------------------- */
+
+/* Slice width beta for inner dimension q, or -1 when none fits. */
+int ozgemm_scheme1_beta(int q);
+
+/* Number of int32 product planes (outputs of the products stage):
+ * k (k + 1) / 2 for RN; the number of runs for Hybrid.  <0 on bad input. */
+int ozgemm_scheme1_outputs(int k, int variant, int q);
+
+/* Workspace bytes needed by a Scheme I call of this shape (0 on bad input). */
+size_t ozgemm_scheme1_workspace_bytes(int m, int n, int q, int k, int variant);
+
+/* C <- A B by Scheme I with k slices (1 <= k <= OZGEMM_S1_K_MAX).
+ * Arguments and conventions as ozgemm_dgemm, with k and variant in place
+ * of s.  Phase timing slots: [scale: 0, split, products, accumulation]. */
+int ozgemm_scheme1_dgemm(int m, int n, int q,
+                         const double *A, int lda, const double *B, int ldb,
+                         double *C, int ldc, int k, int variant);
+
+/* Split stage (Ozaki I notes, RN split / Hybrid split algorithms).
+ * Aslices[p][i][l] (p < k) at p*m_pad*q_pad + i*q_pad + l: slice integers of
+ * row i of A; Bslices[p][j][l] at p*n_pad*q_pad + j*q_pad + l for column j of
+ * B (int8, zero in the padding; m_pad, n_pad, q_pad from ozgemm_plane_dims).
+ * gA[p][i] at p*m_pad + i and gB[p][j] at p*n_pad + j: grid exponents, k
+ * rows for RN, one row (g0) for Hybrid. */
+int ozgemm_scheme1_stage_split(int m, int n, int q, int k, int variant,
+                               const double *A, int lda, const double *B, int ldb,
+                               int8_t *Aslices, int8_t *Bslices,
+                               int32_t *gA, int32_t *gB);
+
+/* Products stage: P[o][j][i] at o*m_pad*n_pad + j*m_pad + i (int32) for
+ * o < ozgemm_scheme1_outputs(k, variant, q), in accumulation order:
+ * RN: o-th pair (i, j) of the triangle, P = A_i B_j^T;
+ * Hybrid: o-th run of pairs (s, g - s), P = sum of their products. */
+int ozgemm_scheme1_stage_products(int m, int n, int q, int k, int variant,
+                                  const int8_t *Aslices, const int8_t *Bslices,
+                                  int32_t *P);
+
+/* Accumulation stage: C (m x n, ld ldc) = sum over o, in order, of
+ * P[o] scaled by 2^(gA + gB) of its slices (Hybrid: 2^(g0A + g0B - beta (g - 2))),
+ * each addition rounded in FP64. */
+int ozgemm_scheme1_stage_accumulate(int m, int n, int q, int k, int variant,
+                                    const int32_t *P, const int32_t *gA,
+                                    const int32_t *gB, double *C, int ldc);
 
 /* ---------------------------------------------------------------------- */
 /* Phase timing                                                           */

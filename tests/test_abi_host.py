@@ -23,7 +23,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libozgem
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ozgemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ozgemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_what_binding_lists():
@@ -145,4 +145,70 @@ def test_config_rejects_q_limit_and_stage_checks():
     assert lib.ozgemm_stage_gemm(8, 8, 8, 15, FAKE, FAKE, None, None) == L.OZGEMM_RANGE
     assert lib.ozgemm_stage_crt(8, 8, 8, 14, None, FAKE, FAKE, FAKE, 8) == -5
     assert lib.ozgemm_stage_residue(8, 8, 8, 14, FAKE, 8, FAKE, 8, FAKE, FAKE, None, FAKE, None, None) == -11
+    lib.ozgemm_free()
+
+
+# ------------------------------------------------------------ Scheme I host side
+
+from oracle import ozaki1 as o1  # noqa: E402
+
+
+@pytest.mark.parametrize("q", [1, 2, 3, 64, 1000, 4096, 4097, 65536, 2**17 + 3, 2**20, 2**23, 2**29, 2**29 + 1])
+def test_scheme1_beta_matches_oracle(q):
+    try:
+        ref = o1.slice_width(q)
+    except ValueError:
+        ref = -1
+    assert L.ozgemm_scheme1_beta(q) == ref
+
+
+@pytest.mark.parametrize("q", [64, 4096, 65536, 2**20])
+@pytest.mark.parametrize("k", [1, 2, 4, 8, 16])
+def test_scheme1_outputs_match_oracle(q, k):
+    beta = o1.slice_width(q)
+    r = o1.group_size(q, beta)
+    assert L.ozgemm_scheme1_outputs(k, L.OZGEMM_S1_RN, q) == len(o1.triangle(k))
+    assert L.ozgemm_scheme1_outputs(k, L.OZGEMM_S1_HYBRID, q) == len(o1.groups(k, r))
+
+
+def test_scheme1_host_validation():
+    assert L.ozgemm_scheme1_outputs(0, 0, 64) < 0
+    assert L.ozgemm_scheme1_outputs(17, 0, 64) < 0
+    assert L.ozgemm_scheme1_outputs(4, 2, 64) < 0
+    assert L.ozgemm_scheme1_workspace_bytes(64, 64, 64, 0, 0) == 0
+    assert L.ozgemm_scheme1_workspace_bytes(64, 64, 64, 4, 5) == 0
+    w = L.ozgemm_scheme1_workspace_bytes(1000, 700, 300, 8, L.OZGEMM_S1_RN)
+    mp, np_, qp = L.ozgemm_plane_dims(1000, 700, 300)
+    # at least the slices and the 36 int32 product planes
+    assert w >= 8 * (mp + np_) * qp + 36 * mp * np_ * 4
+    assert L.ozgemm_scheme1_workspace_bytes(1000, 700, 300, 8, L.OZGEMM_S1_HYBRID) < w
+
+
+@no_gpu_only
+def test_scheme1_validation_before_any_launch():
+    lib = L.lib()
+    lib.ozgemm_free()
+    Cp = FAKE + (1 << 30)
+    d = lib.ozgemm_scheme1_dgemm
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 4, 0) == L.OZGEMM_NOT_CONFIGURED
+    ws = L.ozgemm_workspace_bytes(256, 256, 256, 14)
+    assert lib.ozgemm_config(14, 256, 256, 256, None, FAKE, ws) == 0
+    assert d(-1, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 4, 0) == -1
+    assert d(8, 8, 8, FAKE, 7, FAKE, 8, Cp, 8, 4, 0) == -5
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, None, 8, 4, 0) == -8
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 7, 4, 0) == -9
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 0, 0) == -10
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 17, 0) == -10
+    assert d(8, 8, 8, FAKE, 8, FAKE, 8, Cp, 8, 4, 2) == -11
+    assert d(8, 8, 2**29 + 1, FAKE, 8, FAKE, 2**29 + 1, Cp, 8, 4, 0) == L.OZGEMM_RANGE
+    # a Scheme II sized workspace is too small for a larger Scheme I problem
+    assert d(2048, 2048, 2048, FAKE, 2048, FAKE, 2048, FAKE + (1 << 36), 2048, 8, 0) == L.OZGEMM_WORKSPACE_TOO_SMALL
+    assert d(0, 8, 8, FAKE, 1, FAKE, 8, Cp, 1, 4, 0) == 0
+    s = lib.ozgemm_scheme1_stage_split
+    assert s(8, 8, 8, 4, 0, FAKE, 8, FAKE, 8, None, FAKE, FAKE, FAKE) == -10
+    assert s(8, 8, 8, 4, 3, FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, FAKE) == -9
+    p = lib.ozgemm_scheme1_stage_products
+    assert p(8, 8, 8, 4, 0, FAKE, FAKE, None) == -8
+    a = lib.ozgemm_scheme1_stage_accumulate
+    assert a(8, 8, 8, 4, 0, FAKE, FAKE, FAKE, FAKE, 7) == -10
     lib.ozgemm_free()
