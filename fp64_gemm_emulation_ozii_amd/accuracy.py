@@ -12,9 +12,11 @@ Command line (runs on the GPU)::
     python -m fp64_gemm_emulation_ozii_amd.accuracy --m 1024 --n 1024 --q 1024 \
         --s 8,10,12,14,16,18 --phi 0.5 [--entries 64] [--out table.json]
 
-prints one JSON object per (s, phi) with the correct bits of the emulation
-and of the native FP64 dot products on the same entries, and the time of
-each phase (scale, residue, GEMM, CRT) in milliseconds.
+prints one JSON object per (method, s or k, phi) with the correct bits of the
+emulation and of the native FP64 dot products on the same entries, and the
+time of each phase in milliseconds (Scheme II: scale, residue, GEMM, CRT;
+Scheme I: split, products, accumulation).  ``--methods ozaki2,scheme1-rn,
+scheme1-hybrid --k 4,5,6,7,8`` compares the two schemes on the same inputs.
 """
 from __future__ import annotations
 
@@ -76,7 +78,20 @@ def _parse_list(text: str, conv):
     return [conv(x) for x in text.split(",") if x.strip()]
 
 
-def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats):
+def _runs(s_list, k_list, methods):
+    """(method, parameter) pairs: Scheme II over s, Scheme I variants over k."""
+    out = []
+    for meth in methods:
+        if meth == "ozaki2":
+            out += [("ozaki2", s) for s in s_list]
+        elif meth in ("scheme1-rn", "scheme1-hybrid"):
+            out += [(meth, k) for k in k_list]
+        else:
+            raise SystemExit(f"unknown method {meth}")
+    return out
+
+
+def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats, k_list=(), methods=("ozaki2",)):
     import torch
 
     from . import ozgemm as L
@@ -86,6 +101,7 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats):
     rng = np.random.default_rng(12345)
     rows = rng.integers(0, m, size=entries)
     cols = rng.integers(0, n, size=entries)
+    runs = _runs(s_list, k_list, methods)
     results = []
     for phi in phi_list:
         A, B = hpl_like(m, q, n, phi, seed=seed)
@@ -94,32 +110,52 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats):
         Cd = torch.empty((n, m), dtype=torch.float64, device=dev)
         native = (torch.from_numpy(A[rows, :]).to(dev) * torch.from_numpy(B[:, cols].T.copy()).to(dev)).sum(1)
         native_bits = correct_bits(native.cpu().numpy(), A, B, rows, cols)
-        L.ozgemm_config(max(s_list), m, n, q, stream=torch.cuda.current_stream())
-        for s in s_list:
-            L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)  # warm-up
+        s_max = max([p for meth, p in runs if meth == "ozaki2"] or [1])
+        need1 = max([L.ozgemm_scheme1_workspace_bytes(m, n, q, p, L.OZGEMM_S1_RN if meth == "scheme1-rn"
+                                                       else L.OZGEMM_S1_HYBRID)
+                     for meth, p in runs if meth != "ozaki2"] or [0])
+        ws = torch.empty(max(L.ozgemm_workspace_bytes(m, n, q, s_max), need1), dtype=torch.uint8, device=dev)
+        L.ozgemm_config(s_max, m, n, q, stream=torch.cuda.current_stream(), workspace=ws)
+
+        def call(meth, p):
+            if meth == "ozaki2":
+                L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, p)
+            else:
+                v = L.OZGEMM_S1_RN if meth == "scheme1-rn" else L.OZGEMM_S1_HYBRID
+                L.ozgemm_scheme1_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, p, v)
+
+        for meth, p in runs:
+            call(meth, p)  # warm-up
             torch.cuda.synchronize()
             L.ozgemm_timing(True)
             for _ in range(repeats):
-                L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+                call(meth, p)
             torch.cuda.synchronize()
             phase_ms, calls = L.ozgemm_phase_ms()
             L.ozgemm_timing(False)
             per = [x / max(calls, 1) for x in phase_ms]
             Cs = Cd.T[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)].cpu().numpy()
-            rec = {
-                "m": m, "n": n, "q": q, "s": s, "phi": phi, "k": L.ozgemm_kbits(s, q),
+            rec = {"method": meth, "m": m, "n": n, "q": q, "phi": phi}
+            if meth == "ozaki2":
+                rec.update({"s": p, "k": L.ozgemm_kbits(p, q), "int8_gemms": p})
+                names = ("scale", "residue", "gemm", "crt")
+            else:
+                v = L.OZGEMM_S1_RN if meth == "scheme1-rn" else L.OZGEMM_S1_HYBRID
+                rec.update({"slices": p, "beta": L.ozgemm_scheme1_beta(q), "int8_gemms": p * (p + 1) // 2,
+                            "int32_outputs": L.ozgemm_scheme1_outputs(p, v, q)})
+                names = ("scale", "split", "products", "accumulate")
+            rec.update({
                 "correct_bits": round(correct_bits(Cs, A, B, rows, cols), 2),
                 "correct_bits_native_fp64": round(native_bits, 2),
                 "entries": int(entries),
-                "phases_ms": {"scale": round(per[0], 4), "residue": round(per[1], 4),
-                              "gemm": round(per[2], 4), "crt": round(per[3], 4)},
+                "phases_ms": {nm: round(x, 4) for nm, x in zip(names, per)},
                 "total_ms": round(sum(per), 4),
                 "fp64_tflops": round(2.0 * m * n * q / (sum(per) * 1e-3) / 1e12, 2),
-            }
+            })
             print(json.dumps(rec), flush=True)
             results.append(rec)
         L.ozgemm_free()
-        del Ad, Bd, Cd
+        del Ad, Bd, Cd, ws
         torch.cuda.empty_cache()
     return results
 
@@ -134,9 +170,13 @@ def main(argv=None):
     p.add_argument("--entries", type=int, default=64)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--repeats", type=int, default=5)
+    p.add_argument("--k", type=str, default="4,5,6,7,8", help="Scheme I slice counts")
+    p.add_argument("--methods", type=str, default="ozaki2",
+                   help="comma list of ozaki2, scheme1-rn, scheme1-hybrid")
     p.add_argument("--out", type=str, default="")
     a = p.parse_args(argv)
-    res = run_sweep(a.m, a.n, a.q, _parse_list(a.s, int), _parse_list(a.phi, float), a.entries, a.seed, a.repeats)
+    res = run_sweep(a.m, a.n, a.q, _parse_list(a.s, int), _parse_list(a.phi, float), a.entries, a.seed, a.repeats,
+                    _parse_list(a.k, int), _parse_list(a.methods, str))
     if a.out:
         with open(a.out, "w") as fh:
             json.dump(res, fh, indent=1)
