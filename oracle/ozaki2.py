@@ -262,12 +262,76 @@ def unscale(X: np.ndarray, e: np.ndarray, f: np.ndarray, k: int) -> np.ndarray:
 # The whole scheme
 # ----------------------------------------------------------------------------
 
-def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False):
+# ----------------------------------------------------------------------------
+# OS II-fast bit budget (Ozaki II notes §9)
+# ----------------------------------------------------------------------------
+
+#: Entries are rounded up on a grid of 2^-NORM_GRID (relative to 2^e) when
+#: bounding row norms, so squared norms are integers in units of 2^-2*NORM_GRID.
+NORM_GRID = 20
+
+
+def cs_budget(M: int) -> tuple[int, int]:
+    """(kappa_A, kappa_B) with kappa_A + kappa_B = floor(log2(M/2 - 1)).
+
+    §9 (OS II-fast) bounds c_max with Cauchy-Schwarz instead of §5's
+    q 2^(k_A + k_B): |(A'B')_ij| <= ||A'_i|| ||B'_j||.  Scaling every row of A'
+    to norm <= 2^kappa_A and every column of B' to norm <= 2^kappa_B keeps
+    2 c_max < M, the §5 uniqueness condition.  The budget is split evenly.
+    """
+    K2 = (M // 2 - 1).bit_length() - 1
+    return K2 // 2, K2 - K2 // 2
+
+
+def row_norm_units(A: np.ndarray, e: np.ndarray) -> list[int]:
+    """S_i = sum_l ceil(|a_il| 2^(NORM_GRID - e_i))^2, an integer upper bound of
+    ||a_i 2^-e_i||^2 in units of 2^(-2 NORM_GRID).  0 for rows that are zero
+    or hold Inf/NaN.  Each term is at most 2^(2 NORM_GRID) and q < 2^17, so the
+    int64 sums are exact."""
+    A = np.asarray(A, dtype=np.float64)
+    assert A.shape[1] < 2**17
+    out = []
+    for i in range(A.shape[0]):
+        if e[i] == NONFINITE:
+            out.append(0)
+            continue
+        t = np.ceil(np.ldexp(np.abs(A[i, :]), NORM_GRID - int(e[i]))).astype(np.int64)  # exact, <= 2^NORM_GRID
+        out.append(int(np.sum(t * t)))
+    return out
+
+
+def fast_exponents(A: np.ndarray, e: np.ndarray, kappa: int, kb: int) -> np.ndarray:
+    """Exponents e'_i = kb - d_i for the OS II-fast scaling d_i = kappa - c_i - e_i,
+    with 4^c_i the smallest power of four >= S_i 2^(-2 NORM_GRID).  Then
+    ||trunc(a_i 2^d_i)|| <= 2^d_i ||a_i|| <= 2^kappa, and the kernels' shift
+    kb - e'_i equals d_i.  Zero rows keep 0, non-finite rows NONFINITE."""
+    S = row_norm_units(A, e)
+    out = np.zeros(len(S), dtype=np.int64)
+    for i, Si in enumerate(S):
+        if e[i] == NONFINITE:
+            out[i] = NONFINITE
+        elif Si == 0:
+            out[i] = 0
+        else:
+            b = (Si - 1).bit_length()          # ceil(log2 S_i)
+            c = (b + 1) // 2 - NORM_GRID       # ceil(log2(S_i)/2) - NORM_GRID
+            d = kappa - c - int(e[i])
+            out[i] = kb - d
+    return out
+
+
+def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False, bound: str = "conservative"):
     """C ~= A B by Ozaki Scheme II with s moduli (Ozaki II notes §7).
+
+    ``bound`` selects the bit budget: "conservative" is §5's
+    c_max <= q 2^(k_A + k_B) with k_A = k_B = k; "fast" is the §9 OS II-fast
+    Cauchy-Schwarz budget of :func:`cs_budget` and :func:`fast_exponents`.
 
     With ``stages=True`` also returns a dict of every intermediate:
     ``moduli, M, k, e, f, Ap, Bp, Ares (s x m x q int8), Bres (s x q x n int8),
-    Ct (s x m x n int32), rt (s x m x n uint8), X (object), C``.
+    Ct (s x m x n int32), rt (s x m x n uint8), X (object), C``.  In fast mode
+    ``k`` is the shift base kb and e, f are the exponents e' of
+    :func:`fast_exponents` (row shift kb - e'_i).
     """
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
@@ -282,11 +346,19 @@ def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False):
         return (C, {"moduli": mods, "M": M, "k": None, "C": C}) if stages else C
     if q >= 2**17:
         raise ValueError("q >= 2^17 is outside the exact int32 range")
-    k = kbits(M, q)
-    if k < 1:
-        raise ValueError(f"s={s} leaves no bits for q={q}")
     e = row_exponents(A)
     f = col_exponents(B)
+    if bound == "conservative":
+        k = kbits(M, q)
+        if k < 1:
+            raise ValueError(f"s={s} leaves no bits for q={q}")
+    elif bound == "fast":
+        kA, kB = cs_budget(M)
+        k = max(kA, kB)
+        e = fast_exponents(A, e, kA, k)
+        f = fast_exponents(B.T, f, kB, k)
+    else:
+        raise ValueError(f"unknown bound {bound!r}")
     Ap = truncate_rows(A, e, k)
     Bp = truncate_cols(B, f, k)
     Ares, Bres, Ct, rt = [], [], [], []
@@ -309,16 +381,17 @@ def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False):
     }
 
 
-def dgemm_block(A: np.ndarray, B: np.ndarray, s: int, rows, cols, stages: bool = False):
+def dgemm_block(A: np.ndarray, B: np.ndarray, s: int, rows, cols, stages: bool = False, bound: str = "conservative"):
     """The oracle on the sub-problem A[rows, :] x B[:, cols].
 
     Exponents depend only on their own row of A or column of B and k only on
-    q, so these are exactly the entries (rows x cols) of ``dgemm(A, B, s)``.
-    Used to check sampled outputs of problems too large for the full oracle.
+    q (in fast mode the budget only on M), so these are exactly the entries
+    (rows x cols) of ``dgemm(A, B, s)``.  Used to check sampled outputs of
+    problems too large for the full oracle.
     """
     A = np.asarray(A)
     B = np.asarray(B)
-    return dgemm(A[np.asarray(rows), :], B[:, np.asarray(cols)], s, stages=stages)
+    return dgemm(A[np.asarray(rows), :], B[:, np.asarray(cols)], s, stages=stages, bound=bound)
 
 
 # ----------------------------------------------------------------------------

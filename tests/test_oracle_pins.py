@@ -470,3 +470,103 @@ def test_scheme1_count_table_from_page():
     for k, count in table.items():
         k = int(k)
         assert sum(1 for i in range(1, k + 1) for j in range(1, k + 1) if i + j <= k + 1) == count
+
+
+# ------------------------------------------------------------------ OS II-fast
+
+def _frac_sq_norm(v):
+    return sum(Fraction(float(x)) ** 2 for x in v)
+
+
+@pytest.mark.parametrize("s", [1, 2, 5, 8, 14, 16, 20])
+def test_fast_budget_splits_floor_log2_half_m(s):
+    M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+    kA, kB = oz.cs_budget(M)
+    assert kB - kA in (0, 1)
+    assert 2 ** (kA + kB) <= M // 2 - 1 < 2 ** (kA + kB + 1)
+
+
+def test_norm_units_bound_the_squared_norm_tightly():
+    rng = np.random.default_rng(31)
+    A = (rng.random((7, 300)) - 0.5) * np.exp(2 * rng.standard_normal((7, 300)))
+    A[2, :] = 0.0
+    A[3, 4] = 2.0**-1070
+    e = oz.row_exponents(A)
+    S = oz.row_norm_units(A, e)
+    for i in range(A.shape[0]):
+        exact = _frac_sq_norm(A[i] * 2.0 ** -int(e[i])) if A[i].any() else Fraction(0)
+        bound = Fraction(S[i], 2 ** (2 * oz.NORM_GRID))
+        assert bound >= exact
+        # each entry is rounded up by less than 2^-20 (relative to 2^e)
+        slack = sum(2 * abs(Fraction(float(x)) * Fraction(2) ** -int(e[i])) * Fraction(1, 2**20) + Fraction(1, 2**40)
+                    for x in A[i])
+        assert bound - exact <= slack
+
+
+@pytest.mark.parametrize("s,q", [(6, 40), (10, 64), (14, 100), (18, 33)])
+def test_fast_bound_keeps_crt_exact(s, q):
+    """OS II-fast: ||A'_i|| <= 2^kappa_A, ||B'_j|| <= 2^kappa_B, hence by
+    Cauchy-Schwarz |(A'B')_ij| < M/2 and the CRT returns A'B' exactly."""
+    rng = np.random.default_rng(s * 100 + q)
+    A = (rng.random((9, q)) - 0.5) * np.exp(rng.standard_normal((9, q)))
+    B = (rng.random((q, 8)) - 0.5) * np.exp(rng.standard_normal((q, 8)))
+    A[0, :] = 1.0  # flat row: the bound is nearly tight
+    C, st = oz.dgemm(A, B, s, stages=True, bound="fast")
+    M = st["M"]
+    kA, kB = oz.cs_budget(M)
+    to_int = np.vectorize(int, otypes=[object])
+    Ap = to_int(st["Ap"])
+    Bp = to_int(st["Bp"])
+    for i in range(A.shape[0]):
+        assert sum(int(x) ** 2 for x in Ap[i]) <= 4 ** kA
+    for j in range(B.shape[1]):
+        assert sum(int(x) ** 2 for x in Bp[:, j]) <= 4 ** kB
+    exact = Ap.dot(Bp)
+    assert np.array_equal(st["X"], exact)
+    assert all(2 * abs(int(v)) < M for v in exact.flat)
+
+
+def test_fast_bound_tight_case_and_planted_overshoot(monkeypatch):
+    """All-ones rows with q = 4^j meet the bound with equality; a budget one
+    bit larger on each side breaks the CRT uniqueness."""
+    s, q = 9, 64
+    A = np.ones((3, q))
+    B = np.ones((q, 2))
+    C, st = oz.dgemm(A, B, s, stages=True, bound="fast")
+    kA, kB = oz.cs_budget(st["M"])
+    assert int(st["X"][0, 0]) == 2 ** (kA + kB)
+    assert np.all(C == q)
+    real = oz.cs_budget
+    monkeypatch.setattr(oz, "cs_budget", lambda M: tuple(v + 1 for v in real(M)))
+    C2, st2 = oz.dgemm(A, B, s, stages=True, bound="fast")
+    to_int = np.vectorize(int, otypes=[object])
+    exact = to_int(st2["Ap"]).dot(to_int(st2["Bp"]))
+    assert not np.array_equal(st2["X"], exact)
+
+
+def test_fast_bound_gains_bits_on_wide_rows():
+    rng = np.random.default_rng(8)
+    q = 256
+    A = (rng.random((6, q)) - 0.5) * np.exp(rng.standard_normal((6, q)))
+    B = (rng.random((q, 6)) - 0.5) * np.exp(rng.standard_normal((q, 6)))
+    rows, cols = np.arange(6).repeat(6), np.tile(np.arange(6), 6)
+    for s in (8, 10, 12):
+        cons = oz.correct_bits(oz.dgemm(A, B, s), A, B, rows, cols)
+        fast = oz.correct_bits(oz.dgemm(A, B, s, bound="fast"), A, B, rows, cols)
+        assert fast >= cons + 2.0, (s, cons, fast)
+
+
+def test_fast_bound_special_rows():
+    rng = np.random.default_rng(6)
+    A = rng.standard_normal((5, 20))
+    B = rng.standard_normal((20, 4))
+    A[1, :] = 0.0
+    A[2, 3] = np.nan
+    B[:, 1] = 0.0
+    C = oz.dgemm(A, B, 12, bound="fast")
+    assert np.all(C[1, :] == 0.0) and np.all(np.isnan(C[2, :]))
+    assert np.all(C[[0, 3, 4]][:, 1] == 0.0)
+    Ci = oz.dgemm(np.round(A * 8), np.round(B * 8), 12, bound="fast")
+    ref = np.round(A * 8) @ np.round(B * 8)
+    ok = ~np.isnan(Ci)
+    assert np.array_equal(Ci[ok], ref[ok])
