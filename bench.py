@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--q", type=int, default=8192)
     p.add_argument("--s", type=int, default=14)
     p.add_argument("--phi", type=float, default=1.0)
+    p.add_argument("--bound", choices=["conservative", "fast"], default="conservative",
+                   help="bit budget: the k of the Ozaki II notes section 5, or OS II-fast (section 9)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,7 +71,7 @@ def traffic_record(workload: str):
         return None
 
 
-def cpu_baseline(A, B, s, q, target_s, Cg_full_getter):
+def cpu_baseline(A, B, s, q, target_s, Cg_full_getter, bound="conservative"):
     """Time the oracle on a block of output entries of the same workload."""
     import numpy as np
     from oracle import ozaki2 as oz
@@ -83,13 +85,13 @@ def cpu_baseline(A, B, s, q, target_s, Cg_full_getter):
     # calibrate on a 32x32 block, then size the block for about target_s
     # seconds (cost grows between linearly and quadratically with the side)
     t0 = time.perf_counter()
-    oz.dgemm_block(A, B, s, np.arange(min(32, m)), np.arange(min(32, n)))
+    oz.dgemm_block(A, B, s, np.arange(min(32, m)), np.arange(min(32, n)), bound=bound)
     t_small = time.perf_counter() - t0
     side = int(max(32, min(1024, 32 * (target_s / max(t_small, 1e-6)) ** (1 / 1.6))))
     rows = np.sort(rng.choice(m, size=min(side, m), replace=False))
     cols = np.sort(rng.choice(n, size=min(side, n), replace=False))
     t0 = time.perf_counter()
-    ref = oz.dgemm_block(A, B, s, rows, cols)
+    ref = oz.dgemm_block(A, B, s, rows, cols, bound=bound)
     dt = time.perf_counter() - t0
     entries = len(rows) * len(cols)
     Cg = Cg_full_getter(rows, cols)
@@ -122,7 +124,7 @@ def main():
     from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
 
     m, n, q, s, phi = args.m, args.n, args.q, args.s, args.phi
-    workload = f"ozaki2_dgemm_{m}x{n}x{q}_s{s}_phi{phi:g}"
+    workload = f"ozaki2_dgemm_{m}x{n}x{q}_s{s}_phi{phi:g}" + ("_fast" if args.bound == "fast" else "")
     A, B = hpl_like(m, q, n, phi, seed=args.seed)
     dev = torch.device("cuda:0")
     Ad = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)   # column-major A, lda = m
@@ -130,6 +132,8 @@ def main():
     Cd = torch.empty((n, m), dtype=torch.float64, device=dev)  # column-major C, ldc = m
     stream = torch.cuda.current_stream()
     L.ozgemm_config(s, m, n, q, stream=stream)
+    if args.bound == "fast":
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST)
 
     for _ in range(args.warmup):
         L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
@@ -173,7 +177,7 @@ def main():
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": workload, "m": m, "n": n, "q": q, "s": s, "phi": phi, "seed": args.seed,
-                   "output_dtype": "f64", "layout": "column-major NN"},
+                   "output_dtype": "f64", "layout": "column-major NN", "bit_budget": args.bound},
         "roofline": {
             "bound": "mfma",
             "kernel": "gemm_i8_kernel",
@@ -211,7 +215,7 @@ def main():
         out["correct_bits_native_fp64_dot"] = round(correct_bits(native.cpu().numpy(), A, B, ri, ci), 2)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter)
+        out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter, args.bound)
     L.ozgemm_free()
     print(json.dumps(out), flush=True)
 

@@ -22,7 +22,8 @@ inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
 // Per-modulus constants for the residue kernel (Ozaki II notes §6).
 struct ResidueConsts {
   int s;
-  int k;                        // bits kept: |A'| <= 2^k - 1
+  int k;                        // shift base: row shift is k - e_i
+  int kmag;                     // |A'| < 2^kmag (selects the residue arithmetic)
   int m[OZGEMM_S_MAX];          // moduli
   int lo[OZGEMM_S_MAX];         // -floor(m/2)
   int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1
@@ -57,6 +58,10 @@ hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64
 hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
                                    hipStream_t st);
 hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st);
+// OS II-fast: replace e (f) by e' (f') from Cauchy-Schwarz row (column) norm bounds.
+hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
+                           int kappa, int kb, int32_t* e, hipStream_t st);
+hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, int kb, int32_t* f, hipStream_t st);
 
 // Residues of the rows of X where element (r, l) sits at X[r*rs + l*ls].
 // Writes `rows_pad` x q_pad int8 planes (plane stride rows_pad*q_pad).

@@ -117,6 +117,19 @@ int kbits_exact(int s, int q) {
   return (bl - 1) / 2;
 }
 
+// OS II-fast budget (Ozaki II notes §9): kappa_A + kappa_B = floor(log2(M/2 - 1)),
+// split evenly, so that ||A'_i|| <= 2^kappa_A and ||B'_j|| <= 2^kappa_B keep
+// |(A'B')_ij| < M/2 by Cauchy-Schwarz.
+void fast_budget(int s, int* kappa_a, int* kappa_b) {
+  Big M = product_M(s);
+  Big half;
+  big_divmod_small(M, 2, &half);
+  big_sub_small(half, 1);
+  const int K2 = big_bitlen(half) - 1;
+  *kappa_a = K2 / 2;
+  *kappa_b = K2 - K2 / 2;
+}
+
 int modinv_small(int a, int m) {  // a^-1 mod m, gcd(a, m) = 1
   int t = 0, newt = 1, r = m, newr = a % m;
   while (newr) {
@@ -131,14 +144,31 @@ int modinv_small(int a, int m) {  // a^-1 mod m, gcd(a, m) = 1
   return t < 0 ? t + m : t;
 }
 
-void make_consts(int s, int q, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc) {
+// Shift base k of the residue and CRT kernels and the magnitude bound of A'
+// and B' for the active bit budget: the conservative one (k bits, §5) or
+// OS II-fast (exponents e' relative to kb = max(kappa_A, kappa_B), §9).
+void budget_k(int s, int q, int mode, int* k, int* kmag) {
+  if (mode == OZGEMM_BOUND_FAST) {
+    int ka, kb;
+    fast_budget(s, &ka, &kb);
+    *k = std::max(ka, kb);
+    *kmag = *k + 1;
+  } else {
+    *k = kbits_exact(s, q);
+    *kmag = *k;
+  }
+}
+
+void make_consts(int s, int q, int mode, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc) {
   const auto& mods = moduli_list();
-  const int k = kbits_exact(s, q);
+  int k, kmag;
+  budget_k(s, q, mode, &k, &kmag);
   std::memset(rc, 0, sizeof(*rc));
   std::memset(gc, 0, sizeof(*gc));
   std::memset(cc, 0, sizeof(*cc));
   rc->s = gc->s = cc->s = s;
   rc->k = cc->k = k;
+  rc->kmag = kmag;
   for (int t = 0; t < s; ++t) {
     const int m = mods[t];
     rc->m[t] = gc->m[t] = m;
@@ -218,6 +248,7 @@ struct State {
   Layout lay{};
   bool consts_on_device = false;  // CRT weight table uploaded to the workspace
   std::vector<double> consts_host;
+  int bound = OZGEMM_BOUND_CONSERVATIVE;  // bit budget of Scheme II calls
   bool timing = false;
   std::vector<std::array<hipEvent_t, 5>> events;
   std::string hip_err;
@@ -288,7 +319,7 @@ int check_range(int m, int n, int q, int s) {
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
   if (q >= OZGEMM_Q_LIMIT) return OZGEMM_RANGE;
-  if (q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+  if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
   return 0;
 }
 
@@ -300,15 +331,24 @@ int nchunks_for(int m, int q) {
   return std::max(nch, 1);
 }
 
-int run_scale(int m, int n, int q, const double* A, int lda, const double* B, int ldb, int32_t* e, int32_t* f) {
+int run_scale(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, int32_t* e,
+              int32_t* f) {
   const int mp = (int)round_up((size_t)std::max(g.max_m, 1), ROW_PAD);
   uint64_t* pmax = reinterpret_cast<uint64_t*>(g.ws + g.lay.pmax);
   const int nch = nchunks_for(m, q);
+  const bool fast = g.bound == OZGEMM_BOUND_FAST;
+  int ka = 0, kb = 0;
+  if (fast) fast_budget(s, &ka, &kb);
+  const int kbase = std::max(ka, kb);
   if (m > 0) {
     OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, g.stream));
     OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, g.stream));
+    if (fast) OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, g.stream));
   }
-  if (n > 0) OZ_CHECK(launch_col_exp(B, q, n, ldb, f, g.stream));
+  if (n > 0) {
+    OZ_CHECK(launch_col_exp(B, q, n, ldb, f, g.stream));
+    if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, g.stream));
+  }
   return 0;
 }
 
@@ -319,7 +359,7 @@ int run_residue(int m, int n, int q, int s, const double* A, int lda, const doub
   ResidueConsts rc;
   GemmConsts gc;
   CrtConsts cc;
-  make_consts(s, q, &rc, &gc, &cc);
+  make_consts(s, q, g.bound, &rc, &gc, &cc);
   // A: element (i, l) at A[i + l*lda]; A' copy m x q with ld m
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, Ap, 1, m, g.stream));
   // B seen as rows j: element (j, l) at B[l + j*ldb]; B' copy q x n with ld q
@@ -531,7 +571,7 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   ResidueConsts rc;
   GemmConsts gc;
   CrtConsts cc;
-  make_consts(s, q, &rc, &gc, &cc);
+  make_consts(s, q, g.bound, &rc, &gc, &cc);
   if ((st = ensure_crt_table())) return st;
   cc.wtab = crt_table(s);
 
@@ -541,7 +581,7 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
     for (auto& x : ev) OZ_CHECK(hipEventCreate(&x));
     OZ_CHECK(hipEventRecord(ev[0], g.stream));
   }
-  if ((st = run_scale(m, n, q, A, lda, B, ldb, e, f))) return st;
+  if ((st = run_scale(m, n, q, s, A, lda, B, ldb, e, f))) return st;
   if (timed) OZ_CHECK(hipEventRecord(ev[1], g.stream));
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, g.stream));
   OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
@@ -556,15 +596,43 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   return OZGEMM_OK;
 }
 
-int ozgemm_stage_scale(int m, int n, int q, const double* A, int lda, const double* B, int ldb, int32_t* e,
+int ozgemm_stage_scale(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, int32_t* e,
                        int32_t* f) {
-  int st = check_common(m, n, q, A, lda, B, ldb);
-  if (st) return st;
-  if (e == nullptr && m > 0) return -8;
-  if (f == nullptr && n > 0) return -9;
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (q < 0) return -3;
+  if (s < 1 || s > OZGEMM_S_MAX) return -4;
+  if (A == nullptr && m > 0 && q > 0) return -5;
+  if (lda < std::max(1, m)) return -6;
+  if (B == nullptr && q > 0 && n > 0) return -7;
+  if (ldb < std::max(1, q)) return -8;
+  if (e == nullptr && m > 0) return -9;
+  if (f == nullptr && n > 0) return -10;
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
-  if (m > g.max_m || n > g.max_n || q > g.max_q) return OZGEMM_RANGE;
-  return run_scale(m, n, q, A, lda, B, ldb, e, f);
+  if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
+  return run_scale(m, n, q, s, A, lda, B, ldb, e, f);
+}
+
+int ozgemm_set_bound(int mode) {
+  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST) return -1;
+  g.bound = mode;
+  return OZGEMM_OK;
+}
+
+int ozgemm_bound_budget(int s, int q, int mode, int* kappa_a, int* kappa_b) {
+  if (s < 1 || s > OZGEMM_S_MAX) return -1;
+  if (q < 1 || q >= OZGEMM_Q_LIMIT) return -2;
+  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST) return -3;
+  if (kappa_a == nullptr) return -4;
+  if (kappa_b == nullptr) return -5;
+  if (mode == OZGEMM_BOUND_FAST) {
+    fast_budget(s, kappa_a, kappa_b);
+  } else {
+    const int k = kbits_exact(s, q);
+    if (k < 1) return OZGEMM_RANGE;
+    *kappa_a = *kappa_b = k;
+  }
+  return OZGEMM_OK;
 }
 
 int ozgemm_stage_residue(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb,
@@ -602,7 +670,7 @@ int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8
   ResidueConsts rc;
   GemmConsts gc;
   CrtConsts cc;
-  make_consts(s, q, &rc, &gc, &cc);
+  make_consts(s, q, g.bound, &rc, &gc, &cc);
   OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, g.stream));
   return 0;
 }
@@ -626,7 +694,7 @@ int ozgemm_stage_crt(int m, int n, int q, int s, const uint8_t* rt, const int32_
   ResidueConsts rc;
   GemmConsts gc;
   CrtConsts cc;
-  make_consts(s, q, &rc, &gc, &cc);
+  make_consts(s, q, g.bound, &rc, &gc, &cc);
   if ((st = ensure_crt_table())) return st;
   cc.wtab = crt_table(s);
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));

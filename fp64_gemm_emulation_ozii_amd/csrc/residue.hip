@@ -164,7 +164,7 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
   dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
   const bool rows_contig = (rs == 1);
-  const int mode = c.k <= 50 ? 0 : (c.k <= 53 ? 1 : 2);
+  const int mode = c.kmag <= 50 ? 0 : (c.kmag <= 53 ? 1 : 2);
 #define OZ_RES_LAUNCH(RC, MD)                                                                                \
   hipLaunchKernelGGL((residue_kernel<RC, MD>), grid, dim3(256), 0, st, X, rows, q, rs, ls, ex, c, planes,     \
                      plane_stride, q_pad, prime, prime_rs, prime_ls)

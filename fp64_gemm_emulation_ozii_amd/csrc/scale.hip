@@ -13,6 +13,14 @@
 // columns (consecutive threads read consecutive rows -> coalesced), the
 // chunks are combined by a second small kernel.  A column of B is
 // contiguous: one wavefront per column, then a cross-lane reduction.
+//
+// OS II-fast budget (Ozaki II notes §9: a Cauchy-Schwarz bound of c_max):
+// a second pass bounds each row norm, S_i = sum_l ceil(|a_il| 2^(20 - e_i))^2
+// (an exact integer, at most q 2^40, so the order of the additions does not
+// matter), and replaces e_i by e'_i = kb - d_i with the row shift
+// d_i = kappa - c_i - e_i, 4^c_i the smallest power of four >= S_i 2^-40.
+// Then ||trunc(a_i 2^d_i)|| <= 2^kappa, and the residue and CRT kernels use
+// e'_i exactly like e_i (shift kb - e'_i, unscale e'_i + f'_j - 2 kb).
 #include "oz_internal.h"
 
 namespace oz {
@@ -88,6 +96,83 @@ __global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__
   if (lane == 0) f[j] = exponent_of_bits(v);
 }
 
+constexpr int NORM_GRID = 20;
+
+// ceil(|x| 2^(NORM_GRID - e))^2 as an exact integer (|x| < 2^e).
+__device__ __forceinline__ uint64_t norm_term(double x, int e) {
+  const double t = __builtin_ceil(__builtin_ldexp(__builtin_fabs(x), NORM_GRID - e));
+  const uint64_t u = (uint64_t)t;
+  return u * u;
+}
+
+// e'_i from e_i and the squared-norm bound S (units 2^-2 NORM_GRID).
+__device__ __forceinline__ int32_t fast_exponent(int32_t e, uint64_t S, int kappa, int kb) {
+  if (e == OZGEMM_EXP_NONFINITE) return e;
+  if (S == 0) return 0;
+  const int b = (S == 1) ? 0 : 64 - __clzll((long long)(S - 1));  // ceil(log2 S)
+  const int c = (b + 1) / 2 - NORM_GRID;
+  return kb - (kappa - c - e);
+}
+
+__global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
+                                                                long lda, int chunk,
+                                                                const int32_t* __restrict__ e,
+                                                                uint64_t* __restrict__ psum, int m_stride) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int l0 = blockIdx.y * chunk;
+  const int l1 = min(q, l0 + chunk);
+  uint64_t s0 = 0, s1 = 0;
+  if (i < m) {
+    const int ei = e[i];
+    if (ei != OZGEMM_EXP_NONFINITE) {
+      const double* p = A + i + (long)l0 * lda;
+      int l = l0;
+      for (; l + 2 <= l1; l += 2) {
+        s0 += norm_term(__builtin_nontemporal_load(p), ei);
+        s1 += norm_term(__builtin_nontemporal_load(p + lda), ei);
+        p += 2 * lda;
+      }
+      for (; l < l1; ++l) {
+        s0 += norm_term(*p, ei);
+        p += lda;
+      }
+    }
+  }
+  psum[(long)blockIdx.y * m_stride + i] = s0 + s1;
+}
+
+__global__ __launch_bounds__(256) void row_fast_finalize_kernel(const uint64_t* __restrict__ psum, int m,
+                                                                 int m_stride, int nchunks, int kappa, int kb,
+                                                                 int32_t* __restrict__ e) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= m) return;
+  uint64_t S = 0;
+  for (int c = 0; c < nchunks; ++c) S += psum[(long)c * m_stride + i];
+  e[i] = fast_exponent(e[i], S, kappa, kb);
+}
+
+__global__ __launch_bounds__(256) void col_fast_kernel(const double* __restrict__ B, int q, int n, long ldb,
+                                                        int kappa, int kb, int32_t* __restrict__ f) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= n) return;  // whole wavefront exits together
+  const int fj = f[j];
+  uint64_t S = 0;
+  if (fj != OZGEMM_EXP_NONFINITE) {
+    const double* col = B + (long)j * ldb;
+    uint64_t s0 = 0, s1 = 0;
+    int l = lane;
+    for (; l + 64 < q; l += 128) {
+      s0 += norm_term(__builtin_nontemporal_load(col + l), fj);
+      s1 += norm_term(__builtin_nontemporal_load(col + l + 64), fj);
+    }
+    for (; l < q; l += 64) s0 += norm_term(col[l], fj);
+    S = s0 + s1;
+    for (int off = 32; off > 0; off >>= 1) S += (uint64_t)__shfl_xor((unsigned long long)S, off, 64);
+  }
+  if (lane == 0) f[j] = fast_exponent(fj, S, kappa, kb);
+}
+
 hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,
                                   int nchunks, hipStream_t st) {
   const int chunk = (q + nchunks - 1) / nchunks;
@@ -105,6 +190,22 @@ hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, in
 
 hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st) {
   hipLaunchKernelGGL(col_exp_kernel, dim3((n + 3) / 4), dim3(256), 0, st, B, q, n, (long)ldb, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
+                           int kappa, int kb, int32_t* e, hipStream_t st) {
+  const int chunk = (q + nchunks - 1) / nchunks;
+  dim3 grid((m + 255) / 256, nchunks);
+  hipLaunchKernelGGL(row_norm_partial_kernel, grid, dim3(256), 0, st, A, m, q, (long)lda, chunk, e, psum,
+                     m_stride);
+  hipLaunchKernelGGL(row_fast_finalize_kernel, dim3((m + 255) / 256), dim3(256), 0, st, psum, m, m_stride, nchunks,
+                     kappa, kb, e);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, int kb, int32_t* f, hipStream_t st) {
+  hipLaunchKernelGGL(col_fast_kernel, dim3((n + 3) / 4), dim3(256), 0, st, B, q, n, (long)ldb, kappa, kb, f);
   return hipGetLastError();
 }
 

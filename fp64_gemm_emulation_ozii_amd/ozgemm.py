@@ -24,6 +24,8 @@ OZGEMM_HIP_ERROR = 4
 OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
+OZGEMM_BOUND_CONSERVATIVE = 0
+OZGEMM_BOUND_FAST = 1
 OZGEMM_S1_RN = 0
 OZGEMM_S1_HYBRID = 1
 OZGEMM_S1_K_MAX = 16
@@ -36,6 +38,7 @@ EXPORTS = (
     "ozgemm_stage_residue", "ozgemm_stage_gemm", "ozgemm_stage_crt", "ozgemm_timing", "ozgemm_phase_ms",
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
+    "ozgemm_set_bound", "ozgemm_bound_budget",
 )
 
 _lib = None
@@ -68,7 +71,9 @@ def lib():
         "ozgemm_moduli": (c_int, [c_int, ip]),
         "ozgemm_kbits": (c_int, [c_int, c_int]),
         "ozgemm_plane_dims": (c_int, [c_int, c_int, c_int, ip, ip, ip]),
-        "ozgemm_stage_scale": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp]),
+        "ozgemm_stage_scale": (c_int, [c_int, c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp]),
+        "ozgemm_set_bound": (c_int, [c_int]),
+        "ozgemm_bound_budget": (c_int, [c_int, c_int, c_int, ip, ip]),
         "ozgemm_stage_residue": (c_int, [c_int, c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp, vp, vp, vp, vp]),
         "ozgemm_stage_gemm": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp]),
         "ozgemm_stage_crt": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_int]),
@@ -191,8 +196,8 @@ def ozgemm_dgemm(m, n, q, A, lda, B, ldb, C, ldc, s, check: bool = True) -> int:
     return _check(st, "ozgemm_dgemm") if check else st
 
 
-def ozgemm_stage_scale(m, n, q, A, lda, B, ldb, e, f, check: bool = True) -> int:
-    st = lib().ozgemm_stage_scale(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(e), _ptr(f))
+def ozgemm_stage_scale(m, n, q, s, A, lda, B, ldb, e, f, check: bool = True) -> int:
+    st = lib().ozgemm_stage_scale(m, n, q, s, _ptr(A), lda, _ptr(B), ldb, _ptr(e), _ptr(f))
     return _check(st, "ozgemm_stage_scale") if check else st
 
 
@@ -211,6 +216,17 @@ def ozgemm_stage_gemm(m, n, q, s, Ares, Bres, Ct=None, rt=None, check: bool = Tr
 def ozgemm_stage_crt(m, n, q, s, rt, e, f, C, ldc, check: bool = True) -> int:
     st = lib().ozgemm_stage_crt(m, n, q, s, _ptr(rt), _ptr(e), _ptr(f), _ptr(C), ldc)
     return _check(st, "ozgemm_stage_crt") if check else st
+
+
+def ozgemm_set_bound(mode: int) -> int:
+    return _check(lib().ozgemm_set_bound(mode), "ozgemm_set_bound")
+
+
+def ozgemm_bound_budget(s: int, q: int, mode: int):
+    """(kappa_A, kappa_B) of the bit budget, or raises."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check(lib().ozgemm_bound_budget(s, q, mode, ctypes.byref(a), ctypes.byref(b)), "ozgemm_bound_budget")
+    return a.value, b.value
 
 
 def ozgemm_scheme1_beta(q: int) -> int:

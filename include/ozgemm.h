@@ -60,6 +60,10 @@ extern "C" {
 #define OZGEMM_Q_LIMIT (1 << 17)      /* q must be below this (Ozaki II notes §6) */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
 
+/* Bit budgets of Scheme II (ozgemm_set_bound) */
+#define OZGEMM_BOUND_CONSERVATIVE 0 /* c_max <= q 2^(k_A + k_B), k_A = k_B = k (Ozaki II notes §5) */
+#define OZGEMM_BOUND_FAST         1 /* Cauchy-Schwarz c_max bound, OS II-fast (Ozaki II notes §9) */
+
 /* Scheme I variants (Ozaki I notes, optimized algorithm) */
 #define OZGEMM_S1_RN      0  /* RN split, per-product FP64 accumulation (direction 1) */
 #define OZGEMM_S1_HYBRID  1  /* Hybrid split, group-wise INT32 accumulation (directions 2, 3) */
@@ -122,6 +126,28 @@ int ozgemm_kbits(int s, int q);
  * are padded to *m_pad / *n_pad, the inner dimension to *q_pad. */
 int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
 
+/* Bit budget of later Scheme II calls (ozgemm_dgemm and its stages); the
+ * setting persists until changed (ozgemm_free resets it to conservative).
+ *   OZGEMM_BOUND_CONSERVATIVE: k = floor(1/2 log2((M/2 - 1)/q)) bits per
+ *     entry of every row of A and column of B (Ozaki II notes §5).
+ *   OZGEMM_BOUND_FAST: OS II-fast (Ozaki II notes §9).  With
+ *     kappa_A + kappa_B = floor(log2(M/2 - 1)) split evenly, row i of A is
+ *     scaled by 2^d_i, d_i = kappa_A - c_i - e_i, where 4^c_i is the smallest
+ *     power of four >= S_i 2^-40 and S_i = sum_l ceil(|a_il| 2^(20 - e_i))^2
+ *     (an exact integer bound of ||a_i 2^-e_i||^2 in units of 2^-40); columns
+ *     of B likewise with kappa_B.  Then ||A'_i|| ||B'_j|| <= 2^(kappa_A +
+ *     kappa_B) < M/2 (Cauchy-Schwarz), so the CRT result is still the exact
+ *     A'B', and entries keep more bits whenever a row's norm is well below
+ *     sqrt(q) times its maximum.  The stage exponents become
+ *     e'_i = kb - d_i with kb = max(kappa_A, kappa_B), so that the row shift
+ *     is kb - e'_i and the unscaling exponent e'_i + f'_j - 2 kb.
+ * Returns 0, or -1 for an unknown mode. */
+int ozgemm_set_bound(int mode);
+
+/* Bit budget for (s, q) under `mode`: (k, k) for the conservative bound
+ * (OZGEMM_RANGE if k < 1), (kappa_A, kappa_B) for OS II-fast. */
+int ozgemm_bound_budget(int s, int q, int mode, int *kappa_a, int *kappa_b);
+
 /* ---------------------------------------------------------------------- */
 /* Stage entry points (the same kernels ozgemm_dgemm runs), for parity     */
 /* checks of each integer stage.  All buffers are caller-owned device      */
@@ -131,8 +157,10 @@ int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
 /* Exponents (Ozaki II notes §3, §5): e[i] for i < m with
  * 2^(e_i - 1) <= max_l |a_il| < 2^e_i (0 for an all-zero row,
  * OZGEMM_EXP_NONFINITE for a row holding Inf/NaN); f[j] likewise for the
- * columns of B.  e has m entries, f has n. */
-int ozgemm_stage_scale(int m, int n, int q,
+ * columns of B.  e has m entries, f has n.  Under OZGEMM_BOUND_FAST the
+ * values are the shift exponents e'_i, f'_j of that budget (see
+ * ozgemm_set_bound), which depend on s. */
+int ozgemm_stage_scale(int m, int n, int q, int s,
                        const double *A, int lda, const double *B, int ldb,
                        int32_t *e, int32_t *f);
 

@@ -53,7 +53,7 @@ def run_stages(A: np.ndarray, B: np.ndarray, s: int, lda: int | None = None, ldb
     Ct = torch.full((s * mp * np_,), 7, dtype=torch.int32, device=dev) if want_ct else None
     rt = torch.full((s * mp * np_,), 250, dtype=torch.uint8, device=dev)
     Cd = torch.full((max(n, 1), ldc), 12345.0, dtype=torch.float64, device=dev)
-    L.ozgemm_stage_scale(m, n, q, Ad, lda, Bd, ldb, e, f)
+    L.ozgemm_stage_scale(m, n, q, s, Ad, lda, Bd, ldb, e, f)
     L.ozgemm_stage_residue(m, n, q, s, Ad, lda, Bd, ldb, e, f, Ares, Bres, Ap, Bp)
     L.ozgemm_stage_gemm(m, n, q, s, Ares, Bres, Ct, rt)
     L.ozgemm_stage_crt(m, n, q, s, rt, e, f, Cd, ldc)

@@ -48,7 +48,7 @@ def test_sampled_block_and_exponents(m, q, n, phi):
     L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
     e = torch.empty(m, dtype=torch.int32, device="cuda")
     f = torch.empty(n, dtype=torch.int32, device="cuda")
-    L.ozgemm_stage_scale(m, n, q, Ad, m, Bd, q, e, f)
+    L.ozgemm_stage_scale(m, n, q, s, Ad, m, Bd, q, e, f)
     torch.cuda.synchronize()
     rows = sample_lines(m, 56, seed=1)
     cols = sample_lines(n, 56, seed=2)

@@ -27,9 +27,9 @@ def small_config():
     L.ozgemm_free()
 
 
-def check_all_stages(A, B, s, g, ref=None):
+def check_all_stages(A, B, s, g, ref=None, bound="conservative"):
     """Compare every stage of run_stages output g with the oracle."""
-    C_ref, st = ref if ref is not None else oz.dgemm(A, B, s, stages=True)
+    C_ref, st = ref if ref is not None else oz.dgemm(A, B, s, stages=True, bound=bound)
     m, q = A.shape
     n = B.shape[1]
     assert np.array_equal(g["e"], st["e"]), first_diff(g["e"], st["e"])
