@@ -177,19 +177,21 @@ def smod(X: np.ndarray, m: int) -> np.ndarray:
 
 
 def residue_product(At: np.ndarray, Bt: np.ndarray) -> np.ndarray:
-    """C'_t = A'_t B'_t for int8 residue matrices, exact, as int32
-    (Ozaki II notes §4; §6: exact while q < 2^17).
+    """C'_t = A'_t B'_t for int8 residue matrices, exact, as int64
+    (Ozaki II notes §4).
 
     Every product is an integer of magnitude <= 2^14 and every partial sum of
-    a length-q dot product is an integer of magnitude <= q 2^14 < 2^31, far
-    inside the 53-bit float64 significand, so a float64 matrix product is
-    exact in any summation order.
+    a length-q dot product is an integer of magnitude <= q 2^14, inside the
+    53-bit float64 significand for q < 2^39, so a float64 matrix product is
+    exact in any summation order.  (§6: below q = 2^17 these values also fit
+    int32; for larger q the notes split K into blocks, which changes nothing
+    in the value of C'_t mod m_t, the only thing the method uses.)
     """
     q = At.shape[1]
-    if q >= 2**17:
-        raise ValueError("q >= 2^17: int32 accumulation would not be exact")
+    if q >= 2**39:
+        raise ValueError("q >= 2^39: float64 partial sums would not be exact")
     C = np.asarray(At, dtype=np.float64) @ np.asarray(Bt, dtype=np.float64)
-    return C.astype(np.int32)
+    return C.astype(np.int64)
 
 
 def reduce_product(Ct: np.ndarray, m: int) -> np.ndarray:
@@ -286,10 +288,10 @@ def cs_budget(M: int) -> tuple[int, int]:
 def row_norm_units(A: np.ndarray, e: np.ndarray) -> list[int]:
     """S_i = sum_l ceil(|a_il| 2^(NORM_GRID - e_i))^2, an integer upper bound of
     ||a_i 2^-e_i||^2 in units of 2^(-2 NORM_GRID).  0 for rows that are zero
-    or hold Inf/NaN.  Each term is at most 2^(2 NORM_GRID) and q < 2^17, so the
+    or hold Inf/NaN.  Each term is at most 2^(2 NORM_GRID) and q < 2^23, so the
     int64 sums are exact."""
     A = np.asarray(A, dtype=np.float64)
-    assert A.shape[1] < 2**17
+    assert A.shape[1] < 2**23
     out = []
     for i in range(A.shape[0]):
         if e[i] == NONFINITE:
@@ -344,8 +346,6 @@ def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False, bound: str
     if q == 0:
         C = np.zeros((m, n))
         return (C, {"moduli": mods, "M": M, "k": None, "C": C}) if stages else C
-    if q >= 2**17:
-        raise ValueError("q >= 2^17 is outside the exact int32 range")
     e = row_exponents(A)
     f = col_exponents(B)
     if bound == "conservative":

@@ -246,7 +246,7 @@ def test_residue_product_brute_force():
     At[0, :] = -128
     Bt[:, 0] = -128
     C = oz.residue_product(At, Bt)
-    assert C.dtype == np.int32
+    assert C.dtype == np.int64
     assert product_ok(At, Bt, C)
 
 
@@ -257,8 +257,28 @@ def test_residue_product_worst_case_fits_int32():
     Bt = np.full((q, 1), -128, dtype=np.int8)
     C = oz.residue_product(At, Bt)
     assert int(C[0, 0]) == q * 2 ** facts["product_bound_log2"] < 2**31
-    with pytest.raises(ValueError):
-        oz.residue_product(np.zeros((1, q + 1), np.int8), np.zeros((q + 1, 1), np.int8))
+    # one past the int32 limit: the product leaves int32 and is still exact
+    At = np.full((1, q + 2), -128, dtype=np.int8)
+    Bt = np.full((q + 2, 1), -128, dtype=np.int8)
+    assert int(oz.residue_product(At, Bt)[0, 0]) == (q + 2) * 2**14 > 2**31 - 1
+
+
+def test_long_inner_dimension_brute_force():
+    """q > 2^17 (K split into exact int32 blocks on the GPU): the oracle's
+    result still equals the exact rational product rounded once."""
+    rng = np.random.default_rng(77)
+    q = 2**17 + 300
+    A = (rng.random((3, q)) - 0.5) * np.exp(0.5 * rng.standard_normal((3, q)))
+    B = (rng.random((q, 2)) - 0.5) * np.exp(0.5 * rng.standard_normal((q, 2)))
+    C, st = oz.dgemm(A, B, 14, stages=True)
+    k = st["k"]
+    assert k == oz.kbits(st["M"], q) >= 1
+    to_int = np.vectorize(int, otypes=[object])
+    X = to_int(st["Ap"]).dot(to_int(st["Bp"]))
+    assert np.array_equal(st["X"], X)
+    for i in range(3):
+        for j in range(2):
+            assert C[i, j] == oz.round_scaled(int(X[i, j]), int(st["e"][i]) + int(st["f"][j]) - 2 * k)
 
 
 def test_reduce_product_nonnegative():
