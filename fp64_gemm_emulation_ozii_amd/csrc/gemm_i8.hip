@@ -109,10 +109,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 //  * One barrier per slice, placed before the last step's MFMAs: it publishes
 //    the next slice (after this wave's loads for it have landed) and retires
 //    the current buffer (after this wave's reads of it are in registers).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT, bool MULTI>
+// Inner dimension q >= 2^17 (Ozaki II notes §6, block products): one launch
+// per K block of at most KBLOCK_K entries, each exact in int32
+// (|.| <= 2^16 2^14 < 2^31); with ACC_RT the epilogue adds the block's
+// residue to the residue already in rt, mod m_t.
+constexpr int KBLOCK_K = 1 << 16;
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT, bool MULTI,
+          bool ACC_RT = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
     const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
-    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan) {
+    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan, int k_begin, int k_slices) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
   constexpr int ROWS_PER_KB = 1024 / BK;        // tile rows filled by one wavefront load
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     int8_t* Bs = As + BM * BK;
     const int8_t* ga = Ag;
     const int8_t* gb = Bg;
-    int k0 = kk * BK;
+    int k0 = (k_begin + kk) * BK;
     if (MULTI) {
       const int u = kk / nk;
       k0 = (kk - u * nk) * BK;
@@ -206,11 +213,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int nkt = nk * count;  // K slices of the whole output plane
+  const int nkt = MULTI ? nk * count : k_slices;  // K slices walked by this block
 #pragma unroll
   for (int sidx = 0; sidx < STAGES - 1; ++sidx) issue(sidx, min(sidx, nkt - 1));
   wait_vmcnt<(STAGES - 2) * LPW>();
   __builtin_amdgcn_s_barrier();
+
+  // this plane's modulus, selected without indexing the by-value argument
+  // dynamically (which would copy it to scratch)
+  auto plane_modulus = [&]() {
+    int mm = c.m[0];
+#pragma unroll
+    for (int u = 1; u < OZGEMM_S_MAX; ++u) mm = (u == t) ? c.m[u] : mm;
+    return mm;
+  };
 
   v4i acur[FM], bcur[FN], anxt[FM], bnxt[FN];
   read(0, 0, acur, bcur);
@@ -248,11 +264,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 
   // ---- epilogue: int32 planes and/or residues mod m_t ----
   const long plane = (long)m_pad * n_pad;
-  // select this plane's modulus without indexing the by-value argument
-  // dynamically (which would copy it to scratch)
-  int mt = c.m[0];
-#pragma unroll
-  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+  const int mt = plane_modulus();
   const int c16 = (1 << 16) % mt;
   const float invf = 1.0f / (float)mt;
 #pragma unroll
@@ -267,10 +279,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
         const v16i& v = acc[i][j];
         if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
         if (WRITE_RT) {
-          const uint32_t packed = mod_small(v[4 * g], mt, c16, invf) | (mod_small(v[4 * g + 1], mt, c16, invf) << 8) |
-                                  (mod_small(v[4 * g + 2], mt, c16, invf) << 16) |
-                                  (mod_small(v[4 * g + 3], mt, c16, invf) << 24);
-          *reinterpret_cast<uint32_t*>(rt + off) = packed;
+          uint32_t r0 = mod_small(v[4 * g], mt, c16, invf), r1 = mod_small(v[4 * g + 1], mt, c16, invf);
+          uint32_t r2 = mod_small(v[4 * g + 2], mt, c16, invf), r3 = mod_small(v[4 * g + 3], mt, c16, invf);
+          if (ACC_RT) {  // add the residues of the earlier K blocks, mod m_t
+            const uint32_t old = *reinterpret_cast<const uint32_t*>(rt + off);
+            r0 += old & 0xffu;
+            r1 += (old >> 8) & 0xffu;
+            r2 += (old >> 16) & 0xffu;
+            r3 += old >> 24;
+            r0 = r0 >= (uint32_t)mt ? r0 - mt : r0;
+            r1 = r1 >= (uint32_t)mt ? r1 - mt : r1;
+            r2 = r2 >= (uint32_t)mt ? r2 - mt : r2;
+            r3 = r3 >= (uint32_t)mt ? r3 - mt : r3;
+          }
+          *reinterpret_cast<uint32_t*>(rt + off) = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
         }
       }
       // keep the scheduler from hoisting every accumulator out of AGPRs at once
@@ -287,15 +309,31 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
   const int nblocks = (n_pad / BN) * (m_pad / BM) * c.s;
   const dim3 grid(nblocks), block(WM * WN * 64);
+  const int nk = q_pad / BK;
+  if (q_pad >= OZGEMM_Q_LIMIT && Ct == nullptr && rt != nullptr) {
+    // block products; int32 C_t planes are only asked for while q < 2^17,
+    // where one launch is exact (the padding is zero)
+    constexpr int per = KBLOCK_K / BK;
+    for (int k0 = 0; k0 < nk; k0 += per) {
+      const int cnt = std::min(per, nk - k0);
+      if (k0 == 0)
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false, false>), grid, block, 0, st,
+                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
+      else
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false, true>), grid, block, 0, st,
+                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
+    }
+    return hipGetLastError();
+  }
   if (Ct != nullptr && rt != nullptr)
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, true, false>), grid, block, 0, st, Ares, Bres,
-                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
+                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   else if (Ct != nullptr)
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, false>), grid, block, 0, st, Ares,
-                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
+                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   else if (rt != nullptr)
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false>), grid, block, 0, st, Ares,
-                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr);
+                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   return hipGetLastError();
 }
 
@@ -308,7 +346,7 @@ hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m
   none.m[0] = 2;
   const int nblocks = (n_pad / BN) * (m_pad / BM) * nout;
   hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, true>), dim3(nblocks),
-                     dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan);
+                     dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan, 0, 0);
   return hipGetLastError();
 }
 

@@ -318,7 +318,7 @@ int check_common(int m, int n, int q, const double* A, int lda, const double* B,
 int check_range(int m, int n, int q, int s) {
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
-  if (q >= OZGEMM_Q_LIMIT) return OZGEMM_RANGE;
+  if (q > OZGEMM_Q_MAX) return OZGEMM_RANGE;
   if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
   return 0;
 }
@@ -480,7 +480,7 @@ int ozgemm_config(int s_max, int max_m, int max_n, int max_q, void* hip_stream, 
   if (s_max < 1 || s_max > OZGEMM_S_MAX) return -1;
   if (max_m < 0 || max_m > OZ_MAX_ROWS) return -2;
   if (max_n < 0 || max_n > OZ_MAX_ROWS) return -3;
-  if (max_q < 0 || max_q >= OZGEMM_Q_LIMIT) return -4;
+  if (max_q < 0 || max_q > OZGEMM_Q_MAX) return -4;
   if (workspace == nullptr) return -6;
   const Layout lay = make_layout(max_m, max_n, max_q, s_max);
   if (workspace_bytes < lay.total) return OZGEMM_WORKSPACE_TOO_SMALL;
@@ -535,7 +535,7 @@ int ozgemm_moduli(int s, int* moduli_out) {
 }
 
 int ozgemm_kbits(int s, int q) {
-  if (q >= OZGEMM_Q_LIMIT) return -2;
+  if (q > OZGEMM_Q_MAX) return -2;
   return kbits_exact(s, q);
 }
 
@@ -621,7 +621,7 @@ int ozgemm_set_bound(int mode) {
 
 int ozgemm_bound_budget(int s, int q, int mode, int* kappa_a, int* kappa_b) {
   if (s < 1 || s > OZGEMM_S_MAX) return -1;
-  if (q < 1 || q >= OZGEMM_Q_LIMIT) return -2;
+  if (q < 1 || q > OZGEMM_Q_MAX) return -2;
   if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST) return -3;
   if (kappa_a == nullptr) return -4;
   if (kappa_b == nullptr) return -5;
@@ -665,6 +665,7 @@ int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8
   if (Bres == nullptr) return -6;
   int st = check_range(m, n, q, s);
   if (st) return st;
+  if (Ct != nullptr && q >= OZGEMM_Q_LIMIT) return OZGEMM_RANGE;  // int32 C_t would overflow
   int mp, np, qp;
   dims(m, n, q, &mp, &np, &qp);
   ResidueConsts rc;

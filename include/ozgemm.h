@@ -32,9 +32,11 @@
  *  - s, the number of moduli, is 1..OZGEMM_S_MAX; the moduli are the first s
  *    of the greedy pairwise-coprime sequence 256, 255, 253, 251, 247, 241,
  *    239, 233, 229, 227, 223, 217, 211, 199, 197, 193, 191, 181, 179, 173.
- *  - The inner dimension must satisfy q < 2^17 so that every int8 dot
- *    product (|.| <= q * 2^14) is exact in int32 (Ozaki II notes §6), and s
- *    must leave k >= 1 bits (§5); otherwise OZGEMM_RANGE.
+ *  - Every int8 dot product of length < 2^17 (|.| <= q * 2^14) is exact in
+ *    int32 (Ozaki II notes §6).  For q >= 2^17 the GEMM splits K into blocks
+ *    of 2^16 and folds the int32 accumulators mod m_t between blocks (the
+ *    notes' block products), so q may go up to OZGEMM_Q_MAX; s must leave
+ *    k >= 1 bits (§5).  Otherwise OZGEMM_RANGE.
  *  - Numerics: the result equals X * 2^(e_i + f_j - 2k) rounded once to
  *    nearest-even, where X = (A'B')_ij exactly.  Rows of A / columns of B that
  *    hold Inf or NaN make the outputs they touch NaN; all-zero rows/columns
@@ -52,12 +54,13 @@ extern "C" {
 
 #define OZGEMM_OK                  0
 #define OZGEMM_NOT_CONFIGURED      1  /* ozgemm_config has not succeeded */
-#define OZGEMM_RANGE               2  /* q >= 2^17, or k(s, q) < 1, or size beyond the configured maximum */
+#define OZGEMM_RANGE               2  /* q > OZGEMM_Q_MAX, or k(s, q) < 1, or size beyond the configured maximum */
 #define OZGEMM_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below ozgemm_workspace_bytes(...) */
 #define OZGEMM_HIP_ERROR           4  /* a HIP call failed; ozgemm_strerror(4) names it */
 
 #define OZGEMM_S_MAX 20               /* largest supported number of moduli */
-#define OZGEMM_Q_LIMIT (1 << 17)      /* q must be below this (Ozaki II notes §6) */
+#define OZGEMM_Q_LIMIT (1 << 17)      /* int8 dot products of length < this are exact in int32 (Ozaki II notes §6) */
+#define OZGEMM_Q_MAX   (1 << 27)      /* largest supported inner dimension */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
 
 /* Bit budgets of Scheme II (ozgemm_set_bound) */

@@ -60,8 +60,10 @@ def test_kbits_match_oracle(q):
             assert got == want, (s, q)
 
 
-def test_kbits_rejects_q_limit():
-    assert L.ozgemm_kbits(14, 2**17) < 0
+def test_kbits_accepts_long_k_and_rejects_q_max():
+    assert L.ozgemm_kbits(14, 2**17) == oz.kbits(oz.crt_constants(oz.greedy_moduli(14))[0], 2**17)
+    assert L.ozgemm_kbits(14, 2**20) == oz.kbits(oz.crt_constants(oz.greedy_moduli(14))[0], 2**20)
+    assert L.ozgemm_kbits(14, L.OZGEMM_Q_MAX + 1) < 0
 
 
 def test_workspace_and_plane_dims():
@@ -108,7 +110,7 @@ def test_validation_before_any_launch():
     assert lib.ozgemm_config(16, 512, 512, 512, None, FAKE, ws - 1) == L.OZGEMM_WORKSPACE_TOO_SMALL
     assert lib.ozgemm_config(0, 512, 512, 512, None, FAKE, ws) == -1
     assert lib.ozgemm_config(16, -1, 512, 512, None, FAKE, ws) == -2
-    assert lib.ozgemm_config(16, 512, 512, 2**17, None, FAKE, ws) == -4
+    assert lib.ozgemm_config(16, 512, 512, L.OZGEMM_Q_MAX + 1, None, FAKE, ws) == -4
     assert lib.ozgemm_config(16, 512, 512, 512, None, None, ws) == -6
     assert lib.ozgemm_config(16, 512, 512, 512, None, FAKE, ws) == 0
     Cp = FAKE + (1 << 30)

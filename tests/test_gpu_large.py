@@ -34,6 +34,7 @@ def sample_lines(size: int, count: int, seed: int, tile: int = 256):
     (16384, 1024, 16384, 1.0),
     (1024, 65536, 1024, 1.0),
     (16384, 16384, 16384, 4.0),
+    (512, 2**20, 512, 1.0),
 ])
 def test_sampled_block_and_exponents(m, q, n, phi):
     import torch

@@ -171,3 +171,38 @@ def test_1024_cube_full_oracle(s):
     ref = oz.dgemm(A, B, s, stages=True)
     log(f"1024^3 s={s}: compare")
     check_all_stages(A, B, s, g, ref=ref)
+
+
+@pytest.mark.parametrize("s,q", [(14, 2**17 + 300), (10, 140000), (14, 2**17 - 100)])
+def test_long_inner_dimension(s, q):
+    """q >= 2^17: the GEMM folds its int32 accumulators mod m_t every 2^16 of
+    K (block products); residues of the products and C must still match."""
+    import torch
+    A, B = hpl_like(65, q, 70, 1.0, seed=q % 1000)
+    L.ozgemm_free()
+    configure(256, 256, q, 20)
+    try:
+        log(f"long K s={s} q={q}")
+        g = run_stages(A, B, s, want_ct=q < 2**17, want_prime=True)
+        C, _ = run_dgemm(A, B, s)
+    finally:
+        L.ozgemm_free()
+        torch.cuda.empty_cache()
+        configure(1536, 1536, 1536, 20)
+    ref = oz.dgemm(A, B, s, stages=True)
+    check_all_stages(A, B, s, g, ref=ref)
+    assert same_doubles(C, ref[0])
+
+
+def test_long_inner_dimension_refuses_int32_planes():
+    import torch
+    L.ozgemm_free()
+    configure(256, 256, 2**17 + 128, 14)
+    try:
+        z8 = torch.zeros(14 * 256 * (2**17 + 128), dtype=torch.int8, device="cuda")
+        ct = torch.zeros(14 * 256 * 256, dtype=torch.int32, device="cuda")
+        st = L.ozgemm_stage_gemm(10, 10, 2**17 + 1, 14, z8, z8, ct, None, check=False)
+        assert st == L.OZGEMM_RANGE
+    finally:
+        L.ozgemm_free()
+        configure(1536, 1536, 1536, 20)
