@@ -16,10 +16,10 @@
 //    with M/2 on a double approximation; only inside a band of relative width
 //    2^-40 around M/2 is the comparison made exactly on the limbs.  Outside
 //    (-M/2, M/2) X moves by one M, exactly.
-// 4. |X| as non-negative 32-bit limbs (floor carries), then rounding to
-//    nearest-even of |X| 2^scale from a 64-bit window plus a sticky bit; the
-//    rounding position moves up for subnormal results, and results past the
-//    double range become +-Inf.
+// 4. X in two's-complement 64-bit words, |X|, then rounding to nearest-even
+//    of |X| 2^scale from a 64-bit window plus a sticky bit; the rounding
+//    position moves up for subnormal results, and results past the double
+//    range become +-Inf.
 #pragma once
 
 #include <stdint.h>
@@ -126,43 +126,52 @@ __host__ __device__ __forceinline__ double reconstruct_limbs(const double* S_in,
     carry_limbs<L, false>(x);
   }
 
-  // 4. |X| as non-negative 32-bit limbs, then one rounding
-  const int sg = sign_limbs<L>(x);
-  if (sg == 0) return 0.0;
+  // 4. X as a two's-complement integer in 64-bit words (each balanced limb
+  //    fits int32: |X| < M/2 < 2^(32 L - 1) keeps even the top limb below
+  //    2^31), then |X| and one rounding from its 64 leading bits.
+  constexpr int NW = (L + 1) / 2;
+  uint64_t w[NW];
 #pragma unroll
-  for (int l = 0; l < L; ++l) x[l] = sg < 0 ? -x[l] : x[l];
-  carry_limbs<L, true>(x);
-  uint32_t u[L];
+  for (int v = 0; v < NW; ++v) {
+    const int64_t lo = (int64_t)(int32_t)x[2 * v];
+    const int64_t hi = (2 * v + 1 < L) ? (int64_t)(int32_t)x[2 * v + 1] : 0;
+    w[v] = (uint64_t)lo + ((uint64_t)hi << 32);
+  }
+  // word v holds lo + hi 2^32 as a signed value; carry the signs upward
 #pragma unroll
-  for (int l = 0; l < L; ++l) u[l] = (uint32_t)x[l];
-
-  // normalise so that u[L-1] holds the leading nonzero limb
-  int h = L - 1;
+  for (int v = 0; v + 1 < NW; ++v) {
+    const int64_t sv = (int64_t)w[v];  // signed value of this word (fits: |.| < 2^63)
+    if (sv < 0) w[v + 1] -= 1;         // w[v] read as unsigned = sv + 2^64
+  }
+  const bool neg = (int64_t)w[NW - 1] < 0;
+  if (neg) {  // two's-complement negation of the whole number
+    uint64_t borrow = 1;
 #pragma unroll
-  for (int it = 0; it + 1 < L; ++it) {
-    if (u[L - 1] == 0) {
-#pragma unroll
-      for (int l = L - 1; l > 0; --l) u[l] = u[l - 1];
-      u[0] = 0;
-      --h;
+    for (int v = 0; v < NW; ++v) {
+      const uint64_t nv = ~w[v] + borrow;
+      borrow = (borrow && nv == 0) ? 1 : 0;
+      w[v] = nv;
     }
   }
-  const int lz = __builtin_clz(u[L - 1]);
-  const uint64_t hi64 = ((uint64_t)u[L - 1] << 32) | (L >= 2 ? (uint64_t)u[L - 2] : 0ull);
-  const uint32_t lo32 = (L >= 3) ? u[L - 3] : 0u;
-  uint64_t T = hi64;
-  uint32_t rest = lo32;
-  if (lz > 0) {
-    T = (hi64 << lz) | (uint64_t)(lo32 >> (32 - lz));
-    rest = lo32 << lz;
-  }
-  bool sticky = rest != 0;
+  // leading 64 bits: top word with nonzero content, and the next one
+  int top = -1;
 #pragma unroll
-  for (int l = 0; l + 3 < L; ++l) sticky = sticky || (u[l] != 0);
-  // the leading bit of |X| is bit 32 h + 31 - lz; T holds it in bit 63
-  const int E = 32 * h + 31 - lz + scale;
-  const double res = round_window(T, sticky, E);
-  return sg < 0 ? -res : res;
+  for (int v = 0; v < NW; ++v)
+    if (w[v] != 0) top = v;
+  if (top < 0) return 0.0;
+  uint64_t hiw = 0, low = 0, rest = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    if (v == top) hiw = w[v];
+    if (v == top - 1) low = w[v];
+    if (v < top - 1) rest |= w[v];
+  }
+  const int lz = __builtin_clzll(hiw);
+  const uint64_t T = lz ? (hiw << lz) | (low >> (64 - lz)) : hiw;
+  const bool sticky = ((lz ? (low << lz) : low) != 0) || rest != 0;
+  // the leading bit of |X| is bit 64 top + 63 - lz; T holds it in bit 63
+  const double res = round_window(T, sticky, 64 * top + 63 - lz + scale);
+  return neg ? -res : res;
 }
 
 }  // namespace oz
