@@ -7,10 +7,10 @@
 // of W_t = M_t y_t; every S[l] is an integer below 2^46, held exactly in a
 // double.  Z = sum_l S[l] 2^(32 l).
 //
-// 1. Balanced carries: c = floor(S[l] 2^-32 + 1/2) moves into S[l+1], leaving
-//    S[l] in [-2^31, 2^31).  All operations are exact in FP64.
-// 2. Q = rint(Z / M) from the two top limbs; Q <= 20 * 255, right or off by
-//    one.  X[l] = S[l] - Q M[l] is exact (|.| < 2^47); rebalance.
+// 1. Q = rint(Z / M) from the two top limb sums; Q <= 20 * 255, right or off
+//    by one.  X[l] = S[l] - Q M[l] is exact (|.| < 2^47).
+// 2. Balanced carries: c = floor(X[l] 2^-32 + 1/2) moves into X[l+1], leaving
+//    X[l] in [-2^31, 2^31).  All operations are exact in FP64.
 // 3. With balanced limbs the sign of X is the sign of its top nonzero limb
 //    (the lower ones add up to less than one unit of it).  |X| is compared
 //    with M/2 on a double approximation; only inside a band of relative width
@@ -42,7 +42,17 @@ namespace oz {
 // bits of |X| (bit 63 set) and `sticky` tells whether any lower bit is set.
 __host__ __device__ __forceinline__ double round_window(uint64_t T, bool sticky, int E) {
   if (E >= 1024) return __builtin_inf();
-  const int keep = (E + 1075 < 53) ? E + 1075 : 53;  // significant bits the result can hold
+  if (E >= -1022) {
+    // normal result: 53 significant bits; the rounded significand (bit 52
+    // set, or 2^53 after a carry) added to the exponent field gives the
+    // double directly, including the carry into the next binade and the
+    // overflow to +Inf at E = 1023
+    const uint64_t mant = T >> 11;
+    const uint64_t rem = T & 0x7ff;
+    const bool up = (rem > 0x400) || (rem == 0x400 && (sticky || (mant & 1)));
+    return __builtin_bit_cast(double, ((uint64_t)(E + 1022) << 52) + mant + (up ? 1 : 0));
+  }
+  const int keep = E + 1075;  // significant bits a subnormal result can hold (< 53)
   if (keep <= 0) {
     if (keep == 0) {
       // value in [2^-1075, 2^-1074): above the tie -> smallest subnormal
@@ -51,7 +61,7 @@ __host__ __device__ __forceinline__ double round_window(uint64_t T, bool sticky,
     }
     return 0.0;
   }
-  const int drop = 64 - keep;  // 11..63
+  const int drop = 64 - keep;  // 12..63
   const uint64_t mant = T >> drop;
   const uint64_t rem = T & ((1ull << drop) - 1);
   const uint64_t halfv = 1ull << (drop - 1);
@@ -90,17 +100,14 @@ struct CrtModulus {
 
 template <int L>
 __host__ __device__ __forceinline__ double reconstruct_limbs(const double* S_in, const CrtModulus& K, int scale) {
+  // 2. X = Z - Q M, limb by limb on the raw sums (|S_l| < 2^46 and
+  //    Q M_l < 2^45, so every limb stays an exact integer below 2^47)
+  double zf = S_in[L - 1] * __builtin_ldexp(1.0, 32 * (L - 1));
+  if (L >= 2) zf += S_in[L - 2] * __builtin_ldexp(1.0, 32 * (L - 2));
+  const double Q = __builtin_rint(zf * K.invM);
   double x[L];
 #pragma unroll
-  for (int l = 0; l < L; ++l) x[l] = S_in[l];
-  carry_limbs<L, false>(x);
-
-  // 2. X = Z - Q M
-  double zf = x[L - 1] * __builtin_ldexp(1.0, 32 * (L - 1));
-  if (L >= 2) zf += x[L - 2] * __builtin_ldexp(1.0, 32 * (L - 2));
-  const double Q = __builtin_rint(zf * K.invM);
-#pragma unroll
-  for (int l = 0; l < L; ++l) x[l] = __builtin_fma(-Q, K.Ml[l], x[l]);
+  for (int l = 0; l < L; ++l) x[l] = __builtin_fma(-Q, K.Ml[l], S_in[l]);
   carry_limbs<L, false>(x);
 
   // 3. symmetric representative
@@ -143,15 +150,14 @@ __host__ __device__ __forceinline__ double reconstruct_limbs(const double* S_in,
     const int64_t sv = (int64_t)w[v];  // signed value of this word (fits: |.| < 2^63)
     if (sv < 0) w[v + 1] -= 1;         // w[v] read as unsigned = sv + 2^64
   }
-  const bool neg = (int64_t)w[NW - 1] < 0;
-  if (neg) {  // two's-complement negation of the whole number
-    uint64_t borrow = 1;
+  // |X|: two's-complement negation under a mask (no branch)
+  const uint64_t negmask = (uint64_t)((int64_t)w[NW - 1] >> 63);
+  uint64_t carry = negmask & 1u;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const uint64_t nv = ~w[v] + borrow;
-      borrow = (borrow && nv == 0) ? 1 : 0;
-      w[v] = nv;
-    }
+  for (int v = 0; v < NW; ++v) {
+    const uint64_t nv = (w[v] ^ negmask) + carry;
+    carry = (carry != 0 && nv == 0) ? 1u : 0u;
+    w[v] = nv;
   }
   // leading 64 bits: top word with nonzero content, and the next one
   int top = -1;
@@ -171,7 +177,7 @@ __host__ __device__ __forceinline__ double reconstruct_limbs(const double* S_in,
   const bool sticky = ((lz ? (low << lz) : low) != 0) || rest != 0;
   // the leading bit of |X| is bit 64 top + 63 - lz; T holds it in bit 63
   const double res = round_window(T, sticky, 64 * top + 63 - lz + scale);
-  return neg ? -res : res;
+  return __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, res) | (negmask << 63));
 }
 
 }  // namespace oz
