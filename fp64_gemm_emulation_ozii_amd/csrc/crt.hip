@@ -40,15 +40,9 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
   for (int j = blockIdx.y; j < n; j += gridDim.y) {
     const int fj = f[j];
     const uint8_t* p = rt + (long)j * m_pad + i0;
-    // residues of the four rows for every modulus (planes past s are never
-    // read: their slot loads plane s - 1 and is zeroed, as is its weight)
-    uint32_t rr[OZGEMM_S_MAX];
-#pragma unroll
-    for (int t = 0; t < OZGEMM_S_MAX; ++t) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(p + (long)min(t, s - 1) * plane);
-      rr[t] = (t < s) ? v : 0u;
-    }
     // 1. exact FP64 limb sums for the four rows, moduli in groups of four
+    //    (planes past s are never read: their slot loads plane s - 1 and is
+    //    zeroed, as is its weight)
     double S[4][L];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -57,30 +51,38 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
 #pragma unroll
     for (int tg = 0; tg < OZGEMM_S_MAX; tg += 4) {
       if (tg < s) {
+        uint32_t rr[4];
 #pragma unroll
-        for (int t = tg; t < tg + 4; ++t) {
+        for (int d = 0; d < 4; ++d) {
+          const int t = tg + d;
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(p + (long)min(t, s - 1) * plane);
+          rr[d] = (t < s) ? v : 0u;
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int t = tg + d;
           double w[L];
 #pragma unroll
           for (int l = 0; l < L; ++l) w[l] = wl[t * MAX_LIMBS + l];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const double r = (double)((rr[t] >> (8 * u)) & 0xffu);
+            const double r = (double)((rr[d] >> (8 * u)) & 0xffu);
 #pragma unroll
             for (int l = 0; l < L; ++l) S[u][l] = __builtin_fma(r, w[l], S[u][l]);
           }
         }
       }
     }
-    double res[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      res[u] = reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
-      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res[u] = __builtin_nan("");
-    }
+    // 2. one row at a time (keeps the live registers of a single
+    //    reconstruction, so more wavefronts fit on a SIMD)
     double* out = C + (long)j * ldc + i0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + u < m) out[u] = res[u];
+    for (int u = 0; u < 4; ++u) {
+      double res = reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
+      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res = __builtin_nan("");
+      if (i0 + u < m) out[u] = res;
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
