@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const int t = tg + d;
+          if (t >= s) break;  // uniform: the last group may be partial
           double w[L];
 #pragma unroll
           for (int l = 0; l < L; ++l) w[l] = wl[t * MAX_LIMBS + l];
