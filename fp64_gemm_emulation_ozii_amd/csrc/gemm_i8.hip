@@ -21,7 +21,7 @@
 // LDS: each tile row (BK bytes) is stored as 16-byte chunks whose position
 // is XOR-permuted by a function of the row, so that the rows an MFMA operand
 // load touches fall in distinct bank groups.  K slices move from HBM straight
-// into LDS through STAGES buffers.
+// into LDS through two buffers.
 #include "oz_internal.h"
 
 namespace oz {
@@ -97,26 +97,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 // step whatever order the hardware takes the bytes in.  Lane l receives rows
 // 8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
 //
-// Data movement:
+// Data movement and instruction order:
 //  * K slices of BK bytes go from HBM straight into LDS (global_load_lds, 16
-//    bytes per lane, no register staging) through STAGES buffers; the slice
-//    STAGES-1 ahead is requested as soon as its buffer is free.  Past the
-//    last slice the last one is re-requested, so every iteration has the same
-//    number of loads in flight and the loop needs no branches.
-//  * Inside a slice the operand fragments of the next 32-wide step are read
-//    from LDS into a second register set while the current step's MFMAs run
-//    (one read issued after each MFMA), so LDS latency stays hidden.
-//  * One barrier per slice, placed before the last step's MFMAs: it publishes
-//    the next slice (after this wave's loads for it have landed) and retires
-//    the current buffer (after this wave's reads of it are in registers).
+//    bytes per lane, no register staging) through two buffers.
+//  * One barrier per slice, placed before the last 32-wide step's MFMAs: it
+//    publishes slice kt + 1 (this wave's loads of it have landed) and retires
+//    buffer kt mod 2 (this wave's reads of it are in registers).
+//  * Every step is a fixed sequence of 16 MFMA slots.  The fragments of the
+//    next step are read from LDS after the even slots (eight reads), and the
+//    16 loads of the slice two ahead go after the odd slots of the 32 slots
+//    that follow the barrier (the last step of slice kt, then step 0 of slice
+//    kt + 1).  Spreading the loads this way keeps their issue from stalling
+//    the MFMA stream, and the last of them still has two steps to land.
+//    (Measured at 8192^3 x 14 planes: 7.1 ms with the loads issued as one
+//    burst per slice, 6.3 ms with this order.)
 // Inner dimension q >= 2^17 (Ozaki II notes §6, block products): one launch
 // per K block of at most KBLOCK_K entries, each exact in int32
 // (|.| <= 2^16 2^14 < 2^31); with ACC_RT the epilogue adds the block's
 // residue to the residue already in rt, mod m_t.
 constexpr int KBLOCK_K = 1 << 16;
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool WRITE_CT, bool WRITE_RT, bool MULTI,
-          bool ACC_RT = false>
+template <int BM, int BN, int BK, int WM, int WN, bool WRITE_CT, bool WRITE_RT, bool MULTI, bool ACC_RT = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
     const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
     int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan, int k_begin, int k_slices) {
@@ -129,11 +130,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int NKS = BK / 32;                  // 32-wide MFMA steps per slice
+  constexpr int NF = FM + FN;                   // fragments per step
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
-  static_assert(STAGES >= 2 && (STAGES - 2) * LPW < 64, "pipeline depth");
-  static_assert(FM * FN >= FM + FN, "interleave pattern");
+  static_assert(FM * FN == 16 && NF == 8 && NKS >= 2, "slot plan: 16 MFMAs, 8 reads per step");
+  static_assert(2 * LPW <= 16 * NKS, "every load has an odd slot in its window");
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * (BM + BN) * BK];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * (BM + BN) * BK];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -164,9 +166,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   const int lane_src1 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb + ROWS_PER_KB)) * 16);
   const long kb_stride = (long)ROWS_PER_KB * q_pad;  // source distance of consecutive 1 KB loads
 
-  const int nk = q_pad / BK;  // K slices per product
-  auto issue = [&](int buf, int kk) {
-    int8_t* As = smem + buf * (BM + BN) * BK;
+  const int nk = q_pad / BK;                      // K slices per product
+  const int nkt = MULTI ? nk * count : k_slices;  // K slices walked by this block
+  // load li (A blocks first, then B) of walked slice kk into buffer kk mod 2
+  auto load1 = [&](int kk, int li) {
+    int8_t* As = smem + (kk & 1) * (BM + BN) * BK;
     int8_t* Bs = As + BM * BK;
     const int8_t* ga = Ag;
     const int8_t* gb = Bg;
@@ -177,34 +181,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
       ga += u * a_plane;
       gb -= u * b_plane;
     }
-    ga += (long)(wave * A_LOADS) * kb_stride + k0;
-    gb += (long)(wave * B_LOADS) * kb_stride + k0;
-#pragma unroll
-    for (int p = 0; p < A_LOADS; ++p)
-      __builtin_amdgcn_global_load_lds(ga + p * kb_stride + (((wave * A_LOADS + p) & 1) ? lane_src1 : lane_src0),
-                                       As + (wave * A_LOADS + p) * 1024, 16, 0, 0);
-#pragma unroll
-    for (int p = 0; p < B_LOADS; ++p)
-      __builtin_amdgcn_global_load_lds(gb + p * kb_stride + (((wave * B_LOADS + p) & 1) ? lane_src1 : lane_src0),
-                                       Bs + (wave * B_LOADS + p) * 1024, 16, 0, 0);
+    if (li < A_LOADS) {
+      const int blk = wave * A_LOADS + li;
+      __builtin_amdgcn_global_load_lds(ga + blk * kb_stride + k0 + ((blk & 1) ? lane_src1 : lane_src0),
+                                       As + blk * 1024, 16, 0, 0);
+    } else {
+      const int blk = wave * B_LOADS + (li - A_LOADS);
+      __builtin_amdgcn_global_load_lds(gb + blk * kb_stride + k0 + ((blk & 1) ? lane_src1 : lane_src0),
+                                       Bs + blk * 1024, 16, 0, 0);
+    }
   };
 
   const int lrow = lane & 31;
   const int lkc = lane >> 5;  // K chunk (of 2) within a 32-wide step
-  auto read = [&](int buf, int ks, v4i* af, v4i* bf) {
+  // fragment f of step ks in buffer buf: f < FN are B columns, the rest A rows
+  auto read1 = [&](int buf, int ks, int f) -> v4i {
     const int8_t* As = smem + buf * (BM + BN) * BK;
     const int8_t* Bs = As + BM * BK;
     const int kc = ks * 2 + lkc;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wn * WTN + j * 32 + lrow;
-      bf[j] = *reinterpret_cast<const v4i*>(&Bs[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
+    if (f < FN) {
+      const int row = wn * WTN + f * 32 + lrow;
+      return *reinterpret_cast<const v4i*>(&Bs[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wm * WTM + i * 32 + lrow;
-      af[i] = *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
-    }
+    const int row = wm * WTM + (f - FN) * 32 + lrow;
+    return *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
   };
 
   v16i acc[FM][FN];
@@ -213,58 +213,60 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int nkt = MULTI ? nk * count : k_slices;  // K slices walked by this block
+  // The window after barrier kt - 1 holds 16 NKS slots: the last step of
+  // slice kt - 1 (slots 0..15), then steps 0..NKS-2 of slice kt.  Its loads
+  // fetch slice kt + 1 into the buffer retired by that barrier; load li goes
+  // after slot 2 li + 1.  The prologue stands in for the part of window 0
+  // that precedes slice 0.
 #pragma unroll
-  for (int sidx = 0; sidx < STAGES - 1; ++sidx) issue(sidx, min(sidx, nkt - 1));
-  wait_vmcnt<(STAGES - 2) * LPW>();
+  for (int li = 0; li < LPW; ++li) load1(0, li);
+  if (nkt > 1)
+#pragma unroll
+    for (int li = 0; li < LPW; ++li)
+      if (2 * li + 1 < 16) load1(1, li);
+  wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
 
-  // this plane's modulus, selected without indexing the by-value argument
-  // dynamically (which would copy it to scratch)
-  auto plane_modulus = [&]() {
-    int mm = c.m[0];
+  v4i cur[NF], nxt[NF];
 #pragma unroll
-    for (int u = 1; u < OZGEMM_S_MAX; ++u) mm = (u == t) ? c.m[u] : mm;
-    return mm;
-  };
+  for (int f = 0; f < NF; ++f) cur[f] = read1(0, 0, f);
 
-  v4i acur[FM], bcur[FN], anxt[FM], bnxt[FN];
-  read(0, 0, acur, bcur);
   for (int kt = 0; kt < nkt; ++kt) {
-    issue((kt + STAGES - 1) % STAGES, min(kt + STAGES - 1, nkt - 1));
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if (ks + 1 < NKS) {
-        read(kt % STAGES, ks + 1, anxt, bnxt);
-      } else {
+      const bool last = ks == NKS - 1;
+      const int lslice = last ? kt + 2 : kt + 1;  // slice fetched in this step's window
+      if (last) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slice kt are done
-        wait_vmcnt<(STAGES - 2) * LPW>();    // this wave's loads of slice kt + 1 have landed
+        wait_vmcnt<0>();                     // this wave's loads of slice kt + 1 have landed
         __builtin_amdgcn_s_barrier();
-        read((kt + 1) % STAGES, 0, anxt, bnxt);  // (past the end: unused)
+      }
+      const int rbuf = last ? (kt + 1) & 1 : kt & 1;  // (past the end: read, unused)
+      const int rks = last ? 0 : ks + 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = r / FN, j = r % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+        if ((r & 1) == 0) nxt[r / 2] = read1(rbuf, rks, r / 2);
+        const int slot = last ? r : 16 + ks * 16 + r;
+#pragma unroll
+        for (int li = 0; li < LPW; ++li)
+          if (2 * li + 1 == slot && lslice < nkt) load1(lslice, li);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[i], bcur[j], acc[i][j], 0, 0, 0);
-      // one LDS read after each MFMA while the reads last
-#pragma unroll
-      for (int r = 0; r < FM + FN; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) acur[i] = anxt[i];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bcur[j] = bnxt[j];
+      for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
     }
   }
   wait_vmcnt<0>();  // no load into LDS may outlive the block
 
   // ---- epilogue: int32 planes and/or residues mod m_t ----
+  // this plane's modulus, selected without indexing the by-value argument
+  // dynamically (which would copy it to scratch)
+  int mt = c.m[0];
+#pragma unroll
+  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
   const long plane = (long)m_pad * n_pad;
-  const int mt = plane_modulus();
   const int c16 = (1 << 16) % mt;
   const float invf = 1.0f / (float)mt;
 #pragma unroll
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad, const GemmConsts& c,
                        int32_t* Ct, uint8_t* rt, hipStream_t st) {
-  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, STAGES = 2;
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
   const int nblocks = (n_pad / BN) * (m_pad / BM) * c.s;
   const dim3 grid(nblocks), block(WM * WN * 64);
@@ -317,35 +319,35 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
     for (int k0 = 0; k0 < nk; k0 += per) {
       const int cnt = std::min(per, nk - k0);
       if (k0 == 0)
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false, false>), grid, block, 0, st,
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false>), grid, block, 0, st,
                            Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
       else
-        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false, true>), grid, block, 0, st,
+        hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, true>), grid, block, 0, st,
                            Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
     }
     return hipGetLastError();
   }
   if (Ct != nullptr && rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, true, false>), grid, block, 0, st, Ares, Bres,
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, true, false>), grid, block, 0, st, Ares, Bres,
                        m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   else if (Ct != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, false>), grid, block, 0, st, Ares,
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, false, false>), grid, block, 0, st, Ares,
                        Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   else if (rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, false, true, false>), grid, block, 0, st, Ares,
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false>), grid, block, 0, st, Ares,
                        Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m_pad, int n_pad, int q_pad,
                              const int4* plan, int nout, int32_t* P, hipStream_t st) {
-  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, STAGES = 2;
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
   if (m_pad % BM || n_pad % BN || q_pad % BK || nout < 1) return hipErrorInvalidValue;
   GemmConsts none{};
   none.s = 1;
   none.m[0] = 2;
   const int nblocks = (n_pad / BN) * (m_pad / BM) * nout;
-  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, STAGES, true, false, true>), dim3(nblocks),
+  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, false, true>), dim3(nblocks),
                      dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan, 0, 0);
   return hipGetLastError();
 }
