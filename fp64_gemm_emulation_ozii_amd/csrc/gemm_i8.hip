@@ -23,6 +23,7 @@
 // load touches fall in distinct bank groups.  K slices move from HBM straight
 // into LDS through two buffers.
 #include "oz_internal.h"
+#include "prod_mod.h"
 
 namespace oz {
 
@@ -66,20 +67,6 @@ __host__ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int t
   const int in_group = tile % (GROUP_M * tiles_n);
   mi = first_m + in_group % gm;
   nj = in_group / gm;
-}
-
-// C mod m for an int32 C, as a value in [0, m).  C = h 2^16 + l with
-// |h| <= 2^15 and 0 <= l < 2^16, so x = h (2^16 mod m) + l satisfies
-// |x| < 2^24 and is exact in FP32; x - m floor(x / m) computed with an FP32
-// reciprocal is then exact and off by at most one multiple of m.
-__device__ __forceinline__ uint32_t mod_small(int v, int m, int c16, float invf) {
-  const int x = (v >> 16) * c16 + (v & 0xffff);
-  const float xf = (float)x;
-  const float qf = __builtin_floorf(xf * invf);
-  int r = (int)__builtin_fmaf(-qf, (float)m, xf);
-  r = r < 0 ? r + m : r;
-  r = r >= m ? r - m : r;
-  return (uint32_t)r;
 }
 
 // s_waitcnt with only the vector-memory counter constrained to <= N.
@@ -267,8 +254,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
   const long plane = (long)m_pad * n_pad;
-  const int c16 = (1 << 16) % mt;
-  const float invf = 1.0f / (float)mt;
+  const double md = (double)mt, inv = 1.0 / md;  // correctly rounded
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -281,8 +267,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
         const v16i& v = acc[i][j];
         if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
         if (WRITE_RT) {
-          uint32_t r0 = mod_small(v[4 * g], mt, c16, invf), r1 = mod_small(v[4 * g + 1], mt, c16, invf);
-          uint32_t r2 = mod_small(v[4 * g + 2], mt, c16, invf), r3 = mod_small(v[4 * g + 3], mt, c16, invf);
+          uint32_t r0 = mod_product(v[4 * g], md, inv), r1 = mod_product(v[4 * g + 1], md, inv);
+          uint32_t r2 = mod_product(v[4 * g + 2], md, inv), r3 = mod_product(v[4 * g + 3], md, inv);
           if (ACC_RT) {  // add the residues of the earlier K blocks, mod m_t
             const uint32_t old = *reinterpret_cast<const uint32_t*>(rt + off);
             r0 += old & 0xffu;
