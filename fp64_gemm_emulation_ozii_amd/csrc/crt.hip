@@ -4,14 +4,17 @@
 // the symmetric representative is the integer product A'B' itself;
 // §7 steps 4-6: accumulate, reduce, unscale by D^-1 and E^-1.
 //
-// 1. S_l = sum_t r_t w_{t,l}, where w_{t,l} < 2^32 are the 32-bit limbs of
-//    W_t = M_t y_t (a small device table, staged in LDS per block).  Each
-//    term is < 2^40 and there are at most 20, so every partial sum is an
-//    integer below 2^45 and FP64 fused multiply-adds are exact.
-// 2. The limb sums go to reconstruct_limbs (crt_reconstruct.h): balanced
-//    carries, X = Z - Q M with Q = rint(Z / M), one exact shift by M into
-//    (-M/2, M/2), and a single rounding of X * 2^(e_i + f_j - 2k) to
-//    nearest-even (subnormal and overflowing results included).
+// 1. S_l = sum_t r_t w_{t,l}, where w_{t,l} are the W-bit limbs of
+//    W_t = M_t y_t (a small device table, staged in LDS per block).  With
+//    W = 32 each term is < 2^40 and there are at most 20, so every partial
+//    sum is below 2^45; with W = 40 (used while log2 M <= 120, s <= 15)
+//    each term is < 2^48 and the sums stay below 2^52.  Either way the FP64
+//    fused multiply-adds are exact.
+// 2. The limb sums go to reconstruct40 or reconstruct_limbs
+//    (crt_reconstruct.h): balanced carries, X = Z - Q M with
+//    Q = rint(Z / M), one exact shift by M into (-M/2, M/2), and a single
+//    rounding of X * 2^(e_i + f_j - 2k) to nearest-even (subnormal and
+//    overflowing results included).
 #include "oz_internal.h"
 
 namespace oz {
@@ -22,7 +25,7 @@ namespace {
 // each modulus come in as one 32-bit load (the planes are padded to whole
 // tiles, so rows up to the padded height are always readable).  The limbs of
 // W_t sit in LDS, read once per modulus for all four rows.
-template <int L>
+template <int L, bool W40>
 __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt, int m, int n, int m_pad,
                                                    long plane, const int32_t* __restrict__ e,
                                                    const int32_t* __restrict__ f, CrtConsts c,
@@ -79,7 +82,8 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
     double* out = C + (long)j * ldc + i0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      double res = reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
+      double res = W40 ? reconstruct40<(L <= 3 ? L : 3)>(S[u], c.K, ei[u] + fj - 2 * c.k)
+                       : reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
       if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res = __builtin_nan("");
       if (i0 + u < m) out[u] = res;
       __builtin_amdgcn_sched_barrier(0);
@@ -99,20 +103,26 @@ hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, con
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
   dim3 grid((m + 1023) / 1024, std::min(n, 65535));
   const long plane = (long)m_pad * n_pad;
-  switch (c.L) {
-#define OZ_CRT_CASE(LL)                                                                                      \
-  case LL:                                                                                                    \
-    hipLaunchKernelGGL((crt_kernel<LL>), grid, dim3(256), 0, st, rt, m, n, m_pad, plane, e, f, c, C, (long)ldc); \
-    break;
-    OZ_CRT_CASE(1)
-    OZ_CRT_CASE(2)
-    OZ_CRT_CASE(3)
-    OZ_CRT_CASE(4)
-    OZ_CRT_CASE(5)
-#undef OZ_CRT_CASE
-    default:
-      return hipErrorInvalidValue;
+#define OZ_CRT_CASE(LL, WW)                                                                                \
+  hipLaunchKernelGGL((crt_kernel<LL, WW>), grid, dim3(256), 0, st, rt, m, n, m_pad, plane, e, f, c, C, (long)ldc)
+  if (c.W == 40) {
+    switch (c.L) {
+      case 1: OZ_CRT_CASE(1, true); break;
+      case 2: OZ_CRT_CASE(2, true); break;
+      case 3: OZ_CRT_CASE(3, true); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (c.L) {
+      case 1: OZ_CRT_CASE(1, false); break;
+      case 2: OZ_CRT_CASE(2, false); break;
+      case 3: OZ_CRT_CASE(3, false); break;
+      case 4: OZ_CRT_CASE(4, false); break;
+      case 5: OZ_CRT_CASE(5, false); break;
+      default: return hipErrorInvalidValue;
+    }
   }
+#undef OZ_CRT_CASE
   return hipGetLastError();
 }
 

@@ -20,6 +20,18 @@
 //    of |X| 2^scale from a 64-bit window plus a sticky bit; the rounding
 //    position moves up for subnormal results, and results past the double
 //    range become +-Inf.
+//
+// reconstruct40 is the same computation on 40-bit limbs (used while
+// log2 M <= 120, i.e. at most three limbs): S[l] = sum_t r_t w_{t,l} with
+// w_{t,l} < 2^40 stays below 2^53 for s <= 15, the balanced carries leave
+// limbs in [-2^39, 2^39], and the single rounding of X = x0 + x1 2^40 +
+// x2 2^80 is done in FP64 as the correctly rounded sum of three exact terms
+// (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+// proved algorithms using rounding to odd", IEEE TC 2008: two error-free
+// additions, a round-to-odd addition of the two errors, and one final
+// round-to-nearest addition).  Results that would be subnormal take an
+// exact 128-bit integer path instead, since scaling a rounded value into the
+// subnormal range would round twice.
 #pragma once
 
 #include <stdint.h>
@@ -178,6 +190,117 @@ __host__ __device__ __forceinline__ double reconstruct_limbs(const double* S_in,
   // the leading bit of |X| is bit 64 top + 63 - lz; T holds it in bit 63
   const double res = round_window(T, sticky, 64 * top + 63 - lz + scale);
   return __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, res) | (negmask << 63));
+}
+
+
+// ---------------------------------------------------------------------------
+// 40-bit limbs
+// ---------------------------------------------------------------------------
+
+// Balanced carries between 40-bit limbs: each limb but the top one ends in
+// [-2^39, 2^39].  Exact while every limb stays below 2^53.
+template <int L>
+__host__ __device__ __forceinline__ void carry40(double* x) {
+#pragma unroll
+  for (int l = 0; l + 1 < L; ++l) {
+    const double c = __builtin_rint(x[l] * 0x1p-40);
+    x[l] = __builtin_fma(c, -0x1p40, x[l]);
+    x[l + 1] += c;
+  }
+}
+
+// s = a + b rounded to odd: the exact sum when representable, otherwise
+// whichever neighbour of it has an odd last significand bit.
+__host__ __device__ __forceinline__ double add_round_odd(double a, double b) {
+  const double s = a + b;
+  const double bb = s - a;
+  const double e = (a - (s - bb)) + (b - bb);  // a + b = s + e exactly
+  uint64_t u = __builtin_bit_cast(uint64_t, s);
+  if (e != 0.0 && (u & 1u) == 0) {
+    // away from zero when e has the sign of s, towards zero otherwise
+    const bool away = (e > 0.0) == (s > 0.0);
+    u = away ? u + 1 : u - 1;
+  }
+  return __builtin_bit_cast(double, u);
+}
+
+// Exact rounding of X 2^scale, X = x0 + x1 2^40 + x2 2^80 (limbs exact,
+// |x_l| < 2^53), from the 128-bit integer X; used for subnormal results.
+__host__ __device__ inline double round_limbs40_exact(double x0, double x1, double x2, int scale) {
+  const __int128 X = (__int128)(int64_t)x0 + (__int128)(int64_t)x1 * ((__int128)1 << 40) +
+                     (__int128)(int64_t)x2 * ((__int128)1 << 80);
+  if (X == 0) return 0.0;
+  const bool neg = X < 0;
+  const unsigned __int128 u = neg ? (unsigned __int128)(-X) : (unsigned __int128)X;
+  const uint64_t hi = (uint64_t)(u >> 64), lo = (uint64_t)u;
+  const int top = hi ? 127 - __builtin_clzll(hi) : 63 - __builtin_clzll(lo);  // leading bit position
+  uint64_t T;
+  bool sticky;
+  if (top >= 63) {
+    const int sh = top - 63;
+    T = (uint64_t)(u >> sh);
+    sticky = sh > 0 && (u & (((unsigned __int128)1 << sh) - 1)) != 0;
+  } else {
+    T = lo << (63 - top);
+    sticky = false;
+  }
+  const double r = round_window(T, sticky, top + scale);
+  return neg ? -r : r;
+}
+
+template <int L>
+__host__ __device__ __forceinline__ double reconstruct40(const double* S_in, const CrtModulus& K, int scale) {
+  static_assert(L >= 1 && L <= 3, "40-bit limbs: at most three");
+  // 2. X = Z - Q M (|S_l| < 2^53 - 2^52, Q M_l < 2^52: exact)
+  double zf = S_in[L - 1] * __builtin_ldexp(1.0, 40 * (L - 1));
+  if (L >= 2) zf = __builtin_fma(S_in[L - 2], __builtin_ldexp(1.0, 40 * (L - 2)), zf);
+  const double Q = __builtin_rint(zf * K.invM);
+  double x[L];
+#pragma unroll
+  for (int l = 0; l < L; ++l) x[l] = __builtin_fma(-Q, K.Ml[l], S_in[l]);
+  carry40<L>(x);
+
+  // 3. symmetric representative
+  double xa = x[0];
+  if (L >= 2) xa = __builtin_fma(x[1], 0x1p40, xa);
+  if (L >= 3) xa = __builtin_fma(x[2], 0x1p80, xa);
+  const double ax = xa < 0 ? -xa : xa;
+  int shift_m = 0;  // X -> X - shift_m * M
+  if (ax > K.halfM * (1.0 + 0x1p-40)) {
+    shift_m = xa > 0 ? 1 : -1;
+  } else if (ax >= K.halfM * (1.0 - 0x1p-40)) {
+    // exact: is |X| > M/2 ?  (|X| = M/2 cannot occur)
+    const int sx = sign_limbs<L>(x);
+    double d[L];
+#pragma unroll
+    for (int l = 0; l < L; ++l) d[l] = x[l] - (double)sx * K.Hl[l];
+    carry40<L>(d);
+    if (sign_limbs<L>(d) == sx) shift_m = sx;
+  }
+  if (shift_m != 0) {
+#pragma unroll
+    for (int l = 0; l < L; ++l) x[l] = __builtin_fma(-(double)shift_m, K.Ml[l], x[l]);
+    carry40<L>(x);
+  }
+
+  // 4. z = RN(X): x0, x1 2^40 and x2 2^80 are exact; with the balanced
+  //    limbs |x0| < 2^40 <= |x1 2^40| and |x1 2^40 + x0| < 2^80 <= |x2 2^80|
+  //    (when nonzero), so both error-free additions may be Fast2Sum
+  double z;
+  if (L == 1) {
+    z = x[0];
+  } else if (L == 2) {
+    z = __builtin_fma(x[1], 0x1p40, x[0]);
+  } else {
+    const double b = x[1] * 0x1p40, c = x[0], a = x[L - 1] * 0x1p80;
+    const double uh = b + c, ul = c - (uh - b);
+    const double th = a + uh, tl = uh - (th - a);
+    z = th + add_round_odd(tl, ul);
+  }
+  if (z == 0.0) return 0.0;
+  const int ez = (int)((__builtin_bit_cast(uint64_t, z) >> 52) & 0x7ff) - 1023;  // z is an integer, normal
+  if (ez + scale < -1022) return round_limbs40_exact(x[0], L >= 2 ? x[1] : 0.0, L >= 3 ? x[2] : 0.0, scale);
+  return __builtin_ldexp(z, scale);
 }
 
 }  // namespace oz

@@ -38,11 +38,12 @@ struct GemmConsts {
   double inv[OZGEMM_S_MAX];
 };
 
-// CRT constants (Ozaki II notes §4).  The 32-bit limbs of W_t = M_t y_t < M
+// CRT constants (Ozaki II notes §4).  The W-bit limbs of W_t = M_t y_t < M
 // are stored as doubles in a device table (wtab[t * MAX_LIMBS + l]) so that
 // sum_t r_t W_t accumulates exactly in FP64; the rest travels by value.
 struct CrtConsts {
   int s;
+  int W;                             // limb width: 40 (log2 M <= 120) or 32
   int L;                             // limbs of M (top limb nonzero)
   int k;
   const double* wtab;                // device: s x MAX_LIMBS limbs of W_t

@@ -66,6 +66,16 @@ int big_bitlen(const Big& a) {
   return 0;
 }
 
+// Bits [lo, lo + width) of a (width <= 40) as a double.
+double big_bits(const Big& a, int lo, int width) {
+  uint64_t v = 0;
+  for (int b = 0; b < width; ++b) {
+    const int bit = lo + b;
+    if (bit < 32 * BIG_LIMBS && ((a.w[bit / 32] >> (bit % 32)) & 1u)) v |= 1ull << b;
+  }
+  return (double)v;
+}
+
 double big_to_double(const Big& a) {
   double d = 0.0;
   for (int i = BIG_LIMBS - 1; i >= 0; --i) d = d * 4294967296.0 + (double)a.w[i];
@@ -159,6 +169,11 @@ void budget_k(int s, int q, int mode, int* k, int* kmag) {
   }
 }
 
+// Limb width of the CRT sums: 40 bits while three limbs hold M (log2 M <=
+// 120, s <= 15), where r_t w_{t,l} summed over s <= 15 moduli stays below
+// 2^53; 32 bits otherwise.
+int crt_width(int s) { return big_bitlen(product_M(s)) <= 120 ? 40 : 32; }
+
 void make_consts(int s, int q, int mode, ResidueConsts* rc, GemmConsts* gc, CrtConsts* cc) {
   const auto& mods = moduli_list();
   int k, kmag;
@@ -179,21 +194,24 @@ void make_consts(int s, int q, int mode, ResidueConsts* rc, GemmConsts* gc, CrtC
   }
   const Big M = product_M(s);
   const int bits = big_bitlen(M);
-  cc->L = (bits + 31) / 32;
+  cc->W = crt_width(s);
+  cc->L = (bits + cc->W - 1) / cc->W;
   Big half;
   big_divmod_small(M, 2, &half);
   for (int l = 0; l < MAX_LIMBS; ++l) {
-    cc->K.Ml[l] = l < BIG_LIMBS ? (double)M.w[l] : 0.0;
-    cc->K.Hl[l] = l < BIG_LIMBS ? (double)half.w[l] : 0.0;
+    cc->K.Ml[l] = big_bits(M, l * cc->W, cc->W);
+    cc->K.Hl[l] = big_bits(half, l * cc->W, cc->W);
   }
   cc->K.halfM = big_to_double(half);
   cc->K.invM = 1.0 / big_to_double(M);
 }
 
-// W_t = M_t y_t limbs for s moduli, written to out[t * MAX_LIMBS + l].
+// W_t = M_t y_t limbs (crt_width(s) bits each) for s moduli, written to
+// out[t * MAX_LIMBS + l].
 void crt_weights(int s, double* out) {
   const auto& mods = moduli_list();
   const Big M = product_M(s);
+  const int width = crt_width(s);
   for (int t = 0; t < OZGEMM_S_MAX; ++t)
     for (int l = 0; l < MAX_LIMBS; ++l) out[t * MAX_LIMBS + l] = 0.0;
   for (int t = 0; t < s; ++t) {
@@ -204,7 +222,7 @@ void crt_weights(int s, double* out) {
     const int y = modinv_small((int)Mt_mod, (int)mt);
     Big W = Mt;
     big_mul_small(W, (uint32_t)y);  // W_t = M_t y_t < M
-    for (int l = 0; l < MAX_LIMBS; ++l) out[t * MAX_LIMBS + l] = (double)W.w[l];
+    for (int l = 0; l < MAX_LIMBS; ++l) out[t * MAX_LIMBS + l] = big_bits(W, l * width, width);
   }
 }
 

@@ -48,6 +48,13 @@ __device__ __forceinline__ int smod_small(double a, int m, double inv, int lo, i
   return ri;
 }
 
+// Low bytes of four words as one word (three byte permutes).
+__device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.0, b1.0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // b2.0, b3.0, 0, 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // Same without correction, kept in FP64 (|a| < 2^50).
 __device__ __forceinline__ double smod_exact_d(double a, double m, double inv) {
   const double qf = __builtin_floor(__builtin_fma(a, inv, 0.5));
@@ -131,11 +138,35 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
   }
 
   int8_t* dst = planes + (long)grow * q_pad + l0 + cseg;
+  if (MODE == 0) {
+    // |A'| < 2^50: A' + 1.5 2^52 is exact, and so is fma(-q, m, A' + 1.5 2^52)
+    // = 1.5 2^52 + r, whose low 32 bits are r in two's complement
+    // (|r| <= 128 < 2^51); no conversion instruction is needed
+    double am[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) am[j] = a[j] + 0x1.8p52;
+    for (int t = 0; t < c.s; ++t) {
+      const double md = (double)c.m[t], inv = c.inv[t];
+      uint32_t rb[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const double qf = __builtin_floor(__builtin_fma(a[j], inv, 0.5));
+        rb[j] = (uint32_t)__builtin_bit_cast(uint64_t, __builtin_fma(-qf, md, am[j]));
+      }
+      uint4 out;
+      out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
+      out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
+      out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
+      out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
+      *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
+    }
+    return;
+  }
   for (int t = 0; t < c.s; ++t) {
     const int m = c.m[t];
     const double inv = c.inv[t];
     const int lo = c.lo[t], hi = c.hi[t];
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    uint32_t rb[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       int ri;
@@ -143,15 +174,15 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
         const double rh = smod_exact_d(ahi[j], (double)m, inv);
         ri = smod_small<false>(__builtin_fma(rh, c.c32[t], a[j]), m, inv, lo, hi);
       } else {
-        ri = smod_small<MODE != 0>(a[j], m, inv, lo, hi);
+        ri = smod_small<true>(a[j], m, inv, lo, hi);
       }
-      packed[j >> 2] |= ((uint32_t)ri & 0xffu) << (8 * (j & 3));
+      rb[j] = (uint32_t)ri;
     }
     uint4 out;
-    out.x = packed[0];
-    out.y = packed[1];
-    out.z = packed[2];
-    out.w = packed[3];
+    out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
+    out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
+    out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
+    out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
     *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
   }
 }

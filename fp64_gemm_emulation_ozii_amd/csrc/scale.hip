@@ -47,23 +47,23 @@ __global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __re
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int l0 = blockIdx.y * chunk;
   const int l1 = min(q, l0 + chunk);
-  uint64_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  uint64_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (i < m) {
     const double* p = A + i + (long)l0 * lda;
     int l = l0;
-    for (; l + 4 <= l1; l += 4) {
-      v0 = umax64(v0, abs_bits(__builtin_nontemporal_load(p)));
-      v1 = umax64(v1, abs_bits(__builtin_nontemporal_load(p + lda)));
-      v2 = umax64(v2, abs_bits(__builtin_nontemporal_load(p + 2 * lda)));
-      v3 = umax64(v3, abs_bits(__builtin_nontemporal_load(p + 3 * lda)));
-      p += 4 * lda;
+    for (; l + 8 <= l1; l += 8) {  // eight independent loads in flight
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = umax64(v[u], abs_bits(__builtin_nontemporal_load(p + u * lda)));
+      p += 8 * lda;
     }
     for (; l < l1; ++l) {
-      v0 = umax64(v0, abs_bits(*p));
+      v[0] = umax64(v[0], abs_bits(*p));
       p += lda;
     }
   }
-  pmax[(long)blockIdx.y * m_stride + i] = umax64(umax64(v0, v1), umax64(v2, v3));
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v[0] = umax64(v[0], v[u]);
+  pmax[(long)blockIdx.y * m_stride + i] = v[0];
 }
 
 __global__ __launch_bounds__(256) void row_exp_finalize_kernel(const uint64_t* __restrict__ pmax, int m,
@@ -82,16 +82,15 @@ __global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= n) return;  // whole wavefront exits together
   const double* col = B + (long)j * ldb;
-  uint64_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  uint64_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int l = lane;
-  for (; l + 192 < q; l += 256) {
-    v0 = umax64(v0, abs_bits(__builtin_nontemporal_load(col + l)));
-    v1 = umax64(v1, abs_bits(__builtin_nontemporal_load(col + l + 64)));
-    v2 = umax64(v2, abs_bits(__builtin_nontemporal_load(col + l + 128)));
-    v3 = umax64(v3, abs_bits(__builtin_nontemporal_load(col + l + 192)));
-  }
-  for (; l < q; l += 64) v0 = umax64(v0, abs_bits(col[l]));
-  uint64_t v = umax64(umax64(v0, v1), umax64(v2, v3));
+  for (; l + 448 < q; l += 512)  // eight independent loads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = umax64(w[u], abs_bits(__builtin_nontemporal_load(col + l + 64 * u)));
+  for (; l < q; l += 64) w[0] = umax64(w[0], abs_bits(col[l]));
+  uint64_t v = w[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v = umax64(v, w[u]);
   for (int off = 32; off > 0; off >>= 1) v = umax64(v, (uint64_t)__shfl_xor((unsigned long long)v, off, 64));
   if (lane == 0) f[j] = exponent_of_bits(v);
 }
