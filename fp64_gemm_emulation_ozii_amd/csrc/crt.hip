@@ -23,9 +23,11 @@ namespace {
 
 // Thread = 4 consecutive rows of one output column: the product residues of
 // each modulus come in as one 32-bit load (the planes are padded to whole
-// tiles, so rows up to the padded height are always readable).  The limbs of
-// W_t sit in LDS, read once per modulus for all four rows.
-template <int L, bool W40>
+// tiles, so rows up to the padded height are always readable), all s of them
+// issued before the first is used.  The limbs of W_t sit in LDS, read once
+// per modulus for all four rows.  NG = ceil(s / 4): only the last group of
+// four moduli can be partial.
+template <int L, bool W40, int NG>
 __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt, int m, int n, int m_pad,
                                                    long plane, const int32_t* __restrict__ e,
                                                    const int32_t* __restrict__ f, CrtConsts c,
@@ -43,38 +45,27 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
   for (int j = blockIdx.y; j < n; j += gridDim.y) {
     const int fj = f[j];
     const uint8_t* p = rt + (long)j * m_pad + i0;
-    // 1. exact FP64 limb sums for the four rows, moduli in groups of four
-    //    (planes past s are never read: their slot loads plane s - 1 and is
-    //    zeroed, as is its weight)
+    // 1. exact FP64 limb sums for the four rows
+    uint32_t rr[4 * NG];
+#pragma unroll
+    for (int t = 0; t < 4 * NG; ++t)
+      rr[t] = (t < 4 * (NG - 1) || t < s) ? *reinterpret_cast<const uint32_t*>(p + (long)t * plane) : 0u;
     double S[4][L];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int l = 0; l < L; ++l) S[u][l] = 0.0;
 #pragma unroll
-    for (int tg = 0; tg < OZGEMM_S_MAX; tg += 4) {
-      if (tg < s) {
-        uint32_t rr[4];
+    for (int t = 0; t < 4 * NG; ++t) {
+      if (t >= 4 * (NG - 1) && t >= s) break;  // uniform: the last group may be partial
+      double w[L];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int t = tg + d;
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(p + (long)min(t, s - 1) * plane);
-          rr[d] = (t < s) ? v : 0u;
-        }
+      for (int l = 0; l < L; ++l) w[l] = wl[t * MAX_LIMBS + l];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int t = tg + d;
-          if (t >= s) break;  // uniform: the last group may be partial
-          double w[L];
+      for (int u = 0; u < 4; ++u) {
+        const double r = (double)((rr[t] >> (8 * u)) & 0xffu);
 #pragma unroll
-          for (int l = 0; l < L; ++l) w[l] = wl[t * MAX_LIMBS + l];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const double r = (double)((rr[d] >> (8 * u)) & 0xffu);
-#pragma unroll
-            for (int l = 0; l < L; ++l) S[u][l] = __builtin_fma(r, w[l], S[u][l]);
-          }
-        }
+        for (int l = 0; l < L; ++l) S[u][l] = __builtin_fma(r, w[l], S[u][l]);
       }
     }
     // 2. one row at a time (keeps the live registers of a single
@@ -103,25 +94,36 @@ hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, con
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
   dim3 grid((m + 1023) / 1024, std::min(n, 65535));
   const long plane = (long)m_pad * n_pad;
-#define OZ_CRT_CASE(LL, WW)                                                                                \
-  hipLaunchKernelGGL((crt_kernel<LL, WW>), grid, dim3(256), 0, st, rt, m, n, m_pad, plane, e, f, c, C, (long)ldc)
+  const int ng = (c.s + 3) / 4;
+  if (ng < 1 || ng > 5) return hipErrorInvalidValue;
+#define OZ_CRT_NG(LL, WW)                                                                                     \
+  switch (ng) {                                                                                             \
+    case 1: OZ_CRT_CASE(LL, WW, 1); break;                                                                  \
+    case 2: OZ_CRT_CASE(LL, WW, 2); break;                                                                  \
+    case 3: OZ_CRT_CASE(LL, WW, 3); break;                                                                  \
+    case 4: OZ_CRT_CASE(LL, WW, 4); break;                                                                  \
+    default: OZ_CRT_CASE(LL, WW, 5); break;                                                                 \
+  }
+#define OZ_CRT_CASE(LL, WW, GG)                                                                               \
+  hipLaunchKernelGGL((crt_kernel<LL, WW, GG>), grid, dim3(256), 0, st, rt, m, n, m_pad, plane, e, f, c, C, (long)ldc)
   if (c.W == 40) {
     switch (c.L) {
-      case 1: OZ_CRT_CASE(1, true); break;
-      case 2: OZ_CRT_CASE(2, true); break;
-      case 3: OZ_CRT_CASE(3, true); break;
+      case 1: OZ_CRT_NG(1, true); break;
+      case 2: OZ_CRT_NG(2, true); break;
+      case 3: OZ_CRT_NG(3, true); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (c.L) {
-      case 1: OZ_CRT_CASE(1, false); break;
-      case 2: OZ_CRT_CASE(2, false); break;
-      case 3: OZ_CRT_CASE(3, false); break;
-      case 4: OZ_CRT_CASE(4, false); break;
-      case 5: OZ_CRT_CASE(5, false); break;
+      case 1: OZ_CRT_NG(1, false); break;
+      case 2: OZ_CRT_NG(2, false); break;
+      case 3: OZ_CRT_NG(3, false); break;
+      case 4: OZ_CRT_NG(4, false); break;
+      case 5: OZ_CRT_NG(5, false); break;
       default: return hipErrorInvalidValue;
     }
   }
+#undef OZ_CRT_NG
 #undef OZ_CRT_CASE
   return hipGetLastError();
 }

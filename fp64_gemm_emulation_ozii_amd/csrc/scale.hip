@@ -66,14 +66,28 @@ __global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __re
   pmax[(long)blockIdx.y * m_stride + i] = v[0];
 }
 
+// 64 rows per block, four threads per row each taking every fourth chunk
+// (eight loads in flight), combined through LDS.
 __global__ __launch_bounds__(256) void row_exp_finalize_kernel(const uint64_t* __restrict__ pmax, int m,
                                                                 int m_stride, int nchunks,
                                                                 int32_t* __restrict__ e) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= m) return;
-  uint64_t v = 0;
-  for (int c = 0; c < nchunks; ++c) v = umax64(v, pmax[(long)c * m_stride + i]);
-  e[i] = exponent_of_bits(v);
+  __shared__ uint64_t part[4][64];
+  const int r = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + r;
+  uint64_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (i < m) {
+    int c = g;
+    for (; c + 28 < nchunks; c += 32)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = umax64(v[u], pmax[(long)(c + 4 * u) * m_stride + i]);
+    for (; c < nchunks; c += 4) v[0] = umax64(v[0], pmax[(long)c * m_stride + i]);
+  }
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v[0] = umax64(v[0], v[u]);
+  part[g][r] = v[0];
+  __syncthreads();
+  if (g == 0 && i < m)
+    e[i] = exponent_of_bits(umax64(umax64(part[0][r], part[1][r]), umax64(part[2][r], part[3][r])));
 }
 
 __global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__ B, int q, int n, long ldb,
@@ -182,7 +196,7 @@ hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64
 
 hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
                                    hipStream_t st) {
-  hipLaunchKernelGGL(row_exp_finalize_kernel, dim3((m + 255) / 256), dim3(256), 0, st, pmax, m, m_stride, nchunks,
+  hipLaunchKernelGGL(row_exp_finalize_kernel, dim3((m + 63) / 64), dim3(256), 0, st, pmax, m, m_stride, nchunks,
                      e);
   return hipGetLastError();
 }
