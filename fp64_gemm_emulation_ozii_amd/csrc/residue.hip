@@ -72,29 +72,40 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
   const int l0 = blockIdx.x * TK;
 
   // ---- coalesced load into LDS (zero outside the matrix) ----
-  if (ROWS_CONTIG) {
+  // All loads are issued before any is used: out-of-range lanes read a
+  // clamped, valid element and store zero instead (q >= 1; with no rows at
+  // all nothing is read and the tile is zero padding).
+  if (rows < 1) {
+    for (int idx = tid; idx < TR * LDS_STRIDE; idx += 256) tile[idx] = 0.0;
+  } else if (ROWS_CONTIG) {
     // consecutive lanes -> consecutive rows of one column
     const int r = tid & (TR - 1);
     const int lsub = tid >> 5;  // 0..7
     const bool rok = (r0 + r) < rows;
+    const double* src = X + (long)min(r0 + r, rows - 1);
+    double v[TK / 8];
+#pragma unroll
+    for (int it = 0; it < TK / 8; ++it)
+      v[it] = __builtin_nontemporal_load(src + (long)min(l0 + lsub + 8 * it, q - 1) * ls);
 #pragma unroll
     for (int it = 0; it < TK / 8; ++it) {
       const int l = lsub + 8 * it;
-      double v = 0.0;
-      if (rok && (l0 + l) < q) v = __builtin_nontemporal_load(X + (long)(r0 + r) + (long)(l0 + l) * ls);
-      tile[r * LDS_STRIDE + l] = v;
+      tile[r * LDS_STRIDE + l] = (rok && (l0 + l) < q) ? v[it] : 0.0;
     }
   } else {
     // consecutive lanes -> consecutive inner-dimension entries of one row
     const int l = tid & (TK - 1);
     const int rsub = tid >> 7;  // 0..1
     const bool lok = (l0 + l) < q;
+    const double* src = X + (long)min(l0 + l, q - 1);
+    double v[TR / 2];
+#pragma unroll
+    for (int it = 0; it < TR / 2; ++it)
+      v[it] = __builtin_nontemporal_load(src + (long)min(r0 + rsub + 2 * it, rows - 1) * rs);
 #pragma unroll
     for (int it = 0; it < TR / 2; ++it) {
       const int r = rsub + 2 * it;
-      double v = 0.0;
-      if (lok && (r0 + r) < rows) v = __builtin_nontemporal_load(X + (long)(r0 + r) * rs + (long)(l0 + l));
-      tile[r * LDS_STRIDE + l] = v;
+      tile[r * LDS_STRIDE + l] = (lok && (r0 + r) < rows) ? v[it] : 0.0;
     }
   }
   __syncthreads();
@@ -192,6 +203,7 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
 hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad, double* prime,
                           long prime_rs, long prime_ls, hipStream_t st) {
+  if (q < 1) return hipErrorInvalidValue;  // q = 0 has no residues (callers handle it)
   dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
   const bool rows_contig = (rs == 1);
