@@ -61,27 +61,35 @@ __global__ __launch_bounds__(256) void s1_split_kernel(const double* __restrict_
   const int r0 = blockIdx.y * TR;
   const int l0 = blockIdx.x * TK;
 
-  if (ROWS_CONTIG) {
+  // all loads in flight before any is used; out-of-range lanes read a
+  // clamped valid element and store zero (q >= 1; no rows: zero tile)
+  if (rows < 1) {
+    for (int idx = tid; idx < TR * LDS_STRIDE; idx += 256) tile[idx] = 0.0;
+  } else if (ROWS_CONTIG) {
     const int r = tid & (TR - 1);
     const int lsub = tid >> 5;
     const bool rok = (r0 + r) < rows;
+    const double* src = X + (long)min(r0 + r, rows - 1);
+    double v[TK / 8];
+#pragma unroll
+    for (int it = 0; it < TK / 8; ++it) v[it] = src[(long)min(l0 + lsub + 8 * it, q - 1) * ls];
 #pragma unroll
     for (int it = 0; it < TK / 8; ++it) {
       const int l = lsub + 8 * it;
-      double v = 0.0;
-      if (rok && (l0 + l) < q) v = X[(long)(r0 + r) + (long)(l0 + l) * ls];
-      tile[r * LDS_STRIDE + l] = v;
+      tile[r * LDS_STRIDE + l] = (rok && (l0 + l) < q) ? v[it] : 0.0;
     }
   } else {
     const int l = tid & (TK - 1);
     const int rsub = tid >> 7;
     const bool lok = (l0 + l) < q;
+    const double* src = X + (long)min(l0 + l, q - 1);
+    double v[TR / 2];
+#pragma unroll
+    for (int it = 0; it < TR / 2; ++it) v[it] = src[(long)min(r0 + rsub + 2 * it, rows - 1) * rs];
 #pragma unroll
     for (int it = 0; it < TR / 2; ++it) {
       const int r = rsub + 2 * it;
-      double v = 0.0;
-      if (lok && (r0 + r) < rows) v = X[(long)(r0 + r) * rs + (long)(l0 + l)];
-      tile[r * LDS_STRIDE + l] = v;
+      tile[r * LDS_STRIDE + l] = (lok && (r0 + r) < rows) ? v[it] : 0.0;
     }
   }
   __syncthreads();
@@ -153,15 +161,34 @@ __global__ __launch_bounds__(256) void s1_split_kernel(const double* __restrict_
 // Grid exponent of each row from the partial maxima: E + 1 - beta with
 // E = ceil(log2 max); 0 for a zero row; OZGEMM_EXP_NONFINITE when the row
 // holds Inf or NaN.
-__global__ void s1_grid_kernel(const uint64_t* __restrict__ pmax, int rows_pad, int nchunks, int beta,
-                               int32_t* __restrict__ gout) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= rows_pad) return;
-  uint64_t mx = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    const uint64_t v = pmax[(long)c * rows_pad + row];
-    mx = v > mx ? v : mx;
+__global__ __launch_bounds__(256) void s1_grid_kernel(const uint64_t* __restrict__ pmax, int rows_pad, int nchunks,
+                                                       int beta, int32_t* __restrict__ gout) {
+  // 64 rows per block, four threads per row over every fourth chunk
+  __shared__ uint64_t part[4][64];
+  const int r = threadIdx.x & 63, gi = threadIdx.x >> 6;
+  const int row = blockIdx.x * 64 + r;
+  uint64_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (row < rows_pad) {
+    int c = gi;
+    for (; c + 28 < nchunks; c += 32)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint64_t x = pmax[(long)(c + 4 * u) * rows_pad + row];
+        v[u] = x > v[u] ? x : v[u];
+      }
+    for (; c < nchunks; c += 4) {
+      const uint64_t x = pmax[(long)c * rows_pad + row];
+      v[0] = x > v[0] ? x : v[0];
+    }
   }
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v[0] = v[u] > v[0] ? v[u] : v[0];
+  part[gi][r] = v[0];
+  __syncthreads();
+  if (gi != 0 || row >= rows_pad) return;
+  uint64_t mx = part[0][r];
+#pragma unroll
+  for (int u = 1; u < 4; ++u) mx = part[u][r] > mx ? part[u][r] : mx;
   int gv;
   if (mx >= 0x7ff0000000000000ull) gv = OZGEMM_EXP_NONFINITE;
   else if (mx == 0) gv = 0;
@@ -186,17 +213,28 @@ __global__ __launch_bounds__(256) void s1_accum_kernel(const int32_t* __restrict
   for (int j = blockIdx.y; j < n; j += gridDim.y) {
     const bool bb = gB[j] == OZGEMM_EXP_NONFINITE;
     double c[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int o = 0; o < nout; ++o) {
-      const int4 pl = acc[o];
-      const int4 v = *reinterpret_cast<const int4*>(P + (long)pl.w * plane + (long)j * m_pad + i0);
-      const int4 ea = *reinterpret_cast<const int4*>(gA + (long)pl.x * ma_pad + i0);
-      const int eb = gB[(long)pl.y * nb_pad + j] + pl.z;
-      const int vv[4] = {v.x, v.y, v.z, v.w};
-      const int ee[4] = {ea.x, ea.y, ea.z, ea.w};
+    // four product planes per round: their loads are issued together, the
+    // additions stay in plan order
+    for (int o0 = 0; o0 < nout; o0 += 4) {
+      int4 v[4], ea[4];
+      int eb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = (ba[u] || bb) ? 0 : ee[u] + eb;
-        c[u] = c[u] + __builtin_ldexp((double)vv[u], e);
+      for (int d = 0; d < 4; ++d) {
+        const int4 pl = acc[min(o0 + d, nout - 1)];
+        v[d] = *reinterpret_cast<const int4*>(P + (long)pl.w * plane + (long)j * m_pad + i0);
+        ea[d] = *reinterpret_cast<const int4*>(gA + (long)pl.x * ma_pad + i0);
+        eb[d] = gB[(long)pl.y * nb_pad + j] + pl.z;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        if (o0 + d >= nout) break;  // uniform
+        const int vv[4] = {v[d].x, v[d].y, v[d].z, v[d].w};
+        const int ee[4] = {ea[d].x, ea[d].y, ea[d].z, ea[d].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = (ba[u] || bb) ? 0 : ee[u] + eb[d];
+          c[u] = c[u] + __builtin_ldexp((double)vv[u], e);
+        }
       }
     }
     double* out = C + (long)j * ldc + i0;
@@ -264,7 +302,7 @@ hipError_t launch_s1_rowmax(const double* X, int rows, int q, long rs, long ls, 
 
 hipError_t launch_s1_grid(const uint64_t* pmax, int rows_pad, int nchunks, int beta, int32_t* gout,
                           hipStream_t st) {
-  hipLaunchKernelGGL(s1_grid_kernel, dim3((rows_pad + 255) / 256), dim3(256), 0, st, pmax, rows_pad, nchunks, beta,
+  hipLaunchKernelGGL(s1_grid_kernel, dim3((rows_pad + 63) / 64), dim3(256), 0, st, pmax, rows_pad, nchunks, beta,
                      gout);
   return hipGetLastError();
 }
