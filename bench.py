@@ -14,7 +14,6 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -48,9 +47,11 @@ def parse():
     return p.parse_args()
 
 
-def kernel_hash(name: str) -> str:
-    path = os.path.join(ROOT, "fp64_gemm_emulation_ozii_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def kernel_hash() -> str:
+    """Hash of the int8 GEMM kernel's sources (the same as the one stored
+    with the counter record)."""
+    from fp64_gemm_emulation_ozii_amd.profiling import kernel_sha
+    return kernel_sha()
 
 
 def traffic_record(workload: str):
@@ -63,7 +64,7 @@ def traffic_record(workload: str):
     try:
         rec = json.load(open(path))
         ent = rec.get(workload)
-        if not ent or ent.get("kernel_sha") != kernel_hash("gemm_i8.hip"):
+        if not ent or ent.get("kernel_sha") != kernel_hash():
             return None
         v = ent.get("gemm_hbm_bytes_per_launch")
         return None if v is None else int(v)

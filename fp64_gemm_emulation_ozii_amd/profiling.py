@@ -26,8 +26,16 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def kernel_sha(name: str = "gemm_i8.hip") -> str:
-    return hashlib.sha256(open(os.path.join(PKG, "csrc", name), "rb").read()).hexdigest()[:16]
+# sources that make up the int8 GEMM kernel (a change to any of them
+# invalidates a stored counter record)
+GEMM_SOURCES = ("gemm_i8.hip", "prod_mod.h")
+
+
+def kernel_sha(names=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def short_name(kernel: str) -> str:
