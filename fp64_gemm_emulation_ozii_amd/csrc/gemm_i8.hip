@@ -255,14 +255,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
   const long plane = (long)m_pad * n_pad;
   const double md = (double)mt, inv = 1.0 / md;  // correctly rounded
+  constexpr bool STAGED = WRITE_RT && !WRITE_CT && !ACC_RT;
+  // Staged residue output: the words are first placed in LDS as the
+  // tile's columns (BM bytes each, stride CS), then each wavefront writes
+  // whole column segments with 16-byte stores, four columns per
+  // instruction.  A direct store from the MFMA layout writes 32 scattered
+  // 8-byte pieces per instruction.
+  constexpr int CS = BM + 16;  // 16-byte aligned; consecutive columns start 4 banks apart
+  static_assert(!STAGED || (BN * CS <= 2 * (BM + BN) * BK && BM % 256 == 0 && BN % (4 * NW) == 0),
+                "staging buffer fits the operand buffers");
+  uint8_t* stage = reinterpret_cast<uint8_t*>(smem);
+  if (STAGED) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's last LDS reads are done
+    __builtin_amdgcn_s_barrier();        // and every other wave's
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+      const int lcol = wn * WTN + j * 32 + (lane & 31);
+      const int col = n0 + lcol;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int row = m0 + wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
+        const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
+        const int row = m0 + lrow4;
         const long off = (long)out_t * plane + (long)col * m_pad + row;
         const v16i& v = acc[i][j];
         if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
@@ -280,11 +296,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
             r2 = r2 >= (uint32_t)mt ? r2 - mt : r2;
             r3 = r3 >= (uint32_t)mt ? r3 - mt : r3;
           }
-          *reinterpret_cast<uint32_t*>(rt + off) = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+          const uint32_t word = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+          if (STAGED)
+            *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = word;
+          else
+            *reinterpret_cast<uint32_t*>(rt + off) = word;
         }
       }
       // keep the scheduler from hoisting every accumulator out of AGPRs at once
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (STAGED) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    // wavefront w writes tile columns [w BN/NW, (w+1) BN/NW): 16 lanes per
+    // column, 16 bytes each
+    constexpr int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16;
+    static_assert(!STAGED || 64 % LANES_PER_COL == 0, "whole columns per store");
+    constexpr int COLS_PER_STORE = 64 / LANES_PER_COL;
+#pragma unroll
+    for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it) {
+      const int lcol = wave * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
+      const int rch = (lane % LANES_PER_COL) * 16;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + lcol * CS + rch);
+      *reinterpret_cast<uint4*>(rt + (long)out_t * plane + (long)(n0 + lcol) * m_pad + m0 + rch) = v;
     }
   }
 }
