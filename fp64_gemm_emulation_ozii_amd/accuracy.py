@@ -16,7 +16,8 @@ prints one JSON object per (method, s or k, phi) with the correct bits of the
 emulation and of the native FP64 dot products on the same entries, and the
 time of each phase in milliseconds (Scheme II: scale, residue, GEMM, CRT;
 Scheme I: split, products, accumulation).  ``--methods ozaki2,scheme1-rn,
-scheme1-hybrid --k 4,5,6,7,8`` compares the two schemes on the same inputs.
+scheme1-hybrid --k 4,5,6,7,8`` compares the two schemes on the same inputs;
+``ozaki2-fast`` is Scheme II under the OS II-fast bit budget (§9).
 """
 from __future__ import annotations
 
@@ -82,8 +83,8 @@ def _runs(s_list, k_list, methods):
     """(method, parameter) pairs: Scheme II over s, Scheme I variants over k."""
     out = []
     for meth in methods:
-        if meth == "ozaki2":
-            out += [("ozaki2", s) for s in s_list]
+        if meth in ("ozaki2", "ozaki2-fast"):
+            out += [(meth, s) for s in s_list]
         elif meth in ("scheme1-rn", "scheme1-hybrid"):
             out += [(meth, k) for k in k_list]
         else:
@@ -110,15 +111,16 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats, k_list=(), meth
         Cd = torch.empty((n, m), dtype=torch.float64, device=dev)
         native = (torch.from_numpy(A[rows, :]).to(dev) * torch.from_numpy(B[:, cols].T.copy()).to(dev)).sum(1)
         native_bits = correct_bits(native.cpu().numpy(), A, B, rows, cols)
-        s_max = max([p for meth, p in runs if meth == "ozaki2"] or [1])
+        s_max = max([p for meth, p in runs if meth.startswith("ozaki2")] or [1])
         need1 = max([L.ozgemm_scheme1_workspace_bytes(m, n, q, p, L.OZGEMM_S1_RN if meth == "scheme1-rn"
                                                        else L.OZGEMM_S1_HYBRID)
-                     for meth, p in runs if meth != "ozaki2"] or [0])
+                     for meth, p in runs if not meth.startswith("ozaki2")] or [0])
         ws = torch.empty(max(L.ozgemm_workspace_bytes(m, n, q, s_max), need1), dtype=torch.uint8, device=dev)
         L.ozgemm_config(s_max, m, n, q, stream=torch.cuda.current_stream(), workspace=ws)
 
         def call(meth, p):
-            if meth == "ozaki2":
+            if meth.startswith("ozaki2"):
+                L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if meth == "ozaki2-fast" else L.OZGEMM_BOUND_CONSERVATIVE)
                 L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, p)
             else:
                 v = L.OZGEMM_S1_RN if meth == "scheme1-rn" else L.OZGEMM_S1_HYBRID
@@ -136,7 +138,7 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats, k_list=(), meth
             per = [x / max(calls, 1) for x in phase_ms]
             Cs = Cd.T[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)].cpu().numpy()
             rec = {"method": meth, "m": m, "n": n, "q": q, "phi": phi}
-            if meth == "ozaki2":
+            if meth.startswith("ozaki2"):
                 rec.update({"s": p, "k": L.ozgemm_kbits(p, q), "int8_gemms": p})
                 names = ("scale", "residue", "gemm", "crt")
             else:
@@ -154,6 +156,7 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats, k_list=(), meth
             })
             print(json.dumps(rec), flush=True)
             results.append(rec)
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
         L.ozgemm_free()
         del Ad, Bd, Cd, ws
         torch.cuda.empty_cache()
@@ -172,7 +175,7 @@ def main(argv=None):
     p.add_argument("--repeats", type=int, default=5)
     p.add_argument("--k", type=str, default="4,5,6,7,8", help="Scheme I slice counts")
     p.add_argument("--methods", type=str, default="ozaki2",
-                   help="comma list of ozaki2, scheme1-rn, scheme1-hybrid")
+                   help="comma list of ozaki2, ozaki2-fast, scheme1-rn, scheme1-hybrid")
     p.add_argument("--out", type=str, default="")
     a = p.parse_args(argv)
     res = run_sweep(a.m, a.n, a.q, _parse_list(a.s, int), _parse_list(a.phi, float), a.entries, a.seed, a.repeats,
