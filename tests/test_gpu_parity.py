@@ -66,7 +66,9 @@ def test_ragged_shapes(shape, s):
         pytest.skip("no bits left")
     A, B = hpl_like(m, q, n, 1.0, seed=m + q + n)
     log(f"ragged m={m} q={q} n={n} s={s}")
-    check_all_stages(A, B, s, run_stages(A, B, s))
+    # without int32 planes the GEMM takes its residue-only epilogue (staged
+    # through LDS); with them, the direct one
+    check_all_stages(A, B, s, run_stages(A, B, s, want_ct=(s == 14)))
 
 
 @pytest.mark.parametrize("s,q", [(16, 64), (18, 64), (18, 1000), (20, 3), (20, 200)])
