@@ -47,28 +47,6 @@ __host__ __device__ __forceinline__ int swz(int row) {
   return ((row >> 1) ^ (row << 2)) & 7;  // always < 8: stays inside the row
 }
 
-// Map the linear block id to (modulus, tile row, tile column).
-//
-// Blocks go to the 8 XCDs round-robin (block b runs on XCD b mod 8) and each
-// XCD has its own L2.  The moduli planes are walked one at a time, so all
-// XCDs work on the same plane and its operands stay in the shared
-// last-level cache; inside a plane each XCD takes a contiguous eighth of the
-// tiles, walked in groups of GROUP_M tile rows, so the blocks running on one
-// XCD at a time share A row panels and B column panels in its L2.
-template <int GROUP_M>
-__host__ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int& t, int& mi, int& nj) {
-  const int per_plane = tiles_m * tiles_n;
-  t = b / per_plane;
-  const int w = b % per_plane;
-  const int tile = (per_plane % 8 == 0) ? (w % 8) * (per_plane / 8) + w / 8 : w;
-  const int group = tile / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = tile % (GROUP_M * tiles_n);
-  mi = first_m + in_group % gm;
-  nj = in_group / gm;
-}
-
 // s_waitcnt with only the vector-memory counter constrained to <= N.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -98,10 +76,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 //    the MFMA stream, and the last of them still has two steps to land.
 //    (Measured at 8192^3 x 14 planes: 7.1 ms with the loads issued as one
 //    burst per slice, 6.3 ms with this order.)
-// Inner dimension q >= 2^17 (Ozaki II notes §6, block products): one launch
-// per K block of at most KBLOCK_K entries, each exact in int32
-// (|.| <= 2^16 2^14 < 2^31); with ACC_RT the epilogue adds the block's
-// residue to the residue already in rt, mod m_t.
+// K parts (gemm_grid.h): plane index p s + t of a residue-only launch is
+// part p of modulus t, covering K slices [k_begin + p k_slices, + k_slices)
+// clipped to q_pad; it writes its residue to plane p s + t of rt.  With one
+// part the plane index is the modulus.
+// Inner dimension q >= 2^17 whose parts do not fit (Ozaki II notes §6, block
+// products): one launch per K block of at most KBLOCK_K entries, each exact
+// in int32 (|.| <= 2^16 2^14 < 2^31); with ACC_RT the epilogue adds the
+// block's residue to the residue already in rt, mod m_t.
 constexpr int KBLOCK_K = 1 << 16;
 
 template <int BM, int BN, int BK, int WM, int WN, bool WRITE_CT, bool WRITE_RT, bool MULTI, bool ACC_RT = false>
@@ -128,13 +110,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
+  const int tiles = (m_pad / BM) * (n_pad / BN);
   int t, mi, nj;
-  tile_of_block<4>(blockIdx.x, m_pad / BM, n_pad / BN, t, mi, nj);
+  tile_of_block<4>(blockIdx.x, gridDim.x / tiles, m_pad / BM, n_pad / BN, t, mi, nj);
   const int m0 = mi * BM, n0 = nj * BN;
 
   // operand planes: (t, t) once, or (a0 + u, b0 - u) for u < count
   const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad;
-  int a0 = t, b0 = t, count = 1, out_t = t;
+  int out_t = t;  // output plane
+  int part = 0;
+  if (!MULTI) {
+    part = t / c.s;  // K part of modulus t
+    t -= part * c.s;
+  }
+  int a0 = t, b0 = t, count = 1;
   if (MULTI) {
     const int4 pl = plan[t];
     a0 = pl.x;
@@ -153,15 +142,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   const int lane_src1 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb + ROWS_PER_KB)) * 16);
   const long kb_stride = (long)ROWS_PER_KB * q_pad;  // source distance of consecutive 1 KB loads
 
-  const int nk = q_pad / BK;                      // K slices per product
-  const int nkt = MULTI ? nk * count : k_slices;  // K slices walked by this block
+  const int nk = q_pad / BK;                   // K slices per product
+  const int kfirst = k_begin + part * k_slices;  // first K slice of this block
+  const int nkt = MULTI ? nk * count : min(k_slices, nk - kfirst);  // K slices walked
   // load li (A blocks first, then B) of walked slice kk into buffer kk mod 2
   auto load1 = [&](int kk, int li) {
     int8_t* As = smem + (kk & 1) * (BM + BN) * BK;
     int8_t* Bs = As + BM * BK;
     const int8_t* ga = Ag;
     const int8_t* gb = Bg;
-    int k0 = (k_begin + kk) * BK;
+    int k0 = (kfirst + kk) * BK;
     if (MULTI) {
       const int u = kk / nk;
       k0 = (kk - u * nk) * BK;
@@ -325,15 +315,79 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   }
 }
 
+// Sum of the K parts' residues (gemm_grid.h): dst plane t = (sum over p < P
+// of src plane p s + t) mod m_t, 16 bytes per thread.  The bytes of a word are
+// summed in two 16-bit lanes each (even and odd bytes; P <= 64 keeps a sum
+// below 2^16).  dst may be src: plane t of part 0 is read by the same thread
+// before it is written, and no other thread touches it.
+__global__ __launch_bounds__(256) void rt_parts_reduce_kernel(const uint8_t* __restrict__ src, uint8_t* dst,
+                                                             long plane, int P, GemmConsts c) {
+  const long chunks = plane / 16;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= chunks * c.s) return;
+  const int t = (int)(gid / chunks);
+  const long off = (gid - (long)t * chunks) * 16;
+  int mt = c.m[0];
+#pragma unroll
+  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+  const double md = (double)mt, inv = 1.0 / md;
+  uint32_t ev[4] = {0, 0, 0, 0}, od[4] = {0, 0, 0, 0};
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // all loads first; a clamped index past P is loaded but not added
+      const int p = min(p0 + i, P - 1);
+      v[i] = *reinterpret_cast<const uint4*>(src + ((long)p * c.s + t) * plane + off);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (p0 + i < P) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ev[k] += w[k] & 0x00ff00ffu;
+          od[k] += (w[k] >> 8) & 0x00ff00ffu;
+        }
+      }
+    }
+  }
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t r0 = mod_product((int32_t)(ev[k] & 0xffffu), md, inv);
+    const uint32_t r2 = mod_product((int32_t)(ev[k] >> 16), md, inv);
+    const uint32_t r1 = mod_product((int32_t)(od[k] & 0xffffu), md, inv);
+    const uint32_t r3 = mod_product((int32_t)(od[k] >> 16), md, inv);
+    out[k] = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+  }
+  *reinterpret_cast<uint4*>(dst + (long)t * plane + off) = uint4{out[0], out[1], out[2], out[3]};
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad, const GemmConsts& c,
-                       int32_t* Ct, uint8_t* rt, hipStream_t st) {
+                       int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts, hipStream_t st) {
   constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
+  static_assert(BK == SPLIT_K_SLICE, "K parts are counted in kernel slices");
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
-  const int nblocks = (n_pad / BN) * (m_pad / BM) * c.s;
+  const int tiles = (n_pad / BN) * (m_pad / BM);
+  const int nblocks = tiles * c.s;
   const dim3 grid(nblocks), block(WM * WN * 64);
   const int nk = q_pad / BK;
+  if (Ct == nullptr && rt != nullptr && split.parts > 1) {
+    // K parts into the part planes, then their sum mod m_t into rt
+    const int P = split.parts, per = split.slices;
+    if (parts == nullptr || P > SPLIT_MAX || per < 1 || (long)(P - 1) * per >= nk || (long)P * per < nk ||
+        (q_pad >= OZGEMM_Q_LIMIT && per > KBLOCK_K / BK))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false>), dim3(nblocks * P), block, 0,
+                       st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, parts, nullptr, 0, per);
+    const long plane = (long)m_pad * n_pad;
+    const long threads = plane / 16 * c.s;
+    hipLaunchKernelGGL(rt_parts_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, parts, rt,
+                       plane, P, c);
+    return hipGetLastError();
+  }
   if (q_pad >= OZGEMM_Q_LIMIT && Ct == nullptr && rt != nullptr) {
     // block products; int32 C_t planes are only asked for while q < 2^17,
     // where one launch is exact (the padding is zero)

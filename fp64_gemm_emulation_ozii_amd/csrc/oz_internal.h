@@ -7,6 +7,7 @@
 
 #include "../../include/ozgemm.h"
 #include "crt_reconstruct.h"
+#include "gemm_grid.h"
 
 namespace oz {
 
@@ -70,8 +71,13 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad,
                           double* prime, long prime_rs, long prime_ls, hipStream_t st);
 
+// Scheme II products C_t = A_t B_t^T: int32 planes Ct and/or residues mod m_t
+// in rt.  With split.parts > 1 (residue-only) the K parts write the planes
+// `parts` (split.parts * s planes of m_pad * n_pad bytes; may be rt itself)
+// and are summed into rt; see gemm_grid.h.
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad,
-                       const GemmConsts& c, int32_t* Ct, uint8_t* rt, hipStream_t st);
+                       const GemmConsts& c, int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts,
+                       hipStream_t st);
 
 // Scheme I slice products: output plane plan[o].w (m_pad x n_pad int32, [j][i])
 // = sum over u < plan[o].z of A_{plan[o].x + u} B_{plan[o].y - u}^T.

@@ -232,7 +232,7 @@ void crt_weights(int s, double* out) {
 constexpr int NCH_MAX = 256;  // partial row-max chunks of A
 
 struct Layout {
-  size_t consts, pmax, e, f, ares, bres, rt, total;
+  size_t consts, pmax, e, f, ares, bres, rt, rt_bytes, total;
 };
 
 Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
@@ -252,7 +252,10 @@ Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
   L.f = take(np * 4);
   L.ares = take((size_t)s_max * mp * qp);
   L.bres = take((size_t)s_max * np * qp);
-  L.rt = take((size_t)s_max * mp * np);
+  // product residues; also the K part planes of skinny products (gemm_grid.h)
+  L.rt_bytes = std::max((size_t)s_max * mp * np,
+                        (size_t)split_region_bytes((int)(qp / K_PAD), ROW_PAD * ROW_PAD));
+  L.rt = take(L.rt_bytes);
   L.total = off;
   return L;
 }
@@ -287,6 +290,33 @@ int hip_fail(hipError_t err) {
     const hipError_t oz_err_ = (expr);             \
     if (oz_err_ != hipSuccess) return hip_fail(oz_err_); \
   } while (0)
+
+// Compute units of the current device (queried once per device).
+int device_cus(int* cus) {
+  constexpr int MAX_DEVICES = 64;
+  static int cached[MAX_DEVICES] = {};
+  int dev = 0;
+  OZ_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return hip_fail(hipErrorInvalidDevice);
+  if (cached[dev] == 0) {
+    int v = 0;
+    OZ_CHECK(hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev));
+    cached[dev] = std::max(v, 1);
+  }
+  *cus = cached[dev];
+  return 0;
+}
+
+// K parts of a residue-only Scheme II product of padded size mp x np x qp
+// (gemm_grid.h); their planes go to the workspace's product region.
+int product_split(int mp, int np, int qp, int s, SplitChoice* out) {
+  int cus = 0;
+  const int st = device_cus(&cus);
+  if (st) return st;
+  const long cap = (long)(g.lay.rt_bytes / ((size_t)mp * np));
+  *out = choose_splits((mp / ROW_PAD) * (np / ROW_PAD), s, qp / K_PAD, cus, cap);
+  return 0;
+}
 
 // The CRT weight table lives in the workspace; it is copied there once after
 // each configuration, at the first call that needs it (a blocking 16 KB copy).
@@ -604,7 +634,9 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, g.stream));
   OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
   if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
-  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, g.stream));
+  SplitChoice split{};
+  if ((st = product_split(mp, np, qp, s, &split))) return st;
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, split, rt, g.stream));
   if (timed) OZ_CHECK(hipEventRecord(ev[3], g.stream));
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
   if (timed) {
@@ -690,8 +722,28 @@ int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8
   GemmConsts gc;
   CrtConsts cc;
   make_consts(s, q, g.bound, &rc, &gc, &cc);
-  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, g.stream));
+  SplitChoice split{1, qp / K_PAD};
+  if (Ct == nullptr && rt != nullptr && (st = product_split(mp, np, qp, s, &split))) return st;
+  uint8_t* parts = reinterpret_cast<uint8_t*>(g.ws + g.lay.rt);
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, split, parts, g.stream));
   return 0;
+}
+
+int ozgemm_gemm_parts(int m, int n, int q, int s, int* parts) {
+  if (m < 1) return -1;
+  if (n < 1) return -2;
+  if (q < 1) return -3;
+  if (s < 1 || s > OZGEMM_S_MAX) return -4;
+  if (parts == nullptr) return -5;
+  if (!g.configured) return OZGEMM_NOT_CONFIGURED;
+  if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  SplitChoice split{};
+  const int st = product_split(mp, np, qp, s, &split);
+  if (st) return st;
+  *parts = split.parts;
+  return OZGEMM_OK;
 }
 
 int ozgemm_stage_crt(int m, int n, int q, int s, const uint8_t* rt, const int32_t* e, const int32_t* f, double* C,

@@ -39,7 +39,7 @@ EXPORTS = (
     "ozgemm_stage_residue", "ozgemm_stage_gemm", "ozgemm_stage_crt", "ozgemm_timing", "ozgemm_phase_ms",
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
-    "ozgemm_set_bound", "ozgemm_bound_budget",
+    "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts",
 )
 
 _lib = None
@@ -78,6 +78,7 @@ def lib():
         "ozgemm_stage_residue": (c_int, [c_int, c_int, c_int, c_int, vp, c_int, vp, c_int, vp, vp, vp, vp, vp, vp]),
         "ozgemm_stage_gemm": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp]),
         "ozgemm_stage_crt": (c_int, [c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_int]),
+        "ozgemm_gemm_parts": (c_int, [c_int, c_int, c_int, c_int, ip]),
         "ozgemm_timing": (c_int, [c_int]),
         "ozgemm_phase_ms": (c_int, [ctypes.POINTER(ctypes.c_double), ip]),
         "ozgemm_scheme1_beta": (c_int, [c_int]),
@@ -217,6 +218,13 @@ def ozgemm_stage_gemm(m, n, q, s, Ares, Bres, Ct=None, rt=None, check: bool = Tr
 def ozgemm_stage_crt(m, n, q, s, rt, e, f, C, ldc, check: bool = True) -> int:
     st = lib().ozgemm_stage_crt(m, n, q, s, _ptr(rt), _ptr(e), _ptr(f), _ptr(C), ldc)
     return _check(st, "ozgemm_stage_crt") if check else st
+
+
+def ozgemm_gemm_parts(m: int, n: int, q: int, s: int) -> int:
+    """K parts of the residue-only product of an m x n x q call (needs a device)."""
+    p = ctypes.c_int()
+    _check(lib().ozgemm_gemm_parts(m, n, q, s, ctypes.byref(p)), "ozgemm_gemm_parts")
+    return p.value
 
 
 def ozgemm_set_bound(mode: int) -> int:

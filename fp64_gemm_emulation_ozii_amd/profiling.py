@@ -28,7 +28,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # sources that make up the int8 GEMM kernel (a change to any of them
 # invalidates a stored counter record)
-GEMM_SOURCES = ("gemm_i8.hip", "prod_mod.h")
+GEMM_SOURCES = ("gemm_i8.hip", "gemm_grid.h", "prod_mod.h")
 
 
 def kernel_sha(names=GEMM_SOURCES) -> str:

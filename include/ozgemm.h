@@ -33,10 +33,10 @@
  *    of the greedy pairwise-coprime sequence 256, 255, 253, 251, 247, 241,
  *    239, 233, 229, 227, 223, 217, 211, 199, 197, 193, 191, 181, 179, 173.
  *  - Every int8 dot product of length < 2^17 (|.| <= q * 2^14) is exact in
- *    int32 (Ozaki II notes §6).  For q >= 2^17 the GEMM splits K into blocks
- *    of 2^16 and folds the int32 accumulators mod m_t between blocks (the
- *    notes' block products), so q may go up to OZGEMM_Q_MAX; s must leave
- *    k >= 1 bits (§5).  Otherwise OZGEMM_RANGE.
+ *    int32 (Ozaki II notes §6).  For q >= 2^17 the GEMM splits K into parts
+ *    of at most 2^16 and adds their products mod m_t (the notes' block
+ *    products; see ozgemm_gemm_parts), so q may go up to OZGEMM_Q_MAX; s
+ *    must leave k >= 1 bits (§5).  Otherwise OZGEMM_RANGE.
  *  - Numerics: the result equals X * 2^(e_i + f_j - 2k) rounded once to
  *    nearest-even, where X = (A'B')_ij exactly.  Rows of A / columns of B that
  *    hold Inf or NaN make the outputs they touch NaN; all-zero rows/columns
@@ -79,8 +79,9 @@ extern "C" {
 
 /* Bytes of device workspace needed for problems up to max_m x max_n x max_q
  * with up to s_max moduli (the per-modulus int8 residue planes of A and B,
- * the uint8 product residues and small per-row/column arrays).  Returns 0
- * for invalid arguments.  Host only. */
+ * the uint8 product residues -- at least 128 MiB of them when max_q >= 3969,
+ * for the K parts of skinny products -- and small per-row/column arrays).
+ * Returns 0 for invalid arguments.  Host only. */
 size_t ozgemm_workspace_bytes(int max_m, int max_n, int max_q, int s_max);
 
 /* Record the maximum problem size, the HIP stream (a hipStream_t, may be
@@ -183,10 +184,27 @@ int ozgemm_stage_residue(int m, int n, int q, int s,
 /* Per-modulus products (Ozaki II notes §4, §6): C_t = A_t B_t^T over q_pad,
  * exact in int32.  Ct (optional, NULL to skip) receives int32 planes,
  * column-major with ld m_pad: Ct[t*m_pad*n_pad + j*m_pad + i].  rt
- * (optional) receives C_t mod m_t in [0, m_t) as uint8 in the same layout. */
+ * (optional) receives C_t mod m_t in [0, m_t) as uint8 in the same layout.
+ * Without Ct, the product may run as K parts (ozgemm_gemm_parts) whose
+ * planes use the workspace's product region; rt must not lie in the
+ * workspace. */
 int ozgemm_stage_gemm(int m, int n, int q, int s,
                       const int8_t *Ares, const int8_t *Bres,
                       int32_t *Ct, uint8_t *rt);
+
+/* Number of K parts the residue-only product of an m x n x q call with s
+ * moduli runs as (ozgemm_dgemm, and ozgemm_stage_gemm without Ct), written
+ * to *parts.  When moduli x output tiles of 256 x 256 leave the compute
+ * units idle, the inner dimension is cut into P parts, one block per (part,
+ * modulus, tile); each part's product mod m_t goes to a plane of the
+ * workspace, and a reduction adds the P residues mod m_t (the sum of the
+ * parts is the whole product; a part of at most 2^16 K entries is exact in
+ * int32, Ozaki II notes §6).  1 = one part; 0 = q >= 2^17 with no room for
+ * parts, walked as sequential K blocks instead.  The choice depends on the
+ * device's compute units (queried on the current device) and on the
+ * configured workspace.  Errors: -1..-5, OZGEMM_NOT_CONFIGURED,
+ * OZGEMM_RANGE, OZGEMM_HIP_ERROR. */
+int ozgemm_gemm_parts(int m, int n, int q, int s, int *parts);
 
 /* CRT reconstruction, range reduction and unscaling (Ozaki II notes §4, §5,
  * §7): from rt (layout of ozgemm_stage_gemm), e and f, write the m x n result

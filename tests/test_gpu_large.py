@@ -28,20 +28,29 @@ def sample_lines(size: int, count: int, seed: int, tile: int = 256):
     return np.array(sorted(picks), dtype=np.int64)
 
 
-@pytest.mark.parametrize("m,q,n,phi", [
-    (4096, 4096, 4096, 1.0),
-    (8192, 8192, 8192, 1.0),
-    (16384, 1024, 16384, 1.0),
-    (1024, 65536, 1024, 1.0),
-    (16384, 16384, 16384, 4.0),
-    (512, 2**20, 512, 1.0),
+# parts: K parts of the product launch on a 256-CU device (1: one part; 0:
+# q >= 2^17 walked as sequential K blocks, whose epilogue adds each block's
+# residues to the earlier ones)
+@pytest.mark.parametrize("m,q,n,phi,parts", [
+    (4096, 4096, 4096, 1.0, 1),
+    (8192, 8192, 8192, 1.0, 1),
+    (16384, 1024, 16384, 1.0, 1),
+    (1024, 65536, 1024, 1.0, 8),
+    (16384, 16384, 16384, 4.0, 1),
+    (512, 2**20, 512, 1.0, None),
+    (1792, 2**17 + 300, 1792, 1.0, 0),
 ])
-def test_sampled_block_and_exponents(m, q, n, phi):
+def test_sampled_block_and_exponents(m, q, n, phi, parts):
     import torch
     s = 14
     log(f"large m={m} q={q} n={n} phi={phi}: generate")
     A, B = hpl_like(m, q, n, phi, seed=0)
     L.ozgemm_config(s, m, n, q)
+    got_parts = L.ozgemm_gemm_parts(m, n, q, s)
+    if parts is None:
+        assert got_parts >= 16  # 2^20 / 2^16 parts at least
+    else:
+        assert got_parts == parts
     Ad = dev_colmajor(A)
     Bd = dev_colmajor(B)
     Cd = torch.empty((n, m), dtype=torch.float64, device="cuda")

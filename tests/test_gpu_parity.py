@@ -177,15 +177,41 @@ def test_1024_cube_full_oracle(s):
 
 @pytest.mark.parametrize("s,q", [(14, 2**17 + 300), (10, 140000), (14, 2**17 - 100)])
 def test_long_inner_dimension(s, q):
-    """q >= 2^17: the GEMM folds its int32 accumulators mod m_t every 2^16 of
-    K (block products); residues of the products and C must still match."""
+    """q >= 2^17: the GEMM cuts K into parts of at most 2^16 (block
+    products), here run as K parts of one launch; residues of the products
+    and C must still match."""
     import torch
     A, B = hpl_like(65, q, 70, 1.0, seed=q % 1000)
     L.ozgemm_free()
     configure(256, 256, q, 20)
     try:
+        assert L.ozgemm_gemm_parts(65, 70, q, s) >= 2
         log(f"long K s={s} q={q}")
         g = run_stages(A, B, s, want_ct=q < 2**17, want_prime=True)
+        C, _ = run_dgemm(A, B, s)
+    finally:
+        L.ozgemm_free()
+        torch.cuda.empty_cache()
+        configure(1536, 1536, 1536, 20)
+    ref = oz.dgemm(A, B, s, stages=True)
+    check_all_stages(A, B, s, g, ref=ref)
+    assert same_doubles(C, ref[0])
+
+
+@pytest.mark.parametrize("m,q,n,s,parts", [(300, 5000, 200, 14, 2), (65, 9000, 70, 8, 4), (257, 4200, 513, 13, 2)])
+def test_k_parts(m, q, n, s, parts):
+    """Skinny outputs with a long inner dimension run as K parts: one block
+    per (part, modulus, tile), each part's product mod m_t in a plane of its
+    own, then the parts summed mod m_t.  With 8 | parts * s a plane's tiles
+    also sit on one XCD.  Every stage must still match the oracle."""
+    import torch
+    A, B = hpl_like(m, q, n, 1.0, seed=m + q + n)
+    L.ozgemm_free()
+    configure(1536, 1536, 9000, 20)
+    try:
+        assert L.ozgemm_gemm_parts(m, n, q, s) == parts
+        log(f"K parts m={m} q={q} n={n} s={s} parts={parts}")
+        g = run_stages(A, B, s, want_ct=False)  # int32 planes would keep one part
         C, _ = run_dgemm(A, B, s)
     finally:
         L.ozgemm_free()
