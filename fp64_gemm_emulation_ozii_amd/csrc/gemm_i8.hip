@@ -86,10 +86,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // block's residue to the residue already in rt, mod m_t.
 constexpr int KBLOCK_K = 1 << 16;
 
-template <int BM, int BN, int BK, int WM, int WN, bool WRITE_CT, bool WRITE_RT, bool MULTI, bool ACC_RT = false>
+template <int BM, int BN, int BK, int WM, int WN, bool WRITE_CT, bool WRITE_RT, bool MULTI, bool ACC_RT = false,
+          bool PERSIST = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
     const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
-    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan, int k_begin, int k_slices) {
+    int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan, int k_begin, int k_slices,
+    int nblocks) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
   constexpr int ROWS_PER_KB = 1024 / BK;        // tile rows filled by one wavefront load
@@ -103,36 +105,69 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
   static_assert(FM * FN == 16 && NF == 8 && NKS >= 2, "slot plan: 16 MFMAs, 8 reads per step");
   static_assert(2 * LPW <= 16 * NKS, "every load has an odd slot in its window");
+  constexpr int HALF_LOADS = LPW < 8 ? LPW : 8;  // loads of a slice issued in the window before it
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * (BM + BN) * BK];
+  // Staged residue output: the words are first placed in LDS as the tile's
+  // columns (BM bytes each, stride CS), then each wavefront writes whole
+  // column segments with 16-byte stores, four columns per instruction.  A
+  // direct store from the MFMA layout writes 32 scattered 8-byte pieces per
+  // instruction.  The staging area is the operand buffers (free after the K
+  // loop), or, in the persistent form, buffer 1 and what follows it, so that
+  // the next tile's first slice can land in buffer 0 meanwhile.
+  constexpr bool STAGED = WRITE_RT && !WRITE_CT && !ACC_RT;
+  static_assert(!PERSIST || (STAGED && !MULTI), "persistent form: residue-only products");
+  constexpr int CS = BM + 16;  // 16-byte aligned; consecutive columns start 4 banks apart
+  constexpr int OPERANDS = 2 * (BM + BN) * BK;
+  constexpr int STAGE_OFF = PERSIST ? (BM + BN) * BK : 0;
+  constexpr int SMEM = STAGED && STAGE_OFF + BN * CS > OPERANDS ? STAGE_OFF + BN * CS : OPERANDS;
+  static_assert(!STAGED || (BM % 256 == 0 && BN % (4 * NW) == 0), "whole column segments per store");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int tiles = (m_pad / BM) * (n_pad / BN);
-  int t, mi, nj;
-  tile_of_block<4>(blockIdx.x, gridDim.x / tiles, m_pad / BM, n_pad / BN, t, mi, nj);
-  const int m0 = mi * BM, n0 = nj * BN;
-
-  // operand planes: (t, t) once, or (a0 + u, b0 - u) for u < count
+  const int tiles_m = m_pad / BM, tiles_n = n_pad / BN;
+  const int nplanes = nblocks / (tiles_m * tiles_n);
   const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad;
-  int out_t = t;  // output plane
-  int part = 0;
-  if (!MULTI) {
-    part = t / c.s;  // K part of modulus t
-    t -= part * c.s;
-  }
-  int a0 = t, b0 = t, count = 1;
-  if (MULTI) {
-    const int4 pl = plan[t];
-    a0 = pl.x;
-    b0 = pl.y;
-    count = pl.z;
-    out_t = pl.w;
-  }
-  const int8_t* Ag = Ares + (long)a0 * a_plane + (long)m0 * q_pad;
-  const int8_t* Bg = Bres + (long)b0 * b_plane + (long)n0 * q_pad;
+  const int nk = q_pad / BK;  // K slices per product
+
+  // The tile of linear block id L (one per block, or L = blockIdx.x +
+  // r gridDim.x, r = 0, 1, ... in the persistent form -- the same XCD as in
+  // a grid of nblocks blocks): its modulus or plan entry t, output corner,
+  // output plane, operand panels and K slices.  Operand planes: (t, t) once,
+  // or (a0 + u, b0 - u) for u < count.
+  int t, m0, n0, out_t, kfirst, nkt;
+  const int8_t* Ag;
+  const int8_t* Bg;
+  auto set_tile = [&](int L) {
+    int tt, mi, nj;
+    tile_of_block<4>(L, nplanes, tiles_m, tiles_n, tt, mi, nj);
+    m0 = mi * BM;
+    n0 = nj * BN;
+    out_t = tt;  // output plane
+    int part = 0;
+    if (!MULTI) {
+      part = tt / c.s;  // K part of modulus tt
+      tt -= part * c.s;
+    }
+    int a0 = tt, b0 = tt, count = 1;
+    if (MULTI) {
+      const int4 pl = plan[tt];
+      a0 = pl.x;
+      b0 = pl.y;
+      count = pl.z;
+      out_t = pl.w;
+    }
+    t = tt;
+    Ag = Ares + (long)a0 * a_plane + (long)m0 * q_pad;
+    Bg = Bres + (long)b0 * b_plane + (long)n0 * q_pad;
+    kfirst = k_begin + part * k_slices;                          // first K slice of this block
+    nkt = MULTI ? nk * count : min(k_slices, nk - kfirst);       // K slices walked
+  };
+  int L = blockIdx.x;
+  set_tile(L);
 
   // A wavefront load fills 1 KB of LDS = ROWS_PER_KB whole tile rows, lane l
   // landing in row l / CPR, physical chunk l mod CPR.  The swizzle depends on
@@ -142,9 +177,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   const int lane_src1 = lrow_in_kb * q_pad + (((lane % CPR) ^ swz<BK>(lrow_in_kb + ROWS_PER_KB)) * 16);
   const long kb_stride = (long)ROWS_PER_KB * q_pad;  // source distance of consecutive 1 KB loads
 
-  const int nk = q_pad / BK;                   // K slices per product
-  const int kfirst = k_begin + part * k_slices;  // first K slice of this block
-  const int nkt = MULTI ? nk * count : min(k_slices, nk - kfirst);  // K slices walked
   // load li (A blocks first, then B) of walked slice kk into buffer kk mod 2
   auto load1 = [&](int kk, int li) {
     int8_t* As = smem + (kk & 1) * (BM + BN) * BK;
@@ -197,121 +229,146 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   // that precedes slice 0.
 #pragma unroll
   for (int li = 0; li < LPW; ++li) load1(0, li);
-  if (nkt > 1)
+  if (nkt > 1) {
 #pragma unroll
     for (int li = 0; li < LPW; ++li)
       if (2 * li + 1 < 16) load1(1, li);
-  wait_vmcnt<0>();
+    wait_vmcnt<HALF_LOADS>();  // slice 0 (loads return in order)
+  } else {
+    wait_vmcnt<0>();
+  }
   __builtin_amdgcn_s_barrier();
 
-  v4i cur[NF], nxt[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) cur[f] = read1(0, 0, f);
-
-  for (int kt = 0; kt < nkt; ++kt) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bool last = ks == NKS - 1;
-      const int lslice = last ? kt + 2 : kt + 1;  // slice fetched in this step's window
-      if (last) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slice kt are done
-        wait_vmcnt<0>();                     // this wave's loads of slice kt + 1 have landed
-        __builtin_amdgcn_s_barrier();
-      }
-      const int rbuf = last ? (kt + 1) & 1 : kt & 1;  // (past the end: read, unused)
-      const int rks = last ? 0 : ks + 1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = r / FN, j = r % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
-        if ((r & 1) == 0) nxt[r / 2] = read1(rbuf, rks, r / 2);
-        const int slot = last ? r : 16 + ks * 16 + r;
-#pragma unroll
-        for (int li = 0; li < LPW; ++li)
-          if (2 * li + 1 == slot && lslice < nkt) load1(lslice, li);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
-    }
-  }
-  wait_vmcnt<0>();  // no load into LDS may outlive the block
-
-  // ---- epilogue: int32 planes and/or residues mod m_t ----
-  // this plane's modulus, selected without indexing the by-value argument
-  // dynamically (which would copy it to scratch)
-  int mt = c.m[0];
-#pragma unroll
-  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
   const long plane = (long)m_pad * n_pad;
-  const double md = (double)mt, inv = 1.0 / md;  // correctly rounded
-  constexpr bool STAGED = WRITE_RT && !WRITE_CT && !ACC_RT;
-  // Staged residue output: the words are first placed in LDS as the
-  // tile's columns (BM bytes each, stride CS), then each wavefront writes
-  // whole column segments with 16-byte stores, four columns per
-  // instruction.  A direct store from the MFMA layout writes 32 scattered
-  // 8-byte pieces per instruction.
-  constexpr int CS = BM + 16;  // 16-byte aligned; consecutive columns start 4 banks apart
-  static_assert(!STAGED || (BN * CS <= 2 * (BM + BN) * BK && BM % 256 == 0 && BN % (4 * NW) == 0),
-                "staging buffer fits the operand buffers");
-  uint8_t* stage = reinterpret_cast<uint8_t*>(smem);
-  if (STAGED) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's last LDS reads are done
-    __builtin_amdgcn_s_barrier();        // and every other wave's
-  }
+  uint8_t* stage = reinterpret_cast<uint8_t*>(smem + STAGE_OFF);
+  while (true) {
+    v4i cur[NF], nxt[NF];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int f = 0; f < NF; ++f) cur[f] = read1(0, 0, f);
+
+    for (int kt = 0; kt < nkt; ++kt) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int lcol = wn * WTN + j * 32 + (lane & 31);
-      const int col = n0 + lcol;
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bool last = ks == NKS - 1;
+        const int lslice = last ? kt + 2 : kt + 1;  // slice fetched in this step's window
+        if (last) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slice kt are done
+          wait_vmcnt<0>();                     // this wave's loads of slice kt + 1 have landed
+          __builtin_amdgcn_s_barrier();
+        }
+        const int rbuf = last ? (kt + 1) & 1 : kt & 1;  // (past the end: read, unused)
+        const int rks = last ? 0 : ks + 1;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
-        const int row = m0 + lrow4;
-        const long off = (long)out_t * plane + (long)col * m_pad + row;
-        const v16i& v = acc[i][j];
-        if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-        if (WRITE_RT) {
-          uint32_t r0 = mod_product(v[4 * g], md, inv), r1 = mod_product(v[4 * g + 1], md, inv);
-          uint32_t r2 = mod_product(v[4 * g + 2], md, inv), r3 = mod_product(v[4 * g + 3], md, inv);
-          if (ACC_RT) {  // add the residues of the earlier K blocks, mod m_t
-            const uint32_t old = *reinterpret_cast<const uint32_t*>(rt + off);
-            r0 += old & 0xffu;
-            r1 += (old >> 8) & 0xffu;
-            r2 += (old >> 16) & 0xffu;
-            r3 += old >> 24;
-            r0 = r0 >= (uint32_t)mt ? r0 - mt : r0;
-            r1 = r1 >= (uint32_t)mt ? r1 - mt : r1;
-            r2 = r2 >= (uint32_t)mt ? r2 - mt : r2;
-            r3 = r3 >= (uint32_t)mt ? r3 - mt : r3;
-          }
-          const uint32_t word = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
-          if (STAGED)
-            *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = word;
-          else
-            *reinterpret_cast<uint32_t*>(rt + off) = word;
+        for (int r = 0; r < 16; ++r) {
+          const int i = r / FN, j = r % FN;
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+          if ((r & 1) == 0) nxt[r / 2] = read1(rbuf, rks, r / 2);
+          const int slot = last ? r : 16 + ks * 16 + r;
+#pragma unroll
+          for (int li = 0; li < LPW; ++li)
+            if (2 * li + 1 == slot && lslice < nkt) load1(lslice, li);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
+      }
+    }
+    wait_vmcnt<0>();  // no load into LDS may outlive the block
+
+    // ---- epilogue: int32 planes and/or residues mod m_t ----
+    // this plane's modulus, selected without indexing the by-value argument
+    // dynamically (which would copy it to scratch)
+    int mt = c.m[0];
+#pragma unroll
+    for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+    const double md = (double)mt, inv = 1.0 / md;  // correctly rounded
+    const int em0 = m0, en0 = n0, eout = out_t;    // the finished tile
+    bool more = false;
+    if (STAGED) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's last LDS reads are done
+      __builtin_amdgcn_s_barrier();        // and every other wave's
+      if (PERSIST) {
+        // the next tile's first slice lands in buffer 0 while this one's
+        // residues are reduced and written
+        more = L + (int)gridDim.x < nblocks;
+        if (more) {
+          L += gridDim.x;
+          set_tile(L);
+#pragma unroll
+          for (int li = 0; li < LPW; ++li) load1(0, li);
         }
       }
-      // keep the scheduler from hoisting every accumulator out of AGPRs at once
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  if (STAGED) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int lcol = wn * WTN + j * 32 + (lane & 31);
+        const int col = en0 + lcol;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int row = em0 + lrow4;
+          const long off = (long)eout * plane + (long)col * m_pad + row;
+          const v16i& v = acc[i][j];
+          if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+          if (WRITE_RT) {
+            uint32_t r0 = mod_product(v[4 * g], md, inv), r1 = mod_product(v[4 * g + 1], md, inv);
+            uint32_t r2 = mod_product(v[4 * g + 2], md, inv), r3 = mod_product(v[4 * g + 3], md, inv);
+            if (ACC_RT) {  // add the residues of the earlier K blocks, mod m_t
+              const uint32_t old = *reinterpret_cast<const uint32_t*>(rt + off);
+              r0 += old & 0xffu;
+              r1 += (old >> 8) & 0xffu;
+              r2 += (old >> 16) & 0xffu;
+              r3 += old >> 24;
+              r0 = r0 >= (uint32_t)mt ? r0 - mt : r0;
+              r1 = r1 >= (uint32_t)mt ? r1 - mt : r1;
+              r2 = r2 >= (uint32_t)mt ? r2 - mt : r2;
+              r3 = r3 >= (uint32_t)mt ? r3 - mt : r3;
+            }
+            const uint32_t word = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+            if (STAGED)
+              *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = word;
+            else
+              *reinterpret_cast<uint32_t*>(rt + off) = word;
+          }
+        }
+        // keep the scheduler from hoisting every accumulator out of AGPRs at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (STAGED) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      // wavefront w writes tile columns [w BN/NW, (w+1) BN/NW): 16 lanes per
+      // column, 16 bytes each
+      constexpr int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16;
+      static_assert(!STAGED || 64 % LANES_PER_COL == 0, "whole columns per store");
+      constexpr int COLS_PER_STORE = 64 / LANES_PER_COL;
+#pragma unroll
+      for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it) {
+        const int lcol = wave * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
+        const int rch = (lane % LANES_PER_COL) * 16;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + lcol * CS + rch);
+        *reinterpret_cast<uint4*>(rt + (long)eout * plane + (long)(en0 + lcol) * m_pad + em0 + rch) = v;
+      }
+    }
+    if (!PERSIST || !more) break;
+
+    // next tile: every wave has read its staged columns out of buffer 1
+    // before the first half of slice 1 is loaded there
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
-    // wavefront w writes tile columns [w BN/NW, (w+1) BN/NW): 16 lanes per
-    // column, 16 bytes each
-    constexpr int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16;
-    static_assert(!STAGED || 64 % LANES_PER_COL == 0, "whole columns per store");
-    constexpr int COLS_PER_STORE = 64 / LANES_PER_COL;
+    if (nkt > 1)
 #pragma unroll
-    for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it) {
-      const int lcol = wave * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
-      const int rch = (lane % LANES_PER_COL) * 16;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + lcol * CS + rch);
-      *reinterpret_cast<uint4*>(rt + (long)out_t * plane + (long)(n0 + lcol) * m_pad + m0 + rch) = v;
-    }
+      for (int li = 0; li < LPW; ++li)
+        if (2 * li + 1 < 16) load1(1, li);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+    wait_vmcnt<0>();  // slice 0, the half of slice 1 and this tile's stores
+    __builtin_amdgcn_s_barrier();
   }
 }
 
@@ -366,7 +423,8 @@ __global__ __launch_bounds__(256) void rt_parts_reduce_kernel(const uint8_t* __r
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad, const GemmConsts& c,
-                       int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts, hipStream_t st) {
+                       int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts, int cus,
+                       hipStream_t st) {
   constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
   static_assert(BK == SPLIT_K_SLICE, "K parts are counted in kernel slices");
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
@@ -374,14 +432,23 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   const int nblocks = tiles * c.s;
   const dim3 grid(nblocks), block(WM * WN * 64);
   const int nk = q_pad / BK;
+  // residue-only products walk their tiles with one block per compute unit
+  // (the persistent form) when there are more tiles than units
+  auto launch_rt = [&](uint8_t* out, int total, int per) {
+    if (cus > 0 && total > cus)
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false, true>), dim3(cus), block,
+                         0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per, total);
+    else
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false>), dim3(total), block, 0, st,
+                         Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per, total);
+  };
   if (Ct == nullptr && rt != nullptr && split.parts > 1) {
     // K parts into the part planes, then their sum mod m_t into rt
     const int P = split.parts, per = split.slices;
     if (parts == nullptr || P > SPLIT_MAX || per < 1 || (long)(P - 1) * per >= nk || (long)P * per < nk ||
         (q_pad >= OZGEMM_Q_LIMIT && per > KBLOCK_K / BK))
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false>), dim3(nblocks * P), block, 0,
-                       st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, parts, nullptr, 0, per);
+    launch_rt(parts, nblocks * P, per);
     const long plane = (long)m_pad * n_pad;
     const long threads = plane / 16 * c.s;
     hipLaunchKernelGGL(rt_parts_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, parts, rt,
@@ -396,22 +463,21 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
       const int cnt = std::min(per, nk - k0);
       if (k0 == 0)
         hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false>), grid, block, 0, st,
-                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
+                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt, nblocks);
       else
         hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, true>), grid, block, 0, st,
-                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt);
+                           Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, k0, cnt, nblocks);
     }
     return hipGetLastError();
   }
   if (Ct != nullptr && rt != nullptr)
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, true, false>), grid, block, 0, st, Ares, Bres,
-                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
+                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
   else if (Ct != nullptr)
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, false, false>), grid, block, 0, st, Ares,
-                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
+                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
   else if (rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false>), grid, block, 0, st, Ares,
-                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk);
+    launch_rt(rt, nblocks, nk);
   return hipGetLastError();
 }
 
@@ -424,7 +490,8 @@ hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m
   none.m[0] = 2;
   const int nblocks = (n_pad / BN) * (m_pad / BM) * nout;
   hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, false, true>), dim3(nblocks),
-                     dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan, 0, 0);
+                     dim3(WM * WN * 64), 0, st, Aplanes, Bplanes, m_pad, n_pad, q_pad, none, P, nullptr, plan, 0, 0,
+                     nblocks);
   return hipGetLastError();
 }
 

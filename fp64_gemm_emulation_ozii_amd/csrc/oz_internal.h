@@ -74,10 +74,12 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
 // Scheme II products C_t = A_t B_t^T: int32 planes Ct and/or residues mod m_t
 // in rt.  With split.parts > 1 (residue-only) the K parts write the planes
 // `parts` (split.parts * s planes of m_pad * n_pad bytes; may be rt itself)
-// and are summed into rt; see gemm_grid.h.
+// and are summed into rt; see gemm_grid.h.  Residue-only products with more
+// blocks than cus (the device's compute units; 0 = never) run as cus
+// persistent blocks that walk the tiles.
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad,
                        const GemmConsts& c, int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts,
-                       hipStream_t st);
+                       int cus, hipStream_t st);
 
 // Scheme I slice products: output plane plan[o].w (m_pad x n_pad int32, [j][i])
 // = sum over u < plan[o].z of A_{plan[o].x + u} B_{plan[o].y - u}^T.

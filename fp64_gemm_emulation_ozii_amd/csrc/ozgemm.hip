@@ -309,12 +309,11 @@ int device_cus(int* cus) {
 
 // K parts of a residue-only Scheme II product of padded size mp x np x qp
 // (gemm_grid.h); their planes go to the workspace's product region.
-int product_split(int mp, int np, int qp, int s, SplitChoice* out) {
-  int cus = 0;
-  const int st = device_cus(&cus);
+int product_split(int mp, int np, int qp, int s, SplitChoice* out, int* cus) {
+  const int st = device_cus(cus);
   if (st) return st;
   const long cap = (long)(g.lay.rt_bytes / ((size_t)mp * np));
-  *out = choose_splits((mp / ROW_PAD) * (np / ROW_PAD), s, qp / K_PAD, cus, cap);
+  *out = choose_splits((mp / ROW_PAD) * (np / ROW_PAD), s, qp / K_PAD, *cus, cap);
   return 0;
 }
 
@@ -635,8 +634,9 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
   if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
   SplitChoice split{};
-  if ((st = product_split(mp, np, qp, s, &split))) return st;
-  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, split, rt, g.stream));
+  int cus = 0;
+  if ((st = product_split(mp, np, qp, s, &split, &cus))) return st;
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, split, rt, cus, g.stream));
   if (timed) OZ_CHECK(hipEventRecord(ev[3], g.stream));
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
   if (timed) {
@@ -723,9 +723,10 @@ int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8
   CrtConsts cc;
   make_consts(s, q, g.bound, &rc, &gc, &cc);
   SplitChoice split{1, qp / K_PAD};
-  if (Ct == nullptr && rt != nullptr && (st = product_split(mp, np, qp, s, &split))) return st;
+  int cus = 0;
+  if (Ct == nullptr && rt != nullptr && (st = product_split(mp, np, qp, s, &split, &cus))) return st;
   uint8_t* parts = reinterpret_cast<uint8_t*>(g.ws + g.lay.rt);
-  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, split, parts, g.stream));
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, split, parts, cus, g.stream));
   return 0;
 }
 
@@ -740,7 +741,8 @@ int ozgemm_gemm_parts(int m, int n, int q, int s, int* parts) {
   int mp, np, qp;
   dims(m, n, q, &mp, &np, &qp);
   SplitChoice split{};
-  const int st = product_split(mp, np, qp, s, &split);
+  int cus = 0;
+  const int st = product_split(mp, np, qp, s, &split, &cus);
   if (st) return st;
   *parts = split.parts;
   return OZGEMM_OK;

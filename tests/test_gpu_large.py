@@ -37,7 +37,7 @@ def sample_lines(size: int, count: int, seed: int, tile: int = 256):
     (16384, 1024, 16384, 1.0, 1),
     (1024, 65536, 1024, 1.0, 8),
     (16384, 16384, 16384, 4.0, 1),
-    (512, 2**20, 512, 1.0, None),
+    (384, 2**20, 384, 1.0, None),
     (1792, 2**17 + 300, 1792, 1.0, 0),
 ])
 def test_sampled_block_and_exponents(m, q, n, phi, parts):
@@ -60,8 +60,10 @@ def test_sampled_block_and_exponents(m, q, n, phi, parts):
     f = torch.empty(n, dtype=torch.int32, device="cuda")
     L.ozgemm_stage_scale(m, n, q, s, Ad, m, Bd, q, e, f)
     torch.cuda.synchronize()
-    rows = sample_lines(m, 56, seed=1)
-    cols = sample_lines(n, 56, seed=2)
+    # the oracle's cost grows with rows x cols x q: fewer lines for long K
+    lines = 56 if q < 2**17 else 12
+    rows = sample_lines(m, lines, seed=1)
+    cols = sample_lines(n, lines, seed=2)
     Cg = Cd[torch.from_numpy(cols).cuda()][:, torch.from_numpy(rows).cuda()].cpu().numpy().T
     eg = e.cpu().numpy()
     fg = f.cpu().numpy()
