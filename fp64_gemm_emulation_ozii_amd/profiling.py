@@ -72,13 +72,29 @@ def read_stats(path: str):
     return rows
 
 
-def write_stats(stats_csv: str, out_txt: str, command: str) -> None:
+def timed_average_us(trace_csv: str, kernel_prefix: str, timed: int) -> tuple[int, float]:
+    """(dispatches, mean microseconds) of the last `timed` dispatches of the
+    kernels whose name starts with kernel_prefix in a rocprofv3 kernel trace
+    -- the calls a benchmark times after its warmup calls."""
+    durs = []
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            if short_name(r["Kernel_Name"]).startswith(kernel_prefix):
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    last = durs[-timed:]
+    return len(last), (sum(last) / len(last) if last else float("nan"))
+
+
+def write_stats(stats_csv: str, out_txt: str, command: str, trace_csv: str | None = None, timed: int = 0) -> None:
     rows = read_stats(stats_csv)
     with open(out_txt, "w") as fh:
         fh.write(f"# rocprofv3 kernel statistics\n# command: {command}\n")
         fh.write(f"# {'kernel':<28} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}\n")
         for name, calls, total, avg, pct, mn, mx in sorted(rows, key=lambda r: -r[2]):
             fh.write(f"  {name:<28} {calls:>6} {avg / 1e3:>10.2f} {mn / 1e3:>10.2f} {mx / 1e3:>10.2f} {pct:>8.2f}\n")
+        if trace_csv and timed > 0:
+            n, avg = timed_average_us(trace_csv, "gemm_i8_kernel", timed)
+            fh.write(f"# gemm_i8_kernel, the {n} timed calls (after the warmup calls): avg {avg:.2f} us\n")
 
 
 def read_counter(path: str):
@@ -130,13 +146,51 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str
     return rec[workload]
 
 
+def write_clock(counter_csv: str, xcds: int, simds: int, timed: int, out_txt: str, command: str) -> dict:
+    """Clock and MFMA occupancy of gemm_i8_kernel from one rocprofv3 --pmc run
+    with GRBM_GUI_ACTIVE (summed over the XCDs), SQ_VALU_MFMA_BUSY_CYCLES and
+    SQ_INSTS_MFMA: clock = GUI_ACTIVE / xcds / dispatch time; MFMA busy =
+    busy cycles / (simds x GUI_ACTIVE / xcds), averaged over the last `timed`
+    dispatches."""
+    per = {}
+    with open(counter_csv) as fh:
+        for r in csv.DictReader(fh):
+            if not short_name(r["Kernel_Name"]).startswith("gemm_i8_kernel"):
+                continue
+            d = per.setdefault(int(r["Dispatch_Id"]), {"t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [per[k] for k in sorted(per)][-timed:]
+    clk, busy, mf = [], [], []
+    for d in disp:
+        cyc = d["GRBM_GUI_ACTIVE"] / xcds
+        clk.append(cyc / d["t"])
+        busy.append(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc))
+        mf.append(d["SQ_INSTS_MFMA"])
+    rec = {"dispatches": len(disp), "clock_ghz": sum(clk) / len(clk) / 1e9, "mfma_busy": sum(busy) / len(busy),
+           "mfma_insts": sum(mf) / len(mf), "ms": sum(d["t"] for d in disp) / len(disp) * 1e3}
+    with open(out_txt, "w") as fh:
+        fh.write(f"# gemm_i8_kernel clock and MFMA occupancy (rocprofv3 --pmc)\n# command: {command}\n")
+        fh.write(f"# then: python -m fp64_gemm_emulation_ozii_amd.profiling clock <counter csv> {xcds} {simds} {timed} <this file>\n")
+        fh.write(f"  dispatches averaged     {rec['dispatches']}\n")
+        fh.write(f"  dispatch time           {rec['ms']:.3f} ms\n")
+        fh.write(f"  clock (GUI_ACTIVE/{xcds}/t)  {rec['clock_ghz']:.3f} GHz\n")
+        fh.write(f"  MFMA busy fraction      {rec['mfma_busy']:.3f}\n")
+        fh.write(f"  MFMA instructions       {rec['mfma_insts']:.4g}\n")
+    return rec
+
+
 if __name__ == "__main__":
     what = sys.argv[1]
     if what == "stats":
         write_stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif what == "stats-timed":  # stats csv, trace csv, timed calls, output, command
+        write_stats(sys.argv[2], sys.argv[5], " ".join(sys.argv[6:]), trace_csv=sys.argv[3], timed=int(sys.argv[4]))
     elif what == "traffic":
         r = write_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6],
                           " ".join(sys.argv[7:]))
         print(json.dumps(r, indent=1))
+    elif what == "clock":  # counter csv, xcds, simds, timed calls, output, command
+        print(write_clock(sys.argv[2], int(sys.argv[3]), int(sys.argv[4]), int(sys.argv[5]), sys.argv[6],
+                          " ".join(sys.argv[7:])))
     else:
         raise SystemExit(f"unknown mode {what}")
