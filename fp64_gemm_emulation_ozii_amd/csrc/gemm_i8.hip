@@ -22,6 +22,13 @@
 // is XOR-permuted by a function of the row, so that the rows an MFMA operand
 // load touches fall in distinct bank groups.  K slices move from HBM straight
 // into LDS through two buffers.
+//
+// Grids (gemm_grid.h): a block's linear id picks its plane and tile; skinny
+// products with a long inner dimension are cut into K parts whose residues a
+// small kernel adds mod m_t; residue-only launches with more blocks than
+// compute units run as one persistent block per unit that walks the tiles
+// the hardware would have handed it, loading the next tile's first slice
+// while the finished one is reduced and written.
 #include "oz_internal.h"
 #include "prod_mod.h"
 

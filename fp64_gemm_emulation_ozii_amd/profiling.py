@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import csv
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -31,10 +32,22 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = ("gemm_i8.hip", "gemm_grid.h", "prod_mod.h")
 
 
-def kernel_sha(names=GEMM_SOURCES) -> str:
+def code_only(text: str) -> str:
+    """C++ source without comments and with runs of whitespace collapsed, so
+    that an edit to a comment does not count as a change of the kernel.
+    (String literals in these sources hold no comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_sha(names=GEMM_SOURCES, read=None) -> str:
+    """Hash of the code (comments stripped) of the GEMM sources; `read(name)`
+    returns a source's text (default: the file in csrc/)."""
+    read = read or (lambda name: open(os.path.join(PKG, "csrc", name)).read())
     h = hashlib.sha256()
     for name in names:
-        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
+        h.update(code_only(read(name)).encode())
     return h.hexdigest()[:16]
 
 
