@@ -35,6 +35,7 @@ def sample_lines(size: int, count: int, seed: int, tile: int = 256):
     (4096, 4096, 4096, 1.0, 1),
     (8192, 8192, 8192, 1.0, 1),
     (16384, 1024, 16384, 1.0, 1),
+    (16384, 384, 16384, 1.0, 1),
     (1024, 65536, 1024, 1.0, 8),
     (16384, 16384, 16384, 4.0, 1),
     (384, 2**20, 384, 1.0, None),
