@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -83,12 +84,16 @@ def cpu_baseline(A, B, s, q, target_s, Cg_full_getter, bound="conservative"):
         blas_threads = 1
     m, n = A.shape[0], B.shape[1]
     rng = np.random.default_rng(7)
-    # calibrate on a 32x32 block, then size the block for about target_s
-    # seconds (cost grows between linearly and quadratically with the side)
-    t0 = time.perf_counter()
-    oz.dgemm_block(A, B, s, np.arange(min(32, m)), np.arange(min(32, n)), bound=bound)
-    t_small = time.perf_counter() - t0
-    side = int(max(32, min(1024, 32 * (target_s / max(t_small, 1e-6)) ** (1 / 1.6))))
+    # calibrate on 32x32 and 64x64 blocks, fit how the cost grows with the
+    # side (between linearly and quadratically), and size the block for
+    # about target_s seconds
+    def timed(side):
+        t0 = time.perf_counter()
+        oz.dgemm_block(A, B, s, np.arange(min(side, m)), np.arange(min(side, n)), bound=bound)
+        return time.perf_counter() - t0
+    t32, t64 = timed(32), timed(64)
+    growth = min(2.0, max(1.0, math.log2(max(t64, 1e-6) / max(t32, 1e-6))))
+    side = int(max(32, min(1024, 64 * (target_s / max(t64, 1e-6)) ** (1 / growth))))
     rows = np.sort(rng.choice(m, size=min(side, m), replace=False))
     cols = np.sort(rng.choice(n, size=min(side, n), replace=False))
     t0 = time.perf_counter()
