@@ -42,14 +42,21 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
   int ei[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) ei[u] = e[min(i0 + u, m - 1)];
-  for (int j = blockIdx.y; j < n; j += gridDim.y) {
-    const int fj = f[j];
+  // the residues of the next column this thread handles are loaded before
+  // the current column is reduced, so their latency overlaps the arithmetic
+  auto load_col = [&](int j, uint32_t* rr) {
     const uint8_t* p = rt + (long)j * m_pad + i0;
-    // 1. exact FP64 limb sums for the four rows
-    uint32_t rr[4 * NG];
 #pragma unroll
     for (int t = 0; t < 4 * NG; ++t)
       rr[t] = (t < 4 * (NG - 1) || t < s) ? *reinterpret_cast<const uint32_t*>(p + (long)t * plane) : 0u;
+  };
+  uint32_t rr[4 * NG], rn[4 * NG];
+  if (blockIdx.y < n) load_col(blockIdx.y, rr);
+  for (int j = blockIdx.y; j < n; j += gridDim.y) {
+    const int fj = f[j];
+    const int jn = j + gridDim.y;
+    if (jn < n) load_col(jn, rn);
+    // 1. exact FP64 limb sums for the four rows
     double S[4][L];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -79,6 +86,8 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
       if (i0 + u < m) out[u] = res;
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int t = 0; t < 4 * NG; ++t) rr[t] = rn[t];
   }
 }
 
@@ -92,7 +101,9 @@ __global__ void fill_zero_kernel(double* C, int m, int n, long ldc) {
 
 hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e, const int32_t* f,
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
-  dim3 grid((m + 1023) / 1024, std::min(n, 65535));
+  // two columns per thread (the second one's loads overlap the first's
+  // arithmetic)
+  dim3 grid((m + 1023) / 1024, std::min((n + 1) / 2, 65535));
   const long plane = (long)m_pad * n_pad;
   const int ng = (c.s + 3) / 4;
   if (ng < 1 || ng > 5) return hipErrorInvalidValue;
