@@ -277,8 +277,10 @@ struct State {
 State g;
 
 constexpr size_t TIMING_MAX_CALLS = 4096;
-// residue grids index tiles of 32 rows in grid.y (<= 65535)
-constexpr int OZ_MAX_ROWS = 1 << 21;
+// the residue and Scheme I split grids index tiles of 32 rows in grid.y
+// (<= 65535), over rows padded to ROW_PAD
+constexpr int OZ_MAX_ROWS = OZGEMM_MAX_ROWS;
+static_assert((OZ_MAX_ROWS + ROW_PAD - 1) / ROW_PAD * ROW_PAD / 32 <= 65535, "row tiles fit grid.y");
 
 int hip_fail(hipError_t err) {
   g.hip_err = hipGetErrorString(err);

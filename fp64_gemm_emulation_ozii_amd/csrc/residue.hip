@@ -204,6 +204,7 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad, double* prime,
                           long prime_rs, long prime_ls, hipStream_t st) {
   if (q < 1) return hipErrorInvalidValue;  // q = 0 has no residues (callers handle it)
+  if (rows_pad / TR > 65535) return hipErrorInvalidValue;  // grid.y
   dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
   const bool rows_contig = (rs == 1);

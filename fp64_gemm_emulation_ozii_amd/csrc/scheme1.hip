@@ -290,6 +290,7 @@ __global__ void s1_plan_kernel(int variant, int k, int r, int beta, int4* gemm_p
 
 hipError_t launch_s1_rowmax(const double* X, int rows, int q, long rs, long ls, int rows_pad, int q_pad,
                             uint64_t* pmax, hipStream_t st) {
+  if (rows_pad / TR > 65535) return hipErrorInvalidValue;  // grid.y
   const dim3 grid(q_pad / TK, rows_pad / TR);
   if (rs == 1)
     hipLaunchKernelGGL((s1_split_kernel<true, 0>), grid, dim3(256), 0, st, X, rows, q, rs, ls, nullptr, rows_pad, 0,
@@ -310,6 +311,7 @@ hipError_t launch_s1_grid(const uint64_t* pmax, int rows_pad, int nchunks, int b
 hipError_t launch_s1_split(const double* X, int rows, int q, long rs, long ls, const int32_t* g, int rows_pad,
                            int q_pad, int variant, int pass, int k, int beta, int8_t* planes, uint64_t* pmax,
                            hipStream_t st) {
+  if (rows_pad / TR > 65535) return hipErrorInvalidValue;  // grid.y
   const dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
 #define OZ_S1_LAUNCH(RC, MD)                                                                                 \

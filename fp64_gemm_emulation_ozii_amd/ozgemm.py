@@ -24,6 +24,7 @@ OZGEMM_HIP_ERROR = 4
 OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_Q_MAX = 1 << 27
+OZGEMM_MAX_ROWS = 2096896  # 2^21 - 256
 OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
 OZGEMM_BOUND_CONSERVATIVE = 0
 OZGEMM_BOUND_FAST = 1

@@ -61,6 +61,7 @@ extern "C" {
 #define OZGEMM_S_MAX 20               /* largest supported number of moduli */
 #define OZGEMM_Q_LIMIT (1 << 17)      /* int8 dot products of length < this are exact in int32 (Ozaki II notes §6) */
 #define OZGEMM_Q_MAX   (1 << 27)      /* largest supported inner dimension */
+#define OZGEMM_MAX_ROWS 2096896       /* largest m and n: 2^21 - 256, so that the rows padded to 256 form at most 65535 tiles of 32 */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
 
 /* Bit budgets of Scheme II (ozgemm_set_bound) */
@@ -87,7 +88,8 @@ size_t ozgemm_workspace_bytes(int max_m, int max_n, int max_q, int s_max);
 /* Record the maximum problem size, the HIP stream (a hipStream_t, may be
  * NULL for the null stream) and a caller-owned device workspace of
  * workspace_bytes bytes.  Nothing is allocated or launched.  Replaces any
- * previous configuration.  Errors: -1..-4 bad sizes, -6 NULL workspace,
+ * previous configuration.  Errors: -1..-4 bad sizes (max_m and max_n at most
+ * OZGEMM_MAX_ROWS, max_q at most OZGEMM_Q_MAX), -6 NULL workspace,
  * OZGEMM_WORKSPACE_TOO_SMALL. */
 int ozgemm_config(int s_max, int max_m, int max_n, int max_q,
                   void *hip_stream, void *workspace, size_t workspace_bytes);

@@ -111,6 +111,15 @@ def test_validation_before_any_launch():
     assert lib.ozgemm_config(0, 512, 512, 512, None, FAKE, ws) == -1
     assert lib.ozgemm_config(16, -1, 512, 512, None, FAKE, ws) == -2
     assert lib.ozgemm_config(16, 512, 512, L.OZGEMM_Q_MAX + 1, None, FAKE, ws) == -4
+    # rows padded to 256 must form at most 65535 tiles of 32 (the residue grid's y)
+    assert L.OZGEMM_MAX_ROWS == 2**21 - 256 and -(-L.OZGEMM_MAX_ROWS // 256) * 256 // 32 <= 65535
+    assert -(-(L.OZGEMM_MAX_ROWS + 1) // 256) * 256 // 32 > 65535
+    big = L.ozgemm_workspace_bytes(L.OZGEMM_MAX_ROWS, 1, 1, 1)
+    assert lib.ozgemm_config(1, L.OZGEMM_MAX_ROWS, 1, 1, None, FAKE, big) == 0
+    assert lib.ozgemm_config(1, L.OZGEMM_MAX_ROWS + 1, 1, 1, None, FAKE, big) == -2
+    big = L.ozgemm_workspace_bytes(1, L.OZGEMM_MAX_ROWS, 1, 1)
+    assert lib.ozgemm_config(1, 1, L.OZGEMM_MAX_ROWS, 1, None, FAKE, big) == 0
+    assert lib.ozgemm_config(1, 1, L.OZGEMM_MAX_ROWS + 1, 1, None, FAKE, big) == -3
     assert lib.ozgemm_config(16, 512, 512, 512, None, None, ws) == -6
     assert lib.ozgemm_config(16, 512, 512, 512, None, FAKE, ws) == 0
     Cp = FAKE + (1 << 30)
@@ -214,3 +223,20 @@ def test_scheme1_validation_before_any_launch():
     a = lib.ozgemm_scheme1_stage_accumulate
     assert a(8, 8, 8, 4, 0, FAKE, FAKE, FAKE, FAKE, 7) == -10
     lib.ozgemm_free()
+
+
+def test_binding_constants_match_the_header():
+    """Every integer #define of include/ozgemm.h that the binding mirrors has
+    the same value there."""
+    import os
+    import re
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(here, "..", "include", "ozgemm.h")).read()
+    seen = 0
+    for name, expr in re.findall(r"^#define\s+(OZGEMM_\w+)\s+([^/\n]+)", text, flags=re.M):
+        if not hasattr(L, name):
+            continue
+        value = eval(expr.strip(), {})  # integer literals and shifts only
+        assert getattr(L, name) == value, name
+        seen += 1
+    assert seen >= 10
