@@ -111,7 +111,11 @@ const char *ozgemm_strerror(int status);
  * m, n, q >= 0; m = 0 or n = 0 does nothing; q = 0 writes C = 0.
  * C must not overlap A or B (-8).  Requires m <= max_m, n <= max_n,
  * q <= max_q, s <= s_max of the configuration (OZGEMM_RANGE otherwise).
- * Enqueues four kernels (scale, residue, int8 GEMM, CRT) on the stream. */
+ * Enqueues the scale, residue, int8 GEMM and CRT kernels on the stream.
+ * The first call after ozgemm_config also copies a 16 KB constant table
+ * into the workspace (a blocking host-to-device copy) and queries the
+ * device's compute-unit count; later calls only enqueue kernels, so they can
+ * be captured into a HIP graph once one call has run outside capture. */
 int ozgemm_dgemm(int m, int n, int q,
                  const double *A, int lda, const double *B, int ldb,
                  double *C, int ldc, int s);
