@@ -1,0 +1,98 @@
+"""Seeded random parity sweep of ozgemm_dgemm against the oracle.
+
+24 cases drawn from numpy.random.default_rng(20261202):
+  * shapes m, n in 1..300 and q in 1..6000 (some long enough for K parts,
+    some short enough for the short-K kernel);
+  * s in 6..20 where the bit budget leaves k >= 1;
+  * phi in {0, 0.5, 1, 2, 8} (the HPL-like generator);
+  * the conservative or the OS II-fast bit budget;
+  * leading-dimension padding (padding holds NaN, which must never be read);
+  * sometimes a zero row or column, a row scaled into the subnormal range or
+    towards overflow, or an Inf/NaN entry.
+Every C must equal the oracle's bit for bit (NaN positions alike) and lie
+within 2^-50 (|A||B|)_ij of it.
+"""
+import numpy as np
+import pytest
+
+from oracle import ozaki2 as oz
+from fp64_gemm_emulation_ozii_amd import ozgemm as L
+from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
+
+from gpu_util import configure, first_diff, log, run_dgemm, same_doubles, within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+MAX_M, MAX_N, MAX_Q = 300, 300, 6000
+
+
+def draw_cases(count: int, seed: int = 20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        m = int(rng.integers(1, MAX_M + 1))
+        n = int(rng.integers(1, MAX_N + 1))
+        q = int(rng.integers(1, 600)) if rng.random() < 0.5 else int(rng.integers(600, MAX_Q + 1))
+        s = int(rng.integers(6, 21))
+        bound = "fast" if rng.random() < 0.35 else "conservative"
+        M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+        if bound == "conservative" and oz.kbits(M, q) < 1:
+            continue
+        if bound == "fast" and s < 8:
+            continue
+        phi = float(rng.choice([0.0, 0.5, 1.0, 2.0, 8.0]))
+        pads = tuple(int(rng.integers(0, 4)) for _ in range(3))
+        special = str(rng.choice(["none", "none", "zero", "tiny", "huge", "nonfinite"]))
+        cases.append((m, n, q, s, bound, phi, pads, special, int(rng.integers(0, 2**31))))
+    return cases
+
+
+CASES = draw_cases(24)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def random_config():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    configure(MAX_M, MAX_N, MAX_Q, 20)
+    yield
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
+    L.ozgemm_free()
+
+
+def make_inputs(m, n, q, phi, special, seed):
+    A, B = hpl_like(m, q, n, phi, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    i, j, l = int(rng.integers(0, m)), int(rng.integers(0, n)), int(rng.integers(0, q))
+    if special == "zero":
+        A[i, :] = 0.0
+        B[:, j] = 0.0
+    elif special == "tiny":
+        A[i, :] *= 2.0 ** -1000
+        B[:, j] *= 2.0 ** -60
+    elif special == "huge":
+        A[i, :] *= 2.0 ** 900
+        B[:, j] *= 2.0 ** 200
+    elif special == "nonfinite":
+        A[i, l] = np.inf
+        B[l, j] = np.nan
+    return A, B
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_random_case(case):
+    m, n, q, s, bound, phi, pads, special, seed = CASES[case]
+    log(f"random case {case}: m={m} n={n} q={q} s={s} bound={bound} phi={phi} pads={pads} special={special}")
+    A, B = make_inputs(m, n, q, phi, special, seed)
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if bound == "fast" else L.OZGEMM_BOUND_CONSERVATIVE)
+    try:
+        C, _ = run_dgemm(A, B, s, lda=m + pads[0], ldb=q + pads[1], ldc=m + pads[2])
+    finally:
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
+    ref = oz.dgemm(A, B, s, bound=bound)
+    assert same_doubles(C, ref), first_diff(C, ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        finite_rows = np.isfinite(A).all(axis=1)
+        finite_cols = np.isfinite(B).all(axis=0)
+        sub = np.ix_(finite_rows, finite_cols)
+        assert within_tolerance(C[sub], ref[sub], A[finite_rows], B[:, finite_cols])
