@@ -1,4 +1,5 @@
-"""Seeded random parity sweep of ozgemm_dgemm against the oracle.
+"""Seeded random parity sweeps of ozgemm_dgemm and ozgemm_scheme1_dgemm
+against the oracles.
 
 24 cases drawn from numpy.random.default_rng(20261202):
   * shapes m, n in 1..300 and q in 1..6000 (some long enough for K parts,
@@ -9,8 +10,10 @@
   * leading-dimension padding (padding holds NaN, which must never be read);
   * sometimes a zero row or column, a row scaled into the subnormal range or
     towards overflow, or an Inf/NaN entry.
-Every C must equal the oracle's bit for bit (NaN positions alike) and lie
-within 2^-50 (|A||B|)_ij of it.
+Every C must equal the oracle's bit for bit (NaN positions alike) and, for
+Scheme II, lie within 2^-50 (|A||B|)_ij of it.  The Scheme I sweep draws
+16 cases of the same kinds with k in 2..10 slices and the RN or the Hybrid
+variant.
 """
 import numpy as np
 import pytest
@@ -19,7 +22,7 @@ from oracle import ozaki2 as oz
 from fp64_gemm_emulation_ozii_amd import ozgemm as L
 from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
 
-from gpu_util import configure, first_diff, log, run_dgemm, same_doubles, within_tolerance
+from gpu_util import configure, dev_colmajor, first_diff, log, run_dgemm, same_doubles, within_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +99,53 @@ def test_random_case(case):
         finite_cols = np.isfinite(B).all(axis=0)
         sub = np.ix_(finite_rows, finite_cols)
         assert within_tolerance(C[sub], ref[sub], A[finite_rows], B[:, finite_cols])
+
+
+# ---- Scheme I: 16 cases of the same kinds, k in 2..10, RN or Hybrid ----
+
+def draw_s1_cases(count: int, seed: int = 20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        m = int(rng.integers(1, MAX_M + 1))
+        n = int(rng.integers(1, MAX_N + 1))
+        q = int(rng.integers(1, 600)) if rng.random() < 0.5 else int(rng.integers(600, MAX_Q + 1))
+        k = int(rng.integers(2, 11))
+        variant = str(rng.choice(["rn", "hybrid"]))
+        phi = float(rng.choice([0.0, 0.5, 1.0, 2.0, 8.0]))
+        pads = tuple(int(rng.integers(0, 4)) for _ in range(3))
+        special = str(rng.choice(["none", "none", "zero", "tiny", "huge", "nonfinite"]))
+        cases.append((m, n, q, k, variant, phi, pads, special, int(rng.integers(0, 2**31))))
+    return cases
+
+
+S1_CASES = draw_s1_cases(16)
+
+
+@pytest.mark.parametrize("case", range(len(S1_CASES)))
+def test_random_scheme1_case(case):
+    import torch
+    from oracle import ozaki1 as o1
+    m, n, q, k, variant, phi, pads, special, seed = S1_CASES[case]
+    log(f"random Scheme I case {case}: m={m} n={n} q={q} k={k} {variant} phi={phi} pads={pads} special={special}")
+    A, B = make_inputs(m, n, q, phi, special, seed)
+    v = L.OZGEMM_S1_RN if variant == "rn" else L.OZGEMM_S1_HYBRID
+    need = max(L.ozgemm_workspace_bytes(MAX_M, MAX_N, MAX_Q, 20), L.ozgemm_scheme1_workspace_bytes(m, n, q, k, v))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    L.ozgemm_free()
+    L.ozgemm_config(20, MAX_M, MAX_N, MAX_Q, workspace=ws)
+    try:
+        lda, ldb, ldc = m + pads[0], q + pads[1], m + pads[2]
+        Ad = dev_colmajor(A, lda, fill=np.nan)
+        Bd = dev_colmajor(B, ldb, fill=np.nan)
+        Cd = torch.full((max(n, 1), ldc), 12345.0, dtype=torch.float64, device="cuda")
+        L.ozgemm_scheme1_dgemm(m, n, q, Ad, lda, Bd, ldb, Cd, ldc, k, v)
+        torch.cuda.synchronize()
+        buf = Cd.cpu().numpy()
+        C = buf[:n, :m].T
+        assert np.all(buf[:n, m:] == 12345.0), "ldc padding written"
+    finally:
+        del ws
+        configure(MAX_M, MAX_N, MAX_Q, 20)
+    ref = o1.dgemm(A, B, k, variant)
+    assert same_doubles(C, ref), first_diff(C, ref)
