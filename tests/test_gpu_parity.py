@@ -2,7 +2,7 @@
 
 Integer stages (exponents, A', B', int8 residue planes, int32 products,
 product residues) must match bit for bit; the FP64 result must lie within
-2^-50 (|A||B|)_ij of the oracle's correctly rounded value (the north-star
+2^-50 (|A||B|)_ij of the oracle's correctly rounded value (the required
 tolerance) and, because the CRT kernel also rounds once to nearest, is
 expected to match it bit for bit as well.
 """
