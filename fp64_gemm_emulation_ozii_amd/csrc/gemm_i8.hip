@@ -61,6 +61,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// An accumulator entry read out of its AGPR.  The "a" constraint keeps the
+// 256 accumulators of the main kernel in AGPRs up to the epilogue; read as
+// plain values, each used twice by the biased reduction, the compiler moved
+// some of them into VGPRs and spilled other values.
+__device__ __forceinline__ int32_t from_agpr(int32_t x) {
+  int32_t r;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
+// The low bytes of four words as one word, first word lowest.
+__device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.0, b1.0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // b2.0, b3.0, 0, 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // BM x BN output tile per block of WM x WN wavefronts; each wavefront owns a
 // (BM/WM) x (BN/WN) sub-tile of 32x32 tiles of v_mfma_i32_32x32x32_i8.  Lane
 // l of that instruction supplies 16 bytes of row (l mod 32) of A (column
@@ -122,6 +139,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   // loop), or, in the persistent form, buffer 1 and what follows it, so that
   // the next tile's first slice can land in buffer 0 meanwhile.
   constexpr bool STAGED = WRITE_RT && !WRITE_CT && !ACC_RT;
+  // Residue-only output starts the accumulators at -(m_t - 1)/2 (0 for
+  // m_t = 256), which lets the epilogue reduce each entry with one rounding
+  // fma and one 24-bit multiply-add (mod_product_biased).
+  constexpr bool BIASED = WRITE_RT && !WRITE_CT;
   static_assert(!PERSIST || (STAGED && !MULTI), "persistent form: residue-only products");
   constexpr int CS = BM + 16;  // 16-byte aligned; consecutive columns start 4 banks apart
   constexpr int OPERANDS = 2 * (BM + BN) * BK;
@@ -223,11 +244,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     return *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
   };
 
+  // this plane's modulus, selected without indexing the by-value argument
+  // dynamically (which would copy it to scratch)
+  auto modulus = [&]() {
+    int mt = c.m[0];
+#pragma unroll
+    for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+    return mt;
+  };
+  auto reset_acc = [&](v16i (&a)[FM][FN]) {
+    v16i start = {};
+    if (BIASED) start += mod_bias(modulus()).bias;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) a[i][j] = start;
+  };
+
   v16i acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+  reset_acc(acc);
 
   // The window after barrier kt - 1 holds 16 NKS slots: the last step of
   // slice kt - 1 (slots 0..15), then steps 0..NKS-2 of slice kt.  Its loads
@@ -283,12 +318,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     wait_vmcnt<0>();  // no load into LDS may outlive the block
 
     // ---- epilogue: int32 planes and/or residues mod m_t ----
-    // this plane's modulus, selected without indexing the by-value argument
-    // dynamically (which would copy it to scratch)
-    int mt = c.m[0];
-#pragma unroll
-    for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+    const int mt = modulus();
     const double md = (double)mt, inv = 1.0 / md;  // correctly rounded
+    const ModBias mb = mod_bias(mt);
     const int em0 = m0, en0 = n0, eout = out_t;    // the finished tile
     bool more = false;
     if (STAGED) {
@@ -320,9 +352,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
           const v16i& v = acc[i][j];
           if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
           if (WRITE_RT) {
-            uint32_t r0 = mod_product(v[4 * g], md, inv), r1 = mod_product(v[4 * g + 1], md, inv);
-            uint32_t r2 = mod_product(v[4 * g + 2], md, inv), r3 = mod_product(v[4 * g + 3], md, inv);
+            uint32_t r0, r1, r2, r3;
+            if (BIASED) {  // residues in the low bytes
+              r0 = mod_product_biased(from_agpr(v[4 * g]), mb.negm, inv, mb.magic);
+              r1 = mod_product_biased(from_agpr(v[4 * g + 1]), mb.negm, inv, mb.magic);
+              r2 = mod_product_biased(from_agpr(v[4 * g + 2]), mb.negm, inv, mb.magic);
+              r3 = mod_product_biased(from_agpr(v[4 * g + 3]), mb.negm, inv, mb.magic);
+            } else {
+              r0 = mod_product(v[4 * g], md, inv);
+              r1 = mod_product(v[4 * g + 1], md, inv);
+              r2 = mod_product(v[4 * g + 2], md, inv);
+              r3 = mod_product(v[4 * g + 3], md, inv);
+            }
             if (ACC_RT) {  // add the residues of the earlier K blocks, mod m_t
+              r0 &= 0xffu;
+              r1 &= 0xffu;
+              r2 &= 0xffu;
+              r3 &= 0xffu;
               const uint32_t old = *reinterpret_cast<const uint32_t*>(rt + off);
               r0 += old & 0xffu;
               r1 += (old >> 8) & 0xffu;
@@ -333,7 +379,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
               r2 = r2 >= (uint32_t)mt ? r2 - mt : r2;
               r3 = r3 >= (uint32_t)mt ? r3 - mt : r3;
             }
-            const uint32_t word = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+            const uint32_t word = low_bytes(r0, r1, r2, r3);
             if (STAGED)
               *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = word;
             else
@@ -370,10 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int li = 0; li < LPW; ++li)
         if (2 * li + 1 < 16) load1(1, li);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+    reset_acc(acc);
     wait_vmcnt<0>();  // slice 0, the half of slice 1 and this tile's stores
     __builtin_amdgcn_s_barrier();
   }
@@ -464,11 +507,22 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     return *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz64(row)) * 16)]);
   };
 
+  // this plane's modulus (selected without dynamic indexing of the argument);
+  // the accumulators start at -(m_t - 1)/2, or 0 for m_t = 256, for the
+  // biased reduction of the epilogue
+  int mt = c.m[0];
+#pragma unroll
+  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
+  const ModBias mb = mod_bias(mt);
   v16i acc[FM][FN];
+  {
+    v16i start = {};
+    start += mb.bias;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+      for (int j = 0; j < FN; ++j) acc[i][j] = start;
+  }
 
   // Prologue: slices 0, 1, 2 (as many as exist); wait for slice 0 only
   // (loads return in order).  The window after the barrier of slice kt
@@ -523,10 +577,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   // epilogue: residues mod m_t, staged as the tile's columns, written as
   // whole column segments
-  int mt = c.m[0];
-#pragma unroll
-  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
-  const double md = (double)mt, inv = 1.0 / md;
+  const double inv = 1.0 / (double)mt;  // correctly rounded
   const long plane = (long)m_pad * n_pad;
   uint8_t* stage = reinterpret_cast<uint8_t*>(smem);
   __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -540,9 +591,11 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int g = 0; g < 4; ++g) {
         const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
         const v16i& v = acc[i][j];
-        const uint32_t r0 = mod_product(v[4 * g], md, inv), r1 = mod_product(v[4 * g + 1], md, inv);
-        const uint32_t r2 = mod_product(v[4 * g + 2], md, inv), r3 = mod_product(v[4 * g + 3], md, inv);
-        *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+        const uint32_t r0 = mod_product_biased(v[4 * g], mb.negm, inv, mb.magic);
+        const uint32_t r1 = mod_product_biased(v[4 * g + 1], mb.negm, inv, mb.magic);
+        const uint32_t r2 = mod_product_biased(v[4 * g + 2], mb.negm, inv, mb.magic);
+        const uint32_t r3 = mod_product_biased(v[4 * g + 3], mb.negm, inv, mb.magic);
+        *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = low_bytes(r0, r1, r2, r3);
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -31,4 +31,43 @@ __host__ __device__ __forceinline__ uint32_t mod_product(int32_t v, double m, do
   return (uint32_t)__builtin_fma(-q, m, x);
 }
 
+// Biased form, for accumulators that start at -h instead of 0: acc = v - h
+// with v the product entry.  For odd m, h = (m - 1)/2, so that
+// (v - h)/m = floor(v/m) + (r - h)/m with r = v mod m, and |r - h|/m is at
+// most 1/2 - 1/(2m).  Rounding (v - h)/m to the nearest integer therefore
+// gives floor(v/m), with the same 1/(2m) margin as above; one fma against
+// the magic number 1.5 2^52 + beta rounds it (its grid spacing is 1 between
+// 2^52 and 2^53), and the low 32 bits of the result are floor(v/m) + beta.
+// The residue is needed as a byte only, so the rest runs modulo 256:
+// acc + (256 - m)(floor(v/m) + beta) = r - h - m beta (mod 256), and
+// beta = -h m^-1 (mod 256) leaves r in the low byte.  The product uses the
+// low 24 bits of each factor, which keeps it one 24-bit multiply-add.
+// For m = 256 the bias is 0 and the multiplier 0: the low byte of v is r.
+// Valid for m = 256 and odd 3 <= m <= 255, and every int32 acc.
+struct ModBias {
+  int32_t bias;   // the accumulators' start value, -h
+  uint32_t negm;  // 256 - m, or 0 for m = 256
+  double magic;   // 1.5 2^52 + beta
+};
+
+// Integer operations only (1.5 2^52 + beta is assembled from its bits), so
+// that on the GPU a wave-uniform m keeps every field in scalar registers.
+__host__ __device__ inline ModBias mod_bias(int m) {
+  const uint32_t um = (uint32_t)m, h = m == 256 ? 0u : (um - 1u) >> 1;
+  uint32_t x = um;     // m^-1 mod 8 for odd m (every odd m is its own inverse there)
+  x *= 2u - um * x;    // mod 2^6
+  x *= 2u - um * x;    // mod 2^12
+  const uint32_t beta = ((256u - h) * x) & 255u;  // 0 for m = 256, as h = 0
+  return ModBias{-(int32_t)h, 256u - um, __builtin_bit_cast(double, 0x4338000000000000ull | beta)};
+}
+
+// Low byte: (acc + h) mod m, for acc = v - h as above.  The upper bytes are
+// not cleared.
+__host__ __device__ __forceinline__ uint32_t mod_product_biased(int32_t acc, uint32_t negm, double inv,
+                                                                double magic) {
+  const double t = __builtin_fma((double)acc, inv, magic);
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(uint64_t, t);
+  return (lo & 0xffffffu) * (negm & 0xffffffu) + (uint32_t)acc;
+}
+
 }  // namespace oz
