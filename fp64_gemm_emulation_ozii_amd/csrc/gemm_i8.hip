@@ -79,25 +79,37 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 }
 
 // BM x BN output tile per block of WM x WN wavefronts; each wavefront owns a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 tiles of v_mfma_i32_32x32x32_i8.  Lane
-// l of that instruction supplies 16 bytes of row (l mod 32) of A (column
-// (l mod 32) of B) from K chunk l / 32 of the 32-wide K step; both operands
-// use the same lane -> K mapping, so the product is the dot product over the
-// step whatever order the hardware takes the bytes in.  Lane l receives rows
-// 8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
+// (BM/WM) x (BN/WN) sub-tile of MT x MT tiles of one int8 MFMA:
+//  * MT = 16, v_mfma_i32_16x16x64_i8, for the residue-only products.  On
+//    random int8 operands the chip's power limit lets this instruction
+//    sustain about 15% more operations per second than the 32x32x32 one
+//    (3.65 against 3.15 POP/s in a register-only loop); the 8192^3 product
+//    phase runs 4-5% faster with it.  Lane l supplies 16 bytes of row
+//    (l mod 16) of A (column (l mod 16) of B) from K chunk l / 16 of the
+//    64-wide K step and receives rows 4 (l / 16) + r, r = 0..3, of column
+//    (l mod 16).
+//  * MT = 32, v_mfma_i32_32x32x32_i8, for the int32-output forms (the debug
+//    planes and Scheme I's plan products, whose plan form spills its
+//    accumulators with 16-wide tiles).  Lane l supplies 16 bytes of row
+//    (l mod 32) from K chunk l / 32 of the 32-wide step and receives rows
+//    8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
+// Both operands use the same lane -> K mapping, so the product is the dot
+// product over the step whatever order the hardware takes the bytes in.
 //
 // Data movement and instruction order:
 //  * K slices of BK bytes go from HBM straight into LDS (global_load_lds, 16
 //    bytes per lane, no register staging) through two buffers.
-//  * One barrier per slice, placed before the last 32-wide step's MFMAs: it
+//  * One barrier per slice, placed before the last K step's MFMAs: it
 //    publishes slice kt + 1 (this wave's loads of it have landed) and retires
 //    buffer kt mod 2 (this wave's reads of it are in registers).
-//  * Every step is a fixed sequence of 16 MFMA slots.  The fragments of the
-//    next step are read from LDS after the even slots (eight reads), and the
-//    16 loads of the slice two ahead go after the odd slots of the 32 slots
-//    that follow the barrier (the last step of slice kt, then step 0 of slice
-//    kt + 1).  Spreading the loads this way keeps their issue from stalling
-//    the MFMA stream, and the last of them still has two steps to land.
+//  * Every step is a fixed sequence of MFMA slots (16 with MT = 32, 64 with
+//    MT = 16).  The fragments of the next step are read from LDS, one after
+//    every RS-th slot, and the 16 loads of the slice two ahead go after
+//    slots 1, 1 + RS, 1 + 2 RS, ... of the window that follows the barrier
+//    (the last step of slice kt, then the next slice's steps): over the
+//    first 1024 MFMA cycles of the window with either instruction.
+//    Spreading the loads this way keeps their issue from stalling the MFMA
+//    stream, and the last of them still has half a slice to land.
 //    (Measured at 8192^3 x 14 planes: 7.1 ms with the loads issued as one
 //    burst per slice, 6.3 ms with this order.)
 // K parts (gemm_grid.h): plane index p s + t of a residue-only launch is
@@ -123,13 +135,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int B_LOADS = BN * BK / 1024 / NW;
   constexpr int LPW = A_LOADS + B_LOADS;        // loads per wavefront per slice
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int NKS = BK / 32;                  // 32-wide MFMA steps per slice
+  constexpr int MT = WRITE_RT && !WRITE_CT ? 16 : 32;  // MFMA tile (see above)
+  constexpr int KSTEP = 1024 / MT;              // K bytes per MFMA: 64 or 32
+  constexpr int CPS = KSTEP / 16;               // 16-byte K chunks per step
+  constexpr int ACC_N = MT * MT / 64;           // accumulators per lane per tile: 4 or 16
+  constexpr int FM = WTM / MT, FN = WTN / MT;
+  constexpr int NKS = BK / KSTEP;               // K steps per slice
   constexpr int NF = FM + FN;                   // fragments per step
+  constexpr int SLOTS = FM * FN;                // MFMAs per step
+  constexpr int RS = SLOTS / NF;                // slots per fragment read
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
-  static_assert(FM * FN == 16 && NF == 8 && NKS >= 2, "slot plan: 16 MFMAs, 8 reads per step");
-  static_assert(2 * LPW <= 16 * NKS, "every load has an odd slot in its window");
-  constexpr int HALF_LOADS = LPW < 8 ? LPW : 8;  // loads of a slice issued in the window before it
+  static_assert(SLOTS % NF == 0 && NKS >= 2, "slot plan: whole reads per step, two steps per slice");
+  static_assert(RS * (LPW - 1) + 1 < SLOTS * NKS, "every load has a slot in its window");
+  // loads of a slice issued in the window before it: those with
+  // RS li + 1 < SLOTS (8 with MT = 32, all 16 with MT = 16)
+  constexpr int HALF_LOADS = (SLOTS - 2) / RS + 1 < LPW ? (SLOTS - 2) / RS + 1 : LPW;
+  static_assert(HALF_LOADS == (MT == 32 ? 8 : LPW), "prologue load count");
+  typedef int acc_t __attribute__((ext_vector_type(ACC_N)));
 
   // Staged residue output: the words are first placed in LDS as the tile's
   // columns (BM bytes each, stride CS), then each wavefront writes whole
@@ -229,18 +251,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  const int lrow = lane & 31;
-  const int lkc = lane >> 5;  // K chunk (of 2) within a 32-wide step
+  const int lrow = lane % MT;
+  const int lkc = lane / MT;  // K chunk within a step
   // fragment f of step ks in buffer buf: f < FN are B columns, the rest A rows
   auto read1 = [&](int buf, int ks, int f) -> v4i {
     const int8_t* As = smem + buf * (BM + BN) * BK;
     const int8_t* Bs = As + BM * BK;
-    const int kc = ks * 2 + lkc;
+    const int kc = ks * CPS + lkc;
     if (f < FN) {
-      const int row = wn * WTN + f * 32 + lrow;
+      const int row = wn * WTN + f * MT + lrow;
       return *reinterpret_cast<const v4i*>(&Bs[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
     }
-    const int row = wm * WTM + (f - FN) * 32 + lrow;
+    const int row = wm * WTM + (f - FN) * MT + lrow;
     return *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz<BK>(row)) * 16)]);
   };
 
@@ -252,8 +274,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
     return mt;
   };
-  auto reset_acc = [&](v16i (&a)[FM][FN]) {
-    v16i start = {};
+  auto reset_acc = [&](acc_t (&a)[FM][FN]) {
+    acc_t start = {};
     if (BIASED) start += mod_bias(modulus()).bias;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -261,20 +283,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
       for (int j = 0; j < FN; ++j) a[i][j] = start;
   };
 
-  v16i acc[FM][FN];
+  acc_t acc[FM][FN];
   reset_acc(acc);
 
-  // The window after barrier kt - 1 holds 16 NKS slots: the last step of
-  // slice kt - 1 (slots 0..15), then steps 0..NKS-2 of slice kt.  Its loads
-  // fetch slice kt + 1 into the buffer retired by that barrier; load li goes
-  // after slot 2 li + 1.  The prologue stands in for the part of window 0
-  // that precedes slice 0.
+  // The window after barrier kt - 1 holds SLOTS NKS slots: the last step of
+  // slice kt - 1 (slots 0..SLOTS-1), then steps 0..NKS-2 of slice kt.  Its
+  // loads fetch slice kt + 1 into the buffer retired by that barrier; load li
+  // goes after slot RS li + 1.  The prologue stands in for the part of
+  // window 0 that precedes slice 0.
 #pragma unroll
   for (int li = 0; li < LPW; ++li) load1(0, li);
   if (nkt > 1) {
 #pragma unroll
     for (int li = 0; li < LPW; ++li)
-      if (2 * li + 1 < 16) load1(1, li);
+      if (RS * li + 1 < SLOTS) load1(1, li);
     wait_vmcnt<HALF_LOADS>();  // slice 0 (loads return in order)
   } else {
     wait_vmcnt<0>();
@@ -301,14 +323,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
         const int rbuf = last ? (kt + 1) & 1 : kt & 1;  // (past the end: read, unused)
         const int rks = last ? 0 : ks + 1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < SLOTS; ++r) {
           const int i = r / FN, j = r % FN;
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
-          if ((r & 1) == 0) nxt[r / 2] = read1(rbuf, rks, r / 2);
-          const int slot = last ? r : 16 + ks * 16 + r;
+          if constexpr (MT == 16)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+          if (r % RS == 0) nxt[r / RS] = read1(rbuf, rks, r / RS);
+          const int slot = last ? r : SLOTS + ks * SLOTS + r;
 #pragma unroll
           for (int li = 0; li < LPW; ++li)
-            if (2 * li + 1 == slot && lslice < nkt) load1(lslice, li);
+            if (RS * li + 1 == slot && lslice < nkt) load1(lslice, li);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -342,14 +367,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int lcol = wn * WTN + j * 32 + (lane & 31);
+        const int lcol = wn * WTN + j * MT + lane % MT;
         const int col = en0 + lcol;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
+        for (int g = 0; g < ACC_N / 4; ++g) {  // four consecutive rows each
+          const int lrow4 = wm * WTM + i * MT + 8 * g + 4 * (lane / MT);
           const int row = em0 + lrow4;
           const long off = (long)eout * plane + (long)col * m_pad + row;
-          const v16i& v = acc[i][j];
+          const acc_t& v = acc[i][j];
           if (WRITE_CT) *reinterpret_cast<v4i*>(Ct + off) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
           if (WRITE_RT) {
             uint32_t r0, r1, r2, r3;
@@ -386,8 +411,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
               *reinterpret_cast<uint32_t*>(rt + off) = word;
           }
         }
-        // keep the scheduler from hoisting every accumulator out of AGPRs at once
-        __builtin_amdgcn_sched_barrier(0);
+        // keep the scheduler from hoisting every accumulator out of AGPRs at
+        // once: a barrier after every 16 accumulators
+        if ((j + 1) * ACC_N % 16 == 0) __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (STAGED) {
@@ -415,7 +441,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     if (nkt > 1)
 #pragma unroll
       for (int li = 0; li < LPW; ++li)
-        if (2 * li + 1 < 16) load1(1, li);
+        if (RS * li + 1 < SLOTS) load1(1, li);
     reset_acc(acc);
     wait_vmcnt<0>();  // slice 0, the half of slice 1 and this tile's stores
     __builtin_amdgcn_s_barrier();
