@@ -309,6 +309,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     v4i cur[NF], nxt[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) cur[f] = read1(0, 0, f);
+    // The slice loop is entered, and each iteration ends, with no LDS read in
+    // flight.  The compiler places a full lgkmcnt wait at the loop head;
+    // with each slot's MFMA issued before its read, that wait then costs
+    // nothing, where it used to follow the step's first read and take a whole
+    // LDS latency once per slice (1-1.5% of the product at 8192^3).
+    __builtin_amdgcn_s_waitcnt(0xc07f);
 
     for (int kt = 0; kt < nkt; ++kt) {
 #pragma unroll
@@ -329,6 +335,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
           else
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);  // the slot's MFMA issues before its read
           if (r % RS == 0) nxt[r / RS] = read1(rbuf, rks, r / RS);
           const int slot = last ? r : SLOTS + ks * SLOTS + r;
 #pragma unroll
@@ -336,6 +343,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
             if (RS * li + 1 == slot && lslice < nkt) load1(lslice, li);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (last) __builtin_amdgcn_s_waitcnt(0xc07f);  // no LDS read in flight (see above)
 #pragma unroll
         for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
       }
