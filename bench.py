@@ -168,6 +168,7 @@ def main():
     int8_ops = 2.0 * s * m * n * q
     achieved = int8_ops / (gemm_ms * 1e-3) / 1e12
     mp, np_, qp = L.ozgemm_plane_dims(m, n, q)
+    b_one_pass = args.bound == "conservative" and L.OZGEMM_ONE_PASS_Q_MIN <= q <= L.OZGEMM_ONE_PASS_Q_MAX
 
     out = {
         "metric": "emulated-FP64 TFLOPS (2mnq/t) at 8192^3, s=14; INT8 MFMA peak fraction",
@@ -199,7 +200,9 @@ def main():
         "int8_tops_end_to_end": round(int8_ops / (ms_per_step * 1e-3) / 1e12, 2),
         "int8_peak_frac_end_to_end": round(int8_ops / (ms_per_step * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
         "memory_phases_GBs": {
-            "scale": round(8.0 * (m * q + q * n) / (per[0] * 1e-3) / 1e9, 1),
+            # B is read by the scale phase only when its exponents are not
+            # taken in the residue pass (OS II-fast, or q outside the one-pass range)
+            "scale": round(8.0 * (m * q + (0 if b_one_pass else q * n)) / (per[0] * 1e-3) / 1e9, 1),
             "residue": round((8.0 + s) * (m * q + q * n) / (per[1] * 1e-3) / 1e9, 1),
             "crt": round((s + 8.0) * m * n / (per[3] * 1e-3) / 1e9, 1),
         },

@@ -21,6 +21,26 @@ constexpr int SCALE_CHUNK = 128;  // columns of A per partial row-max block
 inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
 
 // Per-modulus constants for the residue kernel (Ozaki II notes §6).
+// |x| as its IEEE bit pattern: for non-negative doubles the unsigned integer
+// order is the numeric order, and Inf/NaN patterns sort above every finite
+// value (the scale step and the column residue kernel take maxima on these).
+__device__ __forceinline__ uint64_t abs_bits(double x) {
+  return (uint64_t)__double_as_longlong(x) & 0x7fffffffffffffffull;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// frexp exponent of the double whose |.| bit pattern is b:
+// 2^(e - 1) <= |x| < 2^e; 0 for zero, OZGEMM_EXP_NONFINITE for Inf/NaN.
+__device__ __forceinline__ int32_t exponent_of_bits(uint64_t b) {
+  if (b == 0) return 0;
+  if (b >= 0x7ff0000000000000ull) return OZGEMM_EXP_NONFINITE;
+  int biased = (int)(b >> 52);
+  if (biased > 0) return biased - 1022;         // value in [2^(E-1023), 2^(E-1022))
+  int top = 63 - __clzll((long long)b);          // subnormal: mant * 2^-1074
+  return top - 1073;
+}
+
 struct ResidueConsts {
   int s;
   int k;                        // shift base: row shift is k - e_i
@@ -67,6 +87,12 @@ hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, in
 
 // Residues of the rows of X where element (r, l) sits at X[r*rs + l*ls].
 // Writes `rows_pad` x q_pad int8 planes (plane stride rows_pad*q_pad).
+// B's column exponents and residue planes in one pass (conservative bit
+// budget, OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX); writes
+// ex[0..rows) like launch_col_exp would.
+bool col_residue_fits(int q);
+hipError_t launch_col_residue(const double* X, int rows, int q, long rs, int32_t* ex, const ResidueConsts& c,
+                              int8_t* planes, int rows_pad, int q_pad, hipStream_t st);
 hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad,
                           double* prime, long prime_rs, long prime_ls, hipStream_t st);

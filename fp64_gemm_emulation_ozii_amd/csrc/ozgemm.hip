@@ -630,10 +630,16 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
     for (auto& x : ev) OZ_CHECK(hipEventCreate(&x));
     OZ_CHECK(hipEventRecord(ev[0], g.stream));
   }
-  if ((st = run_scale(m, n, q, s, A, lda, B, ldb, e, f))) return st;
+  // B's exponents come out of its residue pass when the column fits (the
+  // OS II-fast budget needs its norms first, so it keeps two passes)
+  const bool b_one_pass = g.bound != OZGEMM_BOUND_FAST && col_residue_fits(q);
+  if ((st = run_scale(m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
   if (timed) OZ_CHECK(hipEventRecord(ev[1], g.stream));
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, g.stream));
-  OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
+  if (b_one_pass)
+    OZ_CHECK(launch_col_residue(B, n, q, ldb, f, rc, Bres, np, qp, g.stream));
+  else
+    OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
   if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
   SplitChoice split{};
   int cus = 0;

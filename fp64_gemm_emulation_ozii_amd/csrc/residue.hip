@@ -61,6 +61,70 @@ __device__ __forceinline__ double smod_exact_d(double a, double m, double inv) {
   return __builtin_fma(-qf, m, a);
 }
 
+// The s residues of 16 consecutive entries of one row, A' exact integers in
+// a[] (|A'| < 2^kmag), as one 16-byte store per modulus at dst + t plane_stride.
+template <int MODE>  // 0: kmag <= 50, 1: kmag <= 53, 2: kmag > 53
+__device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueConsts& c, int8_t* dst,
+                                                 long plane_stride) {
+  constexpr bool BIG = MODE == 2;
+  double ahi[BIG ? 16 : 1];
+  if (BIG) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      ahi[j] = __builtin_floor(a[j] * 0x1p-32);
+      a[j] = __builtin_fma(ahi[j], -0x1p32, a[j]);  // low part, in [0, 2^32)
+    }
+  }
+
+  if (MODE == 0) {
+    // |A'| < 2^50: A' + 1.5 2^52 is exact, and so is fma(-q, m, A' + 1.5 2^52)
+    // = 1.5 2^52 + r, whose low 32 bits are r in two's complement
+    // (|r| <= 128 < 2^51); no conversion instruction is needed
+    double am[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) am[j] = a[j] + 0x1.8p52;
+    for (int t = 0; t < c.s; ++t) {
+      const double md = (double)c.m[t], inv = c.inv[t];
+      uint32_t rb[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const double qf = __builtin_floor(__builtin_fma(a[j], inv, 0.5));
+        rb[j] = (uint32_t)__builtin_bit_cast(uint64_t, __builtin_fma(-qf, md, am[j]));
+      }
+      uint4 out;
+      out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
+      out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
+      out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
+      out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
+      *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
+    }
+    return;
+  }
+  for (int t = 0; t < c.s; ++t) {
+    const int m = c.m[t];
+    const double inv = c.inv[t];
+    const int lo = c.lo[t], hi = c.hi[t];
+    uint32_t rb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int ri;
+      if (BIG) {
+        const double rh = smod_exact_d(ahi[j], (double)m, inv);
+        ri = smod_small<false>(__builtin_fma(rh, c.c32[t], a[j]), m, inv, lo, hi);
+      } else {
+        ri = smod_small<true>(a[j], m, inv, lo, hi);
+      }
+      rb[j] = (uint32_t)ri;
+    }
+    uint4 out;
+    out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
+    out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
+    out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
+    out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
+    *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
+  }
+}
+
 template <bool ROWS_CONTIG, int MODE>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
 __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
                                                        long ls, const int32_t* __restrict__ ex, ResidueConsts c,
@@ -138,66 +202,69 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
     }
   }
 
-  constexpr bool BIG = MODE == 2;
-  double ahi[BIG ? 16 : 1];
-  if (BIG) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      ahi[j] = __builtin_floor(a[j] * 0x1p-32);
-      a[j] = __builtin_fma(ahi[j], -0x1p32, a[j]);  // low part, in [0, 2^32)
-    }
-  }
-
-  int8_t* dst = planes + (long)grow * q_pad + l0 + cseg;
-  if (MODE == 0) {
-    // |A'| < 2^50: A' + 1.5 2^52 is exact, and so is fma(-q, m, A' + 1.5 2^52)
-    // = 1.5 2^52 + r, whose low 32 bits are r in two's complement
-    // (|r| <= 128 < 2^51); no conversion instruction is needed
-    double am[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) am[j] = a[j] + 0x1.8p52;
-    for (int t = 0; t < c.s; ++t) {
-      const double md = (double)c.m[t], inv = c.inv[t];
-      uint32_t rb[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const double qf = __builtin_floor(__builtin_fma(a[j], inv, 0.5));
-        rb[j] = (uint32_t)__builtin_bit_cast(uint64_t, __builtin_fma(-qf, md, am[j]));
-      }
-      uint4 out;
-      out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
-      out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
-      out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
-      out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
-      *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
-    }
-    return;
-  }
-  for (int t = 0; t < c.s; ++t) {
-    const int m = c.m[t];
-    const double inv = c.inv[t];
-    const int lo = c.lo[t], hi = c.hi[t];
-    uint32_t rb[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      int ri;
-      if (BIG) {
-        const double rh = smod_exact_d(ahi[j], (double)m, inv);
-        ri = smod_small<false>(__builtin_fma(rh, c.c32[t], a[j]), m, inv, lo, hi);
-      } else {
-        ri = smod_small<true>(a[j], m, inv, lo, hi);
-      }
-      rb[j] = (uint32_t)ri;
-    }
-    uint4 out;
-    out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
-    out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
-    out.z = pack_bytes(rb[8], rb[9], rb[10], rb[11]);
-    out.w = pack_bytes(rb[12], rb[13], rb[14], rb[15]);
-    *reinterpret_cast<uint4*>(dst + (long)t * plane_stride) = out;
-  }
+  write_residues16<MODE>(a, c, planes + (long)grow * q_pad + l0 + cseg, plane_stride);
 }
 
+
+// B in one pass (Ozaki II notes §15: scaling, truncation, modulo and packing
+// fused): one block per row j of the B planes, i.e. per column of B, which
+// is contiguous.  The block loads the column into LDS (coalesced, all loads
+// in flight before any is used), takes the frexp exponent of its largest
+// |b_lj| (written to ex[j], exactly as the scale step computes it), and then
+// converts it like residue_kernel: each thread owns 16 consecutive entries
+// and writes one 16-byte store per modulus.  One pad double after every 16
+// makes those 16-entry reads conflict-free (64 lanes touch 32 distinct
+// 8-byte bank pairs twice).  Rows j >= rows and entries l >= q are padding
+// and get zero residues.
+constexpr int COL_QMAX = OZGEMM_ONE_PASS_Q_MAX;  // longest column held
+constexpr int COL_LDS = COL_QMAX + COL_QMAX / 16;  // doubles, with the pads
+
+template <int MODE>
+__global__ __launch_bounds__(256) void col_residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
+                                                           int32_t* __restrict__ ex, ResidueConsts c,
+                                                           int8_t* __restrict__ planes, long plane_stride,
+                                                           int q_pad) {
+  __shared__ double col[COL_LDS];
+  __shared__ uint64_t wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = blockIdx.x;
+  int e = 0;
+  bool zero_row = true;
+  if (j < rows) {  // uniform across the block
+    const double* src = X + (long)j * rs;
+    double v[COL_QMAX / 256];
+#pragma unroll
+    for (int i = 0; i < COL_QMAX / 256; ++i) {
+      const int l = tid + 256 * i;
+      v[i] = l < q ? __builtin_nontemporal_load(src + l) : 0.0;
+    }
+    uint64_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < COL_QMAX / 256; ++i) {
+      const int l = tid + 256 * i;
+      mx = umax64(mx, abs_bits(v[i]));
+      col[l + (l >> 4)] = v[i];
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = umax64(mx, (uint64_t)__shfl_xor((unsigned long long)mx, off, 64));
+    if (lane == 0) wmax[wave] = mx;
+    __syncthreads();
+    e = exponent_of_bits(umax64(umax64(wmax[0], wmax[1]), umax64(wmax[2], wmax[3])));
+    if (tid == 0) ex[j] = e;
+    zero_row = (e == OZGEMM_EXP_NONFINITE);
+  }
+  __syncthreads();
+  const int shift = zero_row ? 0 : c.k - e;
+  for (int seg = tid; seg < q_pad / 16; seg += 256) {
+    double a[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const double x = col[17 * seg + jj];  // entry 16 seg + jj, past its pads
+      const double t = __builtin_trunc(__builtin_ldexp(x, shift));
+      a[jj] = zero_row ? 0.0 : t + 0.0;  // + 0.0 turns -0.0 into +0.0
+    }
+    write_residues16<MODE>(a, c, planes + (long)j * q_pad + 16 * seg, plane_stride);
+  }
+}
 }  // namespace
 
 hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
@@ -222,6 +289,27 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
     else OZ_RES_LAUNCH(false, 2);
   }
 #undef OZ_RES_LAUNCH
+  return hipGetLastError();
+}
+
+// Shorter columns keep the two-pass path: a block per column of under 4096
+// entries is too little work for its 68 KB of LDS, and the separate scale
+// read of such a B is cheap (measured at 16384^2 x 1024: the one-pass B took
+// 0.29 ms against 0.14 + 0.02 ms for the two passes).
+bool col_residue_fits(int q) { return q >= OZGEMM_ONE_PASS_Q_MIN && q <= COL_QMAX; }
+
+hipError_t launch_col_residue(const double* X, int rows, int q, long rs, int32_t* ex, const ResidueConsts& c,
+                              int8_t* planes, int rows_pad, int q_pad, hipStream_t st) {
+  if (!col_residue_fits(q) || q_pad > COL_QMAX || q_pad % 16 || rows_pad < rows) return hipErrorInvalidValue;
+  const long plane_stride = (long)rows_pad * q_pad;
+  const int mode = c.kmag <= 50 ? 0 : (c.kmag <= 53 ? 1 : 2);
+#define OZ_COL_LAUNCH(MD)                                                                                    \
+  hipLaunchKernelGGL((col_residue_kernel<MD>), dim3(rows_pad), dim3(256), 0, st, X, rows, q, rs, ex, c, planes, \
+                     plane_stride, q_pad)
+  if (mode == 0) OZ_COL_LAUNCH(0);
+  else if (mode == 1) OZ_COL_LAUNCH(1);
+  else OZ_COL_LAUNCH(2);
+#undef OZ_COL_LAUNCH
   return hipGetLastError();
 }
 

@@ -25,22 +25,6 @@
 
 namespace oz {
 
-__device__ __forceinline__ uint64_t abs_bits(double x) {
-  return (uint64_t)__double_as_longlong(x) & 0x7fffffffffffffffull;
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// frexp exponent of the double whose |.| bit pattern is b.
-__device__ __forceinline__ int32_t exponent_of_bits(uint64_t b) {
-  if (b == 0) return 0;
-  if (b >= 0x7ff0000000000000ull) return OZGEMM_EXP_NONFINITE;
-  int biased = (int)(b >> 52);
-  if (biased > 0) return biased - 1022;         // value in [2^(E-1023), 2^(E-1022))
-  int top = 63 - __clzll((long long)b);          // subnormal: mant * 2^-1074
-  return top - 1073;
-}
-
 __global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __restrict__ A, int m, int q,
                                                                long lda, int chunk,
                                                                uint64_t* __restrict__ pmax, int m_stride) {

@@ -25,6 +25,8 @@ OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_Q_MAX = 1 << 27
 OZGEMM_MAX_ROWS = 2096896  # 2^21 - 256
+OZGEMM_ONE_PASS_Q_MIN = 4096  # B read once by ozgemm_dgemm for q in [MIN, MAX] (conservative budget)
+OZGEMM_ONE_PASS_Q_MAX = 8192
 OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
 OZGEMM_BOUND_CONSERVATIVE = 0
 OZGEMM_BOUND_FAST = 1

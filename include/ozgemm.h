@@ -63,6 +63,8 @@ extern "C" {
 #define OZGEMM_Q_MAX   (1 << 27)      /* largest supported inner dimension */
 #define OZGEMM_MAX_ROWS 2096896       /* largest m and n: 2^21 - 256, so that the rows padded to 256 form at most 65535 tiles of 32 */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
+#define OZGEMM_ONE_PASS_Q_MIN 4096    /* ozgemm_dgemm reads B once for Q_MIN <= q <= Q_MAX (conservative budget) */
+#define OZGEMM_ONE_PASS_Q_MAX 8192
 
 /* Bit budgets of Scheme II (ozgemm_set_bound) */
 #define OZGEMM_BOUND_CONSERVATIVE 0 /* c_max <= q 2^(k_A + k_B), k_A = k_B = k (Ozaki II notes §5) */
@@ -112,6 +114,11 @@ const char *ozgemm_strerror(int status);
  * C must not overlap A or B (-8).  Requires m <= max_m, n <= max_n,
  * q <= max_q, s <= s_max of the configuration (OZGEMM_RANGE otherwise).
  * Enqueues the scale, residue, int8 GEMM and CRT kernels on the stream.
+ * Under the conservative budget with OZGEMM_ONE_PASS_Q_MIN <= q <=
+ * OZGEMM_ONE_PASS_Q_MAX, B's column exponents are taken inside its residue
+ * pass, so B is read once; A is read twice (its row maxima need every column
+ * first).  Shorter columns keep two passes, whose first is cheap there.  The
+ * results are the same as those of the stage entry points.
  * The first call after ozgemm_config also copies a 16 KB constant table
  * into the workspace (a blocking host-to-device copy) and queries the
  * device's compute-unit count; later calls only enqueue kernels, so they can

@@ -246,3 +246,37 @@ def test_long_inner_dimension_refuses_int32_planes():
     finally:
         L.ozgemm_free()
         configure(1536, 1536, 1536, 20)
+
+
+@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MAX,
+                               L.OZGEMM_ONE_PASS_Q_MAX + 1])
+def test_b_one_pass_boundary(q):
+    """For OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX ozgemm_dgemm
+    takes B's column exponents inside its residue pass (B read once);
+    outside that range the scale step does.
+    Columns of B that are all zero, subnormal only, near overflow or hold a
+    NaN exercise that exponent; C must equal the oracle bit for bit either
+    way, and the stage entry points (always two passes) must agree."""
+    import torch
+    m, n = 70, 300
+    A, B = hpl_like(m, q, n, 1.0, seed=q)
+    B[:, 3] = 0.0
+    B[:, 5] *= 2.0 ** -1060          # every entry subnormal
+    B[:, 7] *= 2.0 ** 1000
+    B[q // 2, 11] = np.nan
+    B[q - 1, 13] = 2.0 ** -1074      # the column maximum sits in the last entry
+    B[:q - 1, 13] = 2.0 ** -1075 * 0.0
+    L.ozgemm_free()
+    configure(256, 512, q, 20)
+    try:
+        log(f"one-pass boundary q={q}")
+        C, _ = run_dgemm(A, B, 14)
+        g = run_stages(A, B, 14, want_ct=False, want_prime=False)
+    finally:
+        L.ozgemm_free()
+        torch.cuda.empty_cache()
+        configure(1536, 1536, 1536, 20)
+    ref = oz.dgemm(A, B, 14, stages=True)
+    assert same_doubles(C, ref[0]), first_diff(C, ref[0])
+    assert np.array_equal(g["f"], ref[1]["f"]), first_diff(g["f"], ref[1]["f"])
+    assert same_doubles(g["C"], C)
