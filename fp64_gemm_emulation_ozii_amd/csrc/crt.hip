@@ -78,13 +78,23 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ rt
     // 2. one row at a time (keeps the live registers of a single
     //    reconstruction, so more wavefronts fit on a SIMD)
     double* out = C + (long)j * ldc + i0;
+    double res[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      double res = W40 ? reconstruct40<(L <= 3 ? L : 3)>(S[u], c.K, ei[u] + fj - 2 * c.k)
-                       : reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
-      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res = __builtin_nan("");
-      if (i0 + u < m) out[u] = res;
+      res[u] = W40 ? reconstruct40<(L <= 3 ? L : 3)>(S[u], c.K, ei[u] + fj - 2 * c.k)
+                   : reconstruct_limbs<L>(S[u], c.K, ei[u] + fj - 2 * c.k);
+      if (ei[u] == OZGEMM_EXP_NONFINITE || fj == OZGEMM_EXP_NONFINITE) res[u] = __builtin_nan("");
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // four rows as two 16-byte stores where the column allows it (the same
+    // for every lane of a wave: i0 is a multiple of 4)
+    if (i0 + 3 < m && ((reinterpret_cast<uintptr_t>(out) & 15) == 0)) {
+      reinterpret_cast<double2*>(out)[0] = double2{res[0], res[1]};
+      reinterpret_cast<double2*>(out)[1] = double2{res[2], res[3]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u < m) out[u] = res[u];
     }
 #pragma unroll
     for (int t = 0; t < 4 * NG; ++t) rr[t] = rn[t];
