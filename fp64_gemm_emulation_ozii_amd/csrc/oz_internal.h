@@ -116,6 +116,12 @@ hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m
 hipError_t launch_s1_rowmax(const double* X, int rows, int q, long rs, long ls, int rows_pad, int q_pad,
                             uint64_t* pmax, hipStream_t st);
 hipError_t launch_s1_grid(const uint64_t* pmax, int rows_pad, int nchunks, int beta, int32_t* gout, hipStream_t st);
+// Scheme I split of rows held in LDS (rows contiguous in memory, as the rows
+// of B are), one pass for all k slices; same grids and slices as
+// launch_s1_rowmax + launch_s1_grid + launch_s1_split.
+bool s1_row_split_fits(int q);
+hipError_t launch_s1_row_split(const double* X, int rows, int q, long rs, int rows_pad, int q_pad, int variant, int k,
+                               int beta, int32_t* g, int8_t* planes, hipStream_t st);
 hipError_t launch_s1_split(const double* X, int rows, int q, long rs, long ls, const int32_t* g, int rows_pad,
                            int q_pad, int variant, int pass, int k, int beta, int8_t* planes, uint64_t* pmax,
                            hipStream_t st);

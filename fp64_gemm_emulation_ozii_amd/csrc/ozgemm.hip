@@ -495,6 +495,11 @@ int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const d
     int32_t* gr;
   } sides[2] = {{A, m, 1, (long)lda, L.mp, Asl, gA}, {B, n, (long)ldb, 1, L.np, Bsl, gB}};
   for (const Side& sd : sides) {
+    if (sd.ls == 1 && s1_row_split_fits(q)) {  // rows contiguous and short enough to hold: one pass
+      OZ_CHECK(launch_s1_row_split(sd.X, sd.rows, q, sd.rs, sd.rp, L.qp, variant, k, L.beta, sd.gr, sd.sl,
+                                   g.stream));
+      continue;
+    }
     OZ_CHECK(launch_s1_rowmax(sd.X, sd.rows, q, sd.rs, sd.ls, sd.rp, L.qp, pmax, g.stream));
     OZ_CHECK(launch_s1_grid(pmax, sd.rp, L.nch, L.beta, sd.gr, g.stream));
     if (variant == OZGEMM_S1_RN) {

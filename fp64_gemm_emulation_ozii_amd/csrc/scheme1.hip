@@ -158,6 +158,93 @@ __global__ __launch_bounds__(256) void s1_split_kernel(const double* __restrict_
   }
 }
 
+// One pass for a row held in LDS (the rows of B: a column of B is
+// contiguous), for OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX.  The
+// block loads the row, takes its maximum for the first grid, then writes the
+// k slices in one sweep; with the RN split the grid of slice p + 1 comes from
+// a block reduction of the residual left by slice p.  Grids, slices and the
+// non-finite and padding cases are those of the rowmax + grid + split passes
+// above (one pad double after every 16 entries keeps the 16-entry reads
+// conflict-free; each thread keeps its two segments in registers).
+constexpr int ROW_QMAX = OZGEMM_ONE_PASS_Q_MAX;
+constexpr int ROW_LDS = ROW_QMAX + ROW_QMAX / 16;
+
+template <int MODE>  // 1: RN, 2: Hybrid
+__global__ __launch_bounds__(256) void s1_row_split_kernel(const double* __restrict__ X, int rows, int q, long rs,
+                                                            int rows_pad, int q_pad, int k, int beta,
+                                                            int32_t* __restrict__ g, int8_t* __restrict__ planes,
+                                                            long plane_stride) {
+  __shared__ double row[ROW_LDS];
+  __shared__ uint64_t wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rr = blockIdx.x;
+  const bool live = rr < rows;  // uniform across the block
+  uint64_t mx = 0;
+  if (live) {
+    const double* src = X + (long)rr * rs;
+    double v[ROW_QMAX / 256];
+#pragma unroll
+    for (int i = 0; i < ROW_QMAX / 256; ++i) {
+      const int l = tid + 256 * i;
+      v[i] = l < q ? src[l] : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < ROW_QMAX / 256; ++i) {
+      const int l = tid + 256 * i;
+      mx = umax64(mx, abs_bits(v[i]));
+      row[l + (l >> 4)] = v[i];
+    }
+  }
+  // maximum over the block (every thread calls it; it also orders the LDS)
+  auto block_max = [&](uint64_t x) -> uint64_t {
+    for (int off = 32; off > 0; off >>= 1) x = umax64(x, (uint64_t)__shfl_xor((unsigned long long)x, off, 64));
+    __syncthreads();  // the previous reduction's readers are done with wmax
+    if (lane == 0) wmax[wave] = x;
+    __syncthreads();
+    return umax64(umax64(wmax[0], wmax[1]), umax64(wmax[2], wmax[3]));
+  };
+  auto grid_of = [&](uint64_t b) -> int {  // as s1_grid_kernel
+    if (b >= 0x7ff0000000000000ull) return OZGEMM_EXP_NONFINITE;
+    return b == 0 ? 0 : ceil_log2_bits(b) + 1 - beta;
+  };
+  const int g0 = grid_of(block_max(mx));
+  const bool bad = (g0 == OZGEMM_EXP_NONFINITE);
+  if (tid == 0) g[rr] = g0;
+
+  constexpr int NSEG = ROW_QMAX / 16 / 256;  // 16-entry segments per thread
+  double a[NSEG][16];
+#pragma unroll
+  for (int u = 0; u < NSEG; ++u) {
+    const int seg = tid + 256 * u;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      a[u][jj] = (live && !bad && 16 * seg < q_pad) ? row[17 * seg + jj] : 0.0;  // entry 16 seg + jj
+  }
+  int gp = bad ? 0 : g0;
+  for (int p = 0; p < k; ++p) {
+    if (MODE == 2) gp = (bad ? 0 : g0) - beta * p;
+    uint64_t rmx = 0;
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int seg = tid + 256 * u;
+      if (16 * seg >= q_pad) continue;
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int nn = (int)peel(a[u][jj], gp);
+        packed[jj >> 2] |= ((uint32_t)nn & 0xffu) << (8 * (jj & 3));
+        if (MODE == 1) rmx = umax64(rmx, abs_bits(a[u][jj]));
+      }
+      *reinterpret_cast<uint4*>(planes + (long)p * plane_stride + (long)rr * q_pad + 16 * seg) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+    if (MODE == 1 && p + 1 < k) {
+      gp = grid_of(block_max(rmx));
+      if (tid == 0) g[(long)(p + 1) * rows_pad + rr] = gp;
+    }
+  }
+}
+
 // Grid exponent of each row from the partial maxima: E + 1 - beta with
 // E = ceil(log2 max); 0 for a zero row; OZGEMM_EXP_NONFINITE when the row
 // holds Inf or NaN.
@@ -325,6 +412,21 @@ hipError_t launch_s1_split(const double* X, int rows, int q, long rs, long ls, c
     else OZ_S1_LAUNCH(false, 2);
   }
 #undef OZ_S1_LAUNCH
+  return hipGetLastError();
+}
+
+bool s1_row_split_fits(int q) { return q >= OZGEMM_ONE_PASS_Q_MIN && q <= ROW_QMAX; }
+
+hipError_t launch_s1_row_split(const double* X, int rows, int q, long rs, int rows_pad, int q_pad, int variant, int k,
+                               int beta, int32_t* g, int8_t* planes, hipStream_t st) {
+  if (!s1_row_split_fits(q) || q_pad > ROW_QMAX || q_pad % 16 || rows_pad < rows) return hipErrorInvalidValue;
+  const long plane_stride = (long)rows_pad * q_pad;
+  if (variant == OZGEMM_S1_RN)
+    hipLaunchKernelGGL((s1_row_split_kernel<1>), dim3(rows_pad), dim3(256), 0, st, X, rows, q, rs, rows_pad, q_pad,
+                       k, beta, g, planes, plane_stride);
+  else
+    hipLaunchKernelGGL((s1_row_split_kernel<2>), dim3(rows_pad), dim3(256), 0, st, X, rows, q, rs, rows_pad, q_pad,
+                       k, beta, g, planes, plane_stride);
   return hipGetLastError();
 }
 

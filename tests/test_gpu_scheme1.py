@@ -165,6 +165,30 @@ def test_inner_dimension_beyond_int8_scheme2_limit(variant):
 
 
 @pytest.mark.parametrize("variant", ["rn", "hybrid"])
+@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MAX,
+                               L.OZGEMM_ONE_PASS_Q_MAX + 1])
+def test_row_split_one_pass_boundary(variant, q):
+    """For OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX the rows of B
+    (columns, contiguous in memory) are split in one pass from LDS; outside
+    that range by the rowmax, grid and split passes.  Columns of B that are
+    zero, subnormal only, near overflow, hold a NaN, or whose residual
+    vanishes after one slice check grids, slices, products and C bit for
+    bit against the oracle either way."""
+    m, n, k = 24, 40, 6
+    A, B = hpl_like(m, q, n, 1.0, seed=q + 17)
+    B[:, 2] = 0.0
+    B[:, 4] *= 2.0 ** -1060
+    B[:, 6] *= 2.0 ** 1000
+    B[q // 3, 8] = np.nan
+    B[:, 10] = 0.0
+    B[::7, 10] = 3.0                 # exact in one slice: the residual is zero after it
+    reconfigure(m, n, q, k, VARIANTS[variant])
+    log(f"scheme1 {variant} one-pass boundary q={q}")
+    check_parity(A, B, k, variant)
+    reconfigure(1024, 1024, 1024, 8, L.OZGEMM_S1_RN)
+
+
+@pytest.mark.parametrize("variant", ["rn", "hybrid"])
 @pytest.mark.parametrize("size,k", [(1024, 8), (4096, 8), (4096, 5)])
 def test_large_sampled_block(variant, size, k):
     import torch
