@@ -13,8 +13,9 @@
 // Operands are K-contiguous int8 planes: A_t is m_pad x q_pad (row i at
 // i*q_pad), B_t is n_pad x q_pad (column j of B at j*q_pad), so each product
 // is A_t B_t^T.  A block computes a BM x BN output tile with four wavefronts
-// (2 x 2), each owning (BM/2) x (BN/2) built from 32x32 int32 tiles of
-// v_mfma_i32_32x32x32_i8.  In the multi-product form an output plane is the
+// (2 x 2), each owning (BM/2) x (BN/2) built from 16x16 int32 tiles of
+// v_mfma_i32_16x16x64_i8 (residue-only products) or 32x32 tiles of
+// v_mfma_i32_32x32x32_i8 (int32 output).  In the multi-product form an output plane is the
 // sum of `count` products (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one
 // long K loop.
 //
