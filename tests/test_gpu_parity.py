@@ -248,8 +248,8 @@ def test_long_inner_dimension_refuses_int32_planes():
         configure(1536, 1536, 1536, 20)
 
 
-@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MAX,
-                               L.OZGEMM_ONE_PASS_Q_MAX + 1])
+@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MIN + 37,
+                               L.OZGEMM_ONE_PASS_Q_MAX, L.OZGEMM_ONE_PASS_Q_MAX + 1])
 def test_b_one_pass_boundary(q):
     """For OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX ozgemm_dgemm
     takes B's column exponents inside its residue pass (B read once);

@@ -165,8 +165,8 @@ def test_inner_dimension_beyond_int8_scheme2_limit(variant):
 
 
 @pytest.mark.parametrize("variant", ["rn", "hybrid"])
-@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MAX,
-                               L.OZGEMM_ONE_PASS_Q_MAX + 1])
+@pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MIN + 37,
+                               L.OZGEMM_ONE_PASS_Q_MAX, L.OZGEMM_ONE_PASS_Q_MAX + 1])
 def test_row_split_one_pass_boundary(variant, q):
     """For OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX the rows of B
     (columns, contiguous in memory) are split in one pass from LDS; outside
