@@ -13,7 +13,8 @@ against the oracles.
 Every C must equal the oracle's bit for bit (NaN positions alike) and, for
 Scheme II, lie within 2^-50 (|A||B|)_ij of it.  The Scheme I sweep draws
 16 cases of the same kinds with k in 2..10 slices and the RN or the Hybrid
-variant.
+variant.  12 more Scheme II cases draw q from [4000, 9000), around the range
+where B's exponents are taken in its residue pass.
 """
 import numpy as np
 import pytest
@@ -99,6 +100,52 @@ def test_random_case(case):
         finite_cols = np.isfinite(B).all(axis=0)
         sub = np.ix_(finite_rows, finite_cols)
         assert within_tolerance(C[sub], ref[sub], A[finite_rows], B[:, finite_cols])
+
+
+# ---- 12 more Scheme II cases with q around the one-pass range of B ----
+
+def draw_one_pass_cases(count: int, seed: int = 20261204):
+    """q in [4000, 9000): mostly inside [OZGEMM_ONE_PASS_Q_MIN,
+    OZGEMM_ONE_PASS_Q_MAX], where ozgemm_dgemm takes B's exponents in its
+    residue pass, with ragged K; the rest on either side of it."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        m = int(rng.integers(1, MAX_M + 1))
+        n = int(rng.integers(1, MAX_N + 1))
+        q = int(rng.integers(4000, 9000))
+        s = int(rng.integers(10, 21))
+        bound = "fast" if rng.random() < 0.25 else "conservative"
+        M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+        if bound == "conservative" and oz.kbits(M, q) < 1:
+            continue
+        phi = float(rng.choice([0.0, 0.5, 1.0, 2.0]))
+        pads = tuple(int(rng.integers(0, 4)) for _ in range(3))
+        special = str(rng.choice(["none", "zero", "tiny", "huge", "nonfinite"]))
+        cases.append((m, n, q, s, bound, phi, pads, special, int(rng.integers(0, 2**31))))
+    return cases
+
+
+ONE_PASS_CASES = draw_one_pass_cases(12)
+
+
+@pytest.mark.parametrize("case", range(len(ONE_PASS_CASES)))
+def test_random_one_pass_range_case(case):
+    m, n, q, s, bound, phi, pads, special, seed = ONE_PASS_CASES[case]
+    log(f"random one-pass-range case {case}: m={m} n={n} q={q} s={s} bound={bound} phi={phi} pads={pads} "
+        f"special={special}")
+    A, B = make_inputs(m, n, q, phi, special, seed)
+    L.ozgemm_free()
+    configure(MAX_M, MAX_N, 9000, 20)
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if bound == "fast" else L.OZGEMM_BOUND_CONSERVATIVE)
+    try:
+        C, _ = run_dgemm(A, B, s, lda=m + pads[0], ldb=q + pads[1], ldc=m + pads[2])
+    finally:
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
+        L.ozgemm_free()
+        configure(MAX_M, MAX_N, MAX_Q, 20)
+    ref = oz.dgemm(A, B, s, bound=bound)
+    assert same_doubles(C, ref), first_diff(C, ref)
 
 
 # ---- Scheme I: 16 cases of the same kinds, k in 2..10, RN or Hybrid ----
