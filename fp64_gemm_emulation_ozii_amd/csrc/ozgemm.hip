@@ -235,7 +235,7 @@ struct Layout {
   size_t consts, pmax, e, f, ares, bres, rt, rt_bytes, total;
 };
 
-Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
+Layout make_layout(int max_m, int max_n, int max_q, int s_max, bool split_region = true) {
   const size_t mp = round_up((size_t)std::max(max_m, 1), ROW_PAD);
   const size_t np = round_up((size_t)std::max(max_n, 1), ROW_PAD);
   const size_t qp = round_up((size_t)std::max(max_q, 1), K_PAD);
@@ -254,7 +254,7 @@ Layout make_layout(int max_m, int max_n, int max_q, int s_max) {
   L.bres = take((size_t)s_max * np * qp);
   // product residues; also the K part planes of skinny products (gemm_grid.h)
   L.rt_bytes = std::max((size_t)s_max * mp * np,
-                        (size_t)split_region_bytes((int)(qp / K_PAD), ROW_PAD * ROW_PAD));
+                        split_region ? (size_t)split_region_bytes((int)(qp / K_PAD), ROW_PAD * ROW_PAD) : 0);
   L.rt = take(L.rt_bytes);
   L.total = off;
   return L;
@@ -275,6 +275,21 @@ struct State {
   std::string hip_err;
 };
 State g;
+
+// Where one Scheme II call keeps its intermediates and launches its kernels:
+// the configured workspace and stream (ozgemm_dgemm and the stage entry
+// points).
+struct Ctx {
+  char* ws;
+  Layout lay;
+  int row_stride;  // stride of the partial row maxima (rows padded like the layout's largest m)
+  hipStream_t stream;
+  int bound;
+};
+
+Ctx config_ctx() {
+  return Ctx{g.ws, g.lay, (int)round_up((size_t)std::max(g.max_m, 1), ROW_PAD), g.stream, g.bound};
+}
 
 constexpr size_t TIMING_MAX_CALLS = 4096;
 // the residue and Scheme I split grids index tiles of 32 rows in grid.y
@@ -311,10 +326,10 @@ int device_cus(int* cus) {
 
 // K parts of a residue-only Scheme II product of padded size mp x np x qp
 // (gemm_grid.h); their planes go to the workspace's product region.
-int product_split(int mp, int np, int qp, int s, SplitChoice* out, int* cus) {
+int product_split(const Layout& lay, int mp, int np, int qp, int s, SplitChoice* out, int* cus) {
   const int st = device_cus(cus);
   if (st) return st;
-  const long cap = (long)(g.lay.rt_bytes / ((size_t)mp * np));
+  const long cap = (long)(lay.rt_bytes / ((size_t)mp * np));
   *out = choose_splits((mp / ROW_PAD) * (np / ROW_PAD), s, qp / K_PAD, *cus, cap);
   return 0;
 }
@@ -364,11 +379,20 @@ int check_common(int m, int n, int q, const double* A, int lda, const double* B,
   return 0;
 }
 
+// Limits of the method and of the active bit budget (any entry point).
+int check_method_range(int q, int s) {
+  if (q > OZGEMM_Q_MAX) return OZGEMM_RANGE;
+  if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+  if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
+  return 0;
+}
+
 int check_range(int m, int n, int q, int s) {
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
   if (q > OZGEMM_Q_MAX) return OZGEMM_RANGE;
   if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+  if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
   return 0;
 }
 
@@ -380,23 +404,23 @@ int nchunks_for(int m, int q) {
   return std::max(nch, 1);
 }
 
-int run_scale(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, int32_t* e,
-              int32_t* f) {
-  const int mp = (int)round_up((size_t)std::max(g.max_m, 1), ROW_PAD);
-  uint64_t* pmax = reinterpret_cast<uint64_t*>(g.ws + g.lay.pmax);
+int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb,
+              int32_t* e, int32_t* f) {
+  const int mp = x.row_stride;
+  uint64_t* pmax = reinterpret_cast<uint64_t*>(x.ws + x.lay.pmax);
   const int nch = nchunks_for(m, q);
-  const bool fast = g.bound == OZGEMM_BOUND_FAST;
+  const bool fast = x.bound == OZGEMM_BOUND_FAST;
   int ka = 0, kb = 0;
   if (fast) fast_budget(s, &ka, &kb);
   const int kbase = std::max(ka, kb);
   if (m > 0) {
-    OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, g.stream));
-    OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, g.stream));
-    if (fast) OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, g.stream));
+    OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, x.stream));
+    OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
+    if (fast) OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, x.stream));
   }
   if (n > 0) {
-    OZ_CHECK(launch_col_exp(B, q, n, ldb, f, g.stream));
-    if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, g.stream));
+    OZ_CHECK(launch_col_exp(B, q, n, ldb, f, x.stream));
+    if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
   }
   return 0;
 }
@@ -517,6 +541,67 @@ int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const d
   return 0;
 }
 
+// Argument checks of ozgemm_dgemm (BLAS style).
+int check_dgemm_args(int m, int n, int q, const double* A, int lda, const double* B, int ldb, const double* C,
+                     int ldc, int s) {
+  const int st = check_common(m, n, q, A, lda, B, ldb);
+  if (st) return st;
+  if (C == nullptr && m > 0 && n > 0) return -8;
+  if (ldc < std::max(1, m)) return -9;
+  if (s < 1 || s > OZGEMM_S_MAX) return -10;
+  if (m > 0 && n > 0) {
+    const size_t cb = mat_bytes(m, n, ldc);
+    if (overlaps(C, cb, A, mat_bytes(m, q, lda)) || overlaps(C, cb, B, mat_bytes(q, n, ldb))) return -8;
+  }
+  return 0;
+}
+
+// The four steps of one Scheme II call (Ozaki II notes §7) on the buffers of
+// x: scale, residues, the int8 products with their reduction mod m_t, and the
+// CRT with unscaling.  wtab is the device table of the W_t limbs for s.
+// With ev, HIP events are recorded around the phases.
+int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const double* A, int lda, const double* B,
+              int ldb, double* C, int ldc, int s, std::array<hipEvent_t, 5>* ev) {
+  if (q == 0) {
+    OZ_CHECK(launch_fill_zero(C, m, n, ldc, x.stream));
+    return OZGEMM_OK;
+  }
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  int32_t* e = reinterpret_cast<int32_t*>(x.ws + x.lay.e);
+  int32_t* f = reinterpret_cast<int32_t*>(x.ws + x.lay.f);
+  int8_t* Ares = reinterpret_cast<int8_t*>(x.ws + x.lay.ares);
+  int8_t* Bres = reinterpret_cast<int8_t*>(x.ws + x.lay.bres);
+  uint8_t* rt = reinterpret_cast<uint8_t*>(x.ws + x.lay.rt);
+
+  ResidueConsts rc;
+  GemmConsts gc;
+  CrtConsts cc;
+  make_consts(s, q, x.bound, &rc, &gc, &cc);
+  cc.wtab = wtab;
+  int st = 0;
+  if (ev) OZ_CHECK(hipEventRecord((*ev)[0], x.stream));
+  // B's exponents come out of its residue pass when the column fits (the
+  // OS II-fast budget needs its norms first, so it keeps two passes)
+  const bool b_one_pass = x.bound != OZGEMM_BOUND_FAST && col_residue_fits(q);
+  if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
+  if (ev) OZ_CHECK(hipEventRecord((*ev)[1], x.stream));
+  OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
+  if (b_one_pass)
+    OZ_CHECK(launch_col_residue(B, n, q, ldb, f, rc, Bres, np, qp, x.stream));
+  else
+    OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, x.stream));
+  if (ev) OZ_CHECK(hipEventRecord((*ev)[2], x.stream));
+  SplitChoice split{};
+  int cus = 0;
+  if ((st = product_split(x.lay, mp, np, qp, s, &split, &cus))) return st;
+  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, split, rt, cus, x.stream));
+  if (ev) OZ_CHECK(hipEventRecord((*ev)[3], x.stream));
+  OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, x.stream));
+  if (ev) OZ_CHECK(hipEventRecord((*ev)[4], x.stream));
+  return OZGEMM_OK;
+}
+
 }  // namespace
 }  // namespace oz
 
@@ -573,7 +658,9 @@ const char* ozgemm_strerror(int status) {
   }
   switch (status) {
     case OZGEMM_NOT_CONFIGURED: return "ozgemm_config has not been called";
-    case OZGEMM_RANGE: return "problem outside the supported range (q >= 2^17, k < 1, or above the configured maximum)";
+    case OZGEMM_RANGE:
+      return "problem outside the supported range (q > 2^27, k < 1 under the conservative budget, q >= 2^23 under "
+             "OS II-fast, int32 product planes asked for at q >= 2^17, or a size above the configured maximum)";
     case OZGEMM_WORKSPACE_TOO_SMALL: return "workspace smaller than ozgemm_workspace_bytes";
     case OZGEMM_HIP_ERROR:
       msg = "HIP error: " + g.hip_err;
@@ -601,62 +688,23 @@ int ozgemm_plane_dims(int m, int n, int q, int* m_pad, int* n_pad, int* q_pad) {
 
 int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B, int ldb, double* C, int ldc,
                  int s) {
-  int st = check_common(m, n, q, A, lda, B, ldb);
+  int st = check_dgemm_args(m, n, q, A, lda, B, ldb, C, ldc, s);
   if (st) return st;
-  if (C == nullptr && m > 0 && n > 0) return -8;
-  if (ldc < std::max(1, m)) return -9;
-  if (s < 1 || s > OZGEMM_S_MAX) return -10;
   if ((st = check_range(m, n, q, s))) return st;
   if (m == 0 || n == 0) return OZGEMM_OK;
-  const size_t cb = mat_bytes(m, n, ldc);
-  if (overlaps(C, cb, A, mat_bytes(m, q, lda)) || overlaps(C, cb, B, mat_bytes(q, n, ldb))) return -8;
-  if (q == 0) {
-    OZ_CHECK(launch_fill_zero(C, m, n, ldc, g.stream));
-    return OZGEMM_OK;
-  }
-  int mp, np, qp;
-  dims(m, n, q, &mp, &np, &qp);
-  int32_t* e = reinterpret_cast<int32_t*>(g.ws + g.lay.e);
-  int32_t* f = reinterpret_cast<int32_t*>(g.ws + g.lay.f);
-  int8_t* Ares = reinterpret_cast<int8_t*>(g.ws + g.lay.ares);
-  int8_t* Bres = reinterpret_cast<int8_t*>(g.ws + g.lay.bres);
-  uint8_t* rt = reinterpret_cast<uint8_t*>(g.ws + g.lay.rt);
-
-  ResidueConsts rc;
-  GemmConsts gc;
-  CrtConsts cc;
-  make_consts(s, q, g.bound, &rc, &gc, &cc);
   if ((st = ensure_crt_table())) return st;
-  cc.wtab = crt_table(s);
-
   std::array<hipEvent_t, 5> ev{};
   const bool timed = g.timing && g.events.size() < TIMING_MAX_CALLS;
-  if (timed) {
+  if (timed)
     for (auto& x : ev) OZ_CHECK(hipEventCreate(&x));
-    OZ_CHECK(hipEventRecord(ev[0], g.stream));
-  }
-  // B's exponents come out of its residue pass when the column fits (the
-  // OS II-fast budget needs its norms first, so it keeps two passes)
-  const bool b_one_pass = g.bound != OZGEMM_BOUND_FAST && col_residue_fits(q);
-  if ((st = run_scale(m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
-  if (timed) OZ_CHECK(hipEventRecord(ev[1], g.stream));
-  OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, g.stream));
-  if (b_one_pass)
-    OZ_CHECK(launch_col_residue(B, n, q, ldb, f, rc, Bres, np, qp, g.stream));
-  else
-    OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, g.stream));
-  if (timed) OZ_CHECK(hipEventRecord(ev[2], g.stream));
-  SplitChoice split{};
-  int cus = 0;
-  if ((st = product_split(mp, np, qp, s, &split, &cus))) return st;
-  OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, nullptr, rt, split, rt, cus, g.stream));
-  if (timed) OZ_CHECK(hipEventRecord(ev[3], g.stream));
-  OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, g.stream));
+  st = run_dgemm(config_ctx(), crt_table(s), m, n, q, A, lda, B, ldb, C, ldc, s, timed ? &ev : nullptr);
   if (timed) {
-    OZ_CHECK(hipEventRecord(ev[4], g.stream));
-    g.events.push_back(ev);
+    if (st == OZGEMM_OK)
+      g.events.push_back(ev);
+    else
+      for (auto& x : ev) (void)hipEventDestroy(x);
   }
-  return OZGEMM_OK;
+  return st;
 }
 
 int ozgemm_stage_scale(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, int32_t* e,
@@ -673,7 +721,8 @@ int ozgemm_stage_scale(int m, int n, int q, int s, const double* A, int lda, con
   if (f == nullptr && n > 0) return -10;
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
-  return run_scale(m, n, q, s, A, lda, B, ldb, e, f);
+  if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
+  return run_scale(config_ctx(), m, n, q, s, A, lda, B, ldb, e, f);
 }
 
 int ozgemm_set_bound(int mode) {
@@ -689,6 +738,7 @@ int ozgemm_bound_budget(int s, int q, int mode, int* kappa_a, int* kappa_b) {
   if (kappa_a == nullptr) return -4;
   if (kappa_b == nullptr) return -5;
   if (mode == OZGEMM_BOUND_FAST) {
+    if (q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
     fast_budget(s, kappa_a, kappa_b);
   } else {
     const int k = kbits_exact(s, q);
@@ -737,7 +787,7 @@ int ozgemm_stage_gemm(int m, int n, int q, int s, const int8_t* Ares, const int8
   make_consts(s, q, g.bound, &rc, &gc, &cc);
   SplitChoice split{1, qp / K_PAD};
   int cus = 0;
-  if (Ct == nullptr && rt != nullptr && (st = product_split(mp, np, qp, s, &split, &cus))) return st;
+  if (Ct == nullptr && rt != nullptr && (st = product_split(g.lay, mp, np, qp, s, &split, &cus))) return st;
   uint8_t* parts = reinterpret_cast<uint8_t*>(g.ws + g.lay.rt);
   OZ_CHECK(launch_gemm(Ares, Bres, mp, np, qp, gc, Ct, rt, split, parts, cus, g.stream));
   return 0;
@@ -755,7 +805,7 @@ int ozgemm_gemm_parts(int m, int n, int q, int s, int* parts) {
   dims(m, n, q, &mp, &np, &qp);
   SplitChoice split{};
   int cus = 0;
-  const int st = product_split(mp, np, qp, s, &split, &cus);
+  const int st = product_split(g.lay, mp, np, qp, s, &split, &cus);
   if (st) return st;
   *parts = split.parts;
   return OZGEMM_OK;
@@ -931,6 +981,23 @@ int ozgemm_phase_ms(double* ms_out, int* calls) {
       float ms = 0.f;
       OZ_CHECK(hipEventElapsedTime(&ms, ev[p], ev[p + 1]));
       ms_out[p] += ms;
+    }
+  }
+  if (calls) *calls = (int)g.events.size();
+  return OZGEMM_OK;
+}
+
+int ozgemm_phase_calls(double* ms_out, int max_calls, int* calls) {
+  if (max_calls < 0) return -2;
+  if (ms_out == nullptr && max_calls > 0) return -1;
+  const int n = std::min(max_calls, (int)g.events.size());
+  for (int c = 0; c < n; ++c) {
+    const auto& ev = g.events[(size_t)c];
+    OZ_CHECK(hipEventSynchronize(ev[4]));
+    for (int p = 0; p < 4; ++p) {
+      float ms = 0.f;
+      OZ_CHECK(hipEventElapsedTime(&ms, ev[p], ev[p + 1]));
+      ms_out[4 * c + p] = ms;
     }
   }
   if (calls) *calls = (int)g.events.size();

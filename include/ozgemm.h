@@ -54,13 +54,14 @@ extern "C" {
 
 #define OZGEMM_OK                  0
 #define OZGEMM_NOT_CONFIGURED      1  /* ozgemm_config has not succeeded */
-#define OZGEMM_RANGE               2  /* q > OZGEMM_Q_MAX, or k(s, q) < 1, or size beyond the configured maximum */
+#define OZGEMM_RANGE               2  /* q > OZGEMM_Q_MAX, k(s, q) < 1 (conservative budget), q >= OZGEMM_FAST_Q_LIMIT (OS II-fast), or size beyond the configured maximum */
 #define OZGEMM_WORKSPACE_TOO_SMALL 3  /* workspace_bytes below ozgemm_workspace_bytes(...) */
 #define OZGEMM_HIP_ERROR           4  /* a HIP call failed; ozgemm_strerror(4) names it */
 
 #define OZGEMM_S_MAX 20               /* largest supported number of moduli */
 #define OZGEMM_Q_LIMIT (1 << 17)      /* int8 dot products of length < this are exact in int32 (Ozaki II notes §6) */
 #define OZGEMM_Q_MAX   (1 << 27)      /* largest supported inner dimension */
+#define OZGEMM_FAST_Q_LIMIT (1 << 23) /* OS II-fast needs q below this: its row-norm sums of q terms of at most 2^40 stay exact in 64 bits */
 #define OZGEMM_MAX_ROWS 2096896       /* largest m and n: 2^21 - 256, so that the rows padded to 256 form at most 65535 tiles of 32 */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
 #define OZGEMM_ONE_PASS_Q_MIN 4096    /* ozgemm_dgemm reads B once for Q_MIN <= q <= Q_MAX (conservative budget) */
@@ -135,8 +136,11 @@ int ozgemm_dgemm(int m, int n, int q,
 int ozgemm_moduli(int s, int *moduli_out);
 
 /* k = floor(1/2 log2((M/2 - 1)/q)) for the first s moduli, evaluated with
- * exact integers (Ozaki II notes §5).  Returns k (>= 1) or a negative value
- * when s and q leave no bits or q >= 2^17. */
+ * exact integers (Ozaki II notes §5), for 1 <= q <= OZGEMM_Q_MAX (long inner
+ * dimensions run as K parts, see ozgemm_gemm_parts).  Returns k, which is
+ * < 1 when s and q leave no bits (ozgemm_dgemm then returns OZGEMM_RANGE
+ * under the conservative budget); -1 for s outside 1..OZGEMM_S_MAX or q < 1;
+ * -2 for q > OZGEMM_Q_MAX. */
 int ozgemm_kbits(int s, int q);
 
 /* Padded dimensions of the stage buffers below: rows of the residue planes
@@ -162,7 +166,8 @@ int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
 int ozgemm_set_bound(int mode);
 
 /* Bit budget for (s, q) under `mode`: (k, k) for the conservative bound
- * (OZGEMM_RANGE if k < 1), (kappa_A, kappa_B) for OS II-fast. */
+ * (OZGEMM_RANGE if k < 1), (kappa_A, kappa_B) for OS II-fast (OZGEMM_RANGE
+ * if q >= OZGEMM_FAST_Q_LIMIT). */
 int ozgemm_bound_budget(int s, int q, int mode, int *kappa_a, int *kappa_b);
 
 /* ---------------------------------------------------------------------- */
@@ -303,12 +308,16 @@ int ozgemm_scheme1_stage_accumulate(int m, int n, int q, int k, int variant,
 /* ---------------------------------------------------------------------- */
 
 /* enable != 0: every later ozgemm_dgemm records HIP events on the stream
- * around its four phases.  ozgemm_phase_ms adds, over the calls since timing
- * was enabled, the milliseconds of [scale, residue, gemm, crt] into
- * ms_out[0..3] (synchronising on the events) and the number of calls into
- * *calls.  Disabling discards the events. */
+ * around its four phases (up to 4096 calls).  ozgemm_phase_ms adds, over the
+ * calls since timing was enabled, the milliseconds of [scale, residue, gemm,
+ * crt] into ms_out[0..3] (synchronising on the events) and the number of
+ * calls into *calls.  ozgemm_phase_calls writes the same four times of each
+ * call, ms_out[4c + p] for call c < min(calls, max_calls), and the number of
+ * recorded calls into *calls (either pointer may be NULL when max_calls is
+ * 0).  Disabling discards the events. */
 int ozgemm_timing(int enable);
 int ozgemm_phase_ms(double *ms_out, int *calls);
+int ozgemm_phase_calls(double *ms_out, int max_calls, int *calls);
 
 #ifdef __cplusplus
 }

@@ -81,7 +81,7 @@ def test_workspace_and_plane_dims():
 def test_strerror_texts():
     assert "argument 3" in L.ozgemm_strerror(-3)
     assert "config" in L.ozgemm_strerror(L.OZGEMM_NOT_CONFIGURED)
-    assert "2^17" in L.ozgemm_strerror(L.OZGEMM_RANGE)
+    assert "2^27" in L.ozgemm_strerror(L.OZGEMM_RANGE) and "2^23" in L.ozgemm_strerror(L.OZGEMM_RANGE)
 
 
 FAKE = 1 << 40  # a non-NULL address that no validation path dereferences
@@ -240,3 +240,32 @@ def test_binding_constants_match_the_header():
         assert getattr(L, name) == value, name
         seen += 1
     assert seen >= 10
+
+
+def test_fast_budget_rejects_q_beyond_exact_norm_sums():
+    """OS II-fast sums q squared terms of at most 2^40 into 64 bits; the
+    library refuses q >= 2^23, the oracle's own limit (row_norm_units)."""
+    lim = L.OZGEMM_FAST_Q_LIMIT
+    assert lim == 2**23
+    a, b = L.ozgemm_bound_budget(14, lim - 1, L.OZGEMM_BOUND_FAST)
+    assert (a, b) == oz.cs_budget(oz.crt_constants(oz.greedy_moduli(14))[0])
+    st = L.lib().ozgemm_bound_budget(14, lim, L.OZGEMM_BOUND_FAST, ctypes.byref(ctypes.c_int()),
+                                     ctypes.byref(ctypes.c_int()))
+    assert st == L.OZGEMM_RANGE
+    # the conservative budget has no such limit
+    assert L.ozgemm_bound_budget(14, lim, L.OZGEMM_BOUND_CONSERVATIVE)[0] == L.ozgemm_kbits(14, lim)
+
+
+@no_gpu_only
+def test_fast_budget_q_limit_before_any_launch():
+    lib = L.lib()
+    lim = L.OZGEMM_FAST_Q_LIMIT
+    ws = L.ozgemm_workspace_bytes(8, 8, lim, 14)
+    assert lib.ozgemm_config(14, 8, 8, lim, None, FAKE, ws) == 0
+    Cp = FAKE + (1 << 40)
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_FAST) == 0
+    e = ctypes.c_void_p(FAKE + (1 << 41))
+    assert lib.ozgemm_dgemm(8, 8, lim, FAKE, 8, FAKE, lim, Cp, 8, 14) == L.OZGEMM_RANGE
+    assert lib.ozgemm_stage_scale(8, 8, lim, 14, FAKE, 8, FAKE, lim, e, e) == L.OZGEMM_RANGE
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE) == 0
+    lib.ozgemm_free()
