@@ -37,11 +37,16 @@ __device__ __forceinline__ int ceil_log2_bits(uint64_t b) {
   return ex - 1023 + (man != 0 ? 1 : 0);
 }
 
-// The residual after rounding a to the grid 2^g: returns rint(a 2^-g) and
-// replaces a by a - rint(a 2^-g) 2^g (both exact).
+// The residual after rounding a to the grid 2^g: returns n = rint(a 2^-g)
+// and replaces a by a - n 2^g, exactly.  For n != 0, |a 2^-g| >= 1/2, so the
+// scaling is exact and the difference is formed on the grid as
+// (a 2^-g - n) 2^g, which stays finite where n 2^g alone would overflow (a
+// row maximum within one grid step of the largest double).  For n = 0 the
+// residual is a (a 2^-g may have lost bits to underflow there).
 __device__ __forceinline__ double peel(double& a, int g) {
-  const double nn = __builtin_rint(__builtin_ldexp(a, -g));
-  a = a - __builtin_ldexp(nn, g);
+  const double x = __builtin_ldexp(a, -g);
+  const double nn = __builtin_rint(x);
+  a = (nn == 0.0) ? a : __builtin_ldexp(x - nn, g);
   return nn;
 }
 

@@ -119,6 +119,16 @@ def _round_to_grid(R: np.ndarray, g: np.ndarray) -> np.ndarray:
     return np.rint(np.ldexp(R, -g[:, None]))
 
 
+def _residual(R: np.ndarray, n: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """R - n 2^g, exactly (the residual the split keeps).  Where n != 0 the
+    difference is formed on the grid, (R 2^-g - n) 2^g: both steps are exact,
+    and n 2^g itself may overflow when the row maximum lies within one grid
+    step of the largest double.  Where n = 0 the residual is R itself."""
+    with np.errstate(over="ignore", under="ignore"):
+        scaled = np.ldexp(np.ldexp(R, -g[:, None]) - n, g[:, None])
+    return np.where(n == 0.0, R, scaled)
+
+
 def split_rn(X: np.ndarray, k: int, beta: int):
     """RN split of the rows of X into k int8 slices (Ozaki I notes, RN split
     algorithm).  Returns (slices (k, rows, cols) int8, grid exponents
@@ -137,7 +147,7 @@ def split_rn(X: np.ndarray, k: int, beta: int):
         assert np.all(np.abs(n) <= 2 ** (beta - 1)), "slice outside int8 budget"
         sl[p] = n.astype(np.int8)                  # step 6: INT8(mu^-1 A_s)
         ge[p] = g
-        R = R - np.ldexp(n, g[:, None])            # step 7: residual
+        R = _residual(R, n, g)                     # step 7: residual
     return sl, ge, bad
 
 
@@ -158,7 +168,7 @@ def split_hybrid(X: np.ndarray, k: int, beta: int):
         n[zero | bad, :] = 0.0
         assert np.all(np.abs(n) <= 2 ** (beta - 1)), "slice outside int8 budget"
         sl[p] = n.astype(np.int8)
-        R = R - np.ldexp(n, g[:, None])
+        R = _residual(R, n, g)
     return sl, g0.astype(np.int64), bad
 
 

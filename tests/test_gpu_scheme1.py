@@ -141,6 +141,32 @@ def test_special_values(variant):
 
 
 @pytest.mark.parametrize("variant", ["rn", "hybrid"])
+@pytest.mark.parametrize("q", [150, L.OZGEMM_ONE_PASS_Q_MIN])
+def test_rows_near_the_largest_double(variant, q):
+    """Rows of A and columns of B whose maximum is within one grid step of the
+    largest double: the first slice's grid times 2^(beta-1) is 2^1024, and the
+    residual must still be the exact difference.  B's columns are split by the
+    multi-pass kernels at q = 150 and by the one-pass kernel at q = 4096."""
+    rng = np.random.default_rng(23)
+    m, n = 40, 24
+    big = np.nextafter(np.inf, 0.0)
+    A = (rng.random((m, q)) - 0.5) * np.exp(rng.standard_normal((m, q)))
+    B = (rng.random((q, n)) - 0.5) * np.exp(rng.standard_normal((q, n))) * 2.0**-1000
+    A[0, 3], A[0, 5] = big, -0.75 * big
+    A[1, 0] = 1.9921875 * 2.0**1023
+    A[2, :] = np.ldexp(A[2, :] / np.abs(A[2, :]).max(), 1023)
+    A[2, 1] = -big
+    Bb = (rng.random((q, n)) - 0.5) * 2.0**-40
+    Bb[4, 0], Bb[7, 1] = big, -big
+    B[:, :2] = Bb[:, :2]  # two columns of B near the top too (against finite rows of A only)
+    A2 = A * 2.0**-30
+    A2[:3, :] = 0.0
+    log(f"scheme1 near-overflow {variant} q={q}")
+    check_parity(A, B[:, 2:], 6, variant)
+    check_parity(A2, B, 6, variant)
+
+
+@pytest.mark.parametrize("variant", ["rn", "hybrid"])
 def test_small_integers_exact(variant):
     rng = np.random.default_rng(2)
     A = rng.integers(-63, 64, size=(100, 333)).astype(np.float64)

@@ -249,3 +249,35 @@ def test_planted_grid_off_by_one_is_caught(monkeypatch):
     B[0, :] = 63.0
     C = o1.dgemm(A, B, 1, "rn")
     assert not np.array_equal(C, A @ B)
+
+
+@pytest.mark.parametrize("variant", ["rn", "hybrid"])
+def test_split_near_the_largest_double_stays_exact(variant):
+    """A row whose maximum lies within one grid step of the largest double:
+    its first slice rounds up to 2^(beta-1) on the grid 2^(1025 - beta), whose
+    product 2^1024 is not a double.  The residual is still the exact
+    difference (RN split, step 7), so slices and residual reconstruct the row
+    exactly, and the product with a small B column stays finite."""
+    big = np.nextafter(np.inf, 0.0)  # (2 - 2^-52) 2^1023
+    X = np.array([[big, -big * 0.75, 1.0, 3.0e-300, 5e-324, 0.0],
+                  [1.9921875 * 2.0**1023, 2.0**1000, -1.0, 0.0, 0.0, 0.0]])
+    beta, k = 7, 8
+    if variant == "rn":
+        sl, ge, bad = o1.split_rn(X, k, beta)
+        grids = ge
+    else:
+        sl, g0, bad = o1.split_hybrid(X, k, beta)
+        grids = np.stack([g0 - beta * p for p in range(k)])
+    assert not bad.any()
+    assert int(grids[0, 0]) == 1025 - beta and int(sl[0, 0, 0]) == 2 ** (beta - 1)
+    for i in range(X.shape[0]):
+        for j in range(X.shape[1]):
+            rec = sum(Fraction(int(sl[p, i, j])) * Fraction(2) ** int(grids[p, i]) for p in range(k))
+            err = Fraction(float(X[i, j])) - rec
+            assert abs(err) <= Fraction(2) ** int(grids[k - 1, i]) / 2, (i, j)
+    B = np.zeros((6, 2))
+    B[0, 0], B[1, 0], B[2, 1] = 2.0**-30, 2.0**-31, 1.0
+    C = (o1.dgemm_rn if variant == "rn" else o1.dgemm_hybrid)(X, B, k)
+    assert np.all(np.isfinite(C))
+    exact = Fraction(float(X[0, 0])) * Fraction(2) ** -30 + Fraction(float(X[0, 1])) * Fraction(2) ** -31
+    assert abs(Fraction(float(C[0, 0])) - exact) <= abs(exact) * Fraction(2) ** -40
