@@ -17,6 +17,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -41,6 +42,10 @@ def parse():
                    help="bit budget: the k of the Ozaki II notes section 5, or OS II-fast (section 9)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
+    p.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (default: host CPUs, <= 16)")
+    p.add_argument("--settle-seconds", type=float, default=2.0,
+                   help="untimed steady-state window after the warmup calls, timed per call with HIP events")
+    p.add_argument("--bits-entries", type=int, default=4096, help="sampled output entries for the correct bits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-accuracy", action="store_true")
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -73,44 +78,94 @@ def traffic_record(workload: str):
         return None
 
 
-def cpu_baseline(A, B, s, q, target_s, Cg_full_getter, bound="conservative"):
-    """Time the oracle on a block of output entries of the same workload."""
-    import numpy as np
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, run as it stands, in worker processes on the
+# host's cores (each worker evaluates oracle.ozaki2.dgemm_block on a block of
+# rows of the sampled output block; BLAS in each worker is single-threaded)
+# ---------------------------------------------------------------------------
+_W = {}
+
+
+def _oracle_worker_init(Bcols, s, bound):
+    _W["B"], _W["s"], _W["bound"] = Bcols, s, bound
+
+
+def _oracle_worker_block(Arows):
     from oracle import ozaki2 as oz
+    import numpy as np
+    B = _W["B"]
+    return oz.dgemm_block(Arows, B, _W["s"], np.arange(Arows.shape[0]), np.arange(B.shape[1]), bound=_W["bound"])
+
+
+def host_cpus() -> int:
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(A, B, s, q, target_s, Cg_full_getter, bound="conservative", workers=0):
+    """Time the oracle on a block of output entries of the same workload,
+    spread over `workers` processes (default: the host's CPUs, at most 16)."""
+    import multiprocessing as mp
+    import numpy as np
     m, n = A.shape[0], B.shape[1]
+    cpus = host_cpus()
+    W = workers if workers > 0 else max(1, min(16, cpus))
     rng = np.random.default_rng(7)
-    # calibrate on 32x32 and 64x64 blocks, fit how the cost grows with the
-    # side (between linearly and quadratically), and size the block for
-    # about target_s seconds
-    def timed(side):
-        t0 = time.perf_counter()
-        oz.dgemm_block(A, B, s, np.arange(min(side, m)), np.arange(min(side, n)), bound=bound)
-        return time.perf_counter() - t0
-    t32, t64 = timed(32), timed(64)
-    growth = min(2.0, max(1.0, math.log2(max(t64, 1e-6) / max(t32, 1e-6))))
-    side = int(max(32, min(1024, 64 * (target_s / max(t64, 1e-6)) ** (1 / growth))))
-    rows = np.sort(rng.choice(m, size=min(side, m), replace=False))
-    cols = np.sort(rng.choice(n, size=min(side, n), replace=False))
-    t0 = time.perf_counter()
-    ref = oz.dgemm_block(A, B, s, rows, cols, bound=bound)
-    dt = time.perf_counter() - t0
-    entries = len(rows) * len(cols)
+    ncols = min(n, 256)
+    cols = np.sort(rng.choice(n, size=ncols, replace=False))
+    Bc = np.ascontiguousarray(B[:, cols])
+    blas_env = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in blas_env}
+    for k in blas_env:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")  # fresh interpreters that never touch the GPU
+        with ctx.Pool(W, initializer=_oracle_worker_init, initargs=(Bc, s, bound)) as pool:
+            # calibrate with blocks of 4 and then 20 rows per worker: a block
+            # costs a fixed part (B's residues for the sampled columns) plus a
+            # part per row; size one block per worker for about target_s
+            perm = rng.permutation(m)
+
+            def timed_round(nrows):
+                blocks = [np.sort(perm[(nrows * w) % m:(nrows * w) % m + nrows]) for w in range(W)]
+                t0 = time.perf_counter()
+                pool.map(_oracle_worker_block, [np.ascontiguousarray(A[b, :]) for b in blocks], chunksize=1)
+                return time.perf_counter() - t0
+
+            timed_round(1)  # workers import the oracle
+            t4, t20 = timed_round(4), timed_round(20)
+            per_row = max((t20 - t4) / 16.0, 1e-6)
+            fixed = max(t4 - 4 * per_row, 0.0)
+            rows_per_worker = int(max(8, min(-(-m // W), (target_s - fixed) / per_row)))
+            total = min(m, rows_per_worker * W)
+            rows = np.sort(perm[:total])
+            blocks = np.array_split(rows, W)
+            t0 = time.perf_counter()
+            parts = pool.map(_oracle_worker_block, [np.ascontiguousarray(A[b, :]) for b in blocks], chunksize=1)
+            dt = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    ref = np.concatenate(parts, axis=0)
+    entries = ref.shape[0] * ref.shape[1]
     Cg = Cg_full_getter(rows, cols)
     exact = int(np.sum(Cg.view(np.uint64) == ref.view(np.uint64)))
     return {
         "value": 2.0 * q * entries / dt / 1e12,
         "unit": "TFLOPS",
-        "cores": blas_threads,
+        "cores": W,
         "kind": "oracle",
-        "sample": f"{len(rows)}x{len(cols)} output block (random rows/cols) of the same workload; "
-                  f"{dt:.1f} s wall; python-int CRT is single-threaded, numpy BLAS residue products "
-                  f"use {blas_threads} threads",
+        "sample": f"{len(rows)}x{len(cols)} output block (random rows and columns) of the same workload, "
+                  f"{dt:.1f} s wall on {W} worker processes (one oracle.ozaki2.dgemm_block per row block, "
+                  f"single-threaded BLAS each)",
         "seconds": dt,
+        "host_cpus": cpus,
+        "nproc": os.cpu_count(),
         "parity_entries": entries,
         "parity_bit_exact": exact,
     }
@@ -141,8 +196,11 @@ def main():
     if args.bound == "fast":
         L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST)
 
-    for _ in range(args.warmup):
+    def call():
         L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+
+    for _ in range(args.warmup):
+        call()
     torch.cuda.synchronize()
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 8, dtype=torch.float64, device=dev)
@@ -151,19 +209,53 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Steady state: the part runs under a power limit, and a short burst on a
+    # cool chip runs faster than the sustained rate.  Keep it busy for at
+    # least settle_seconds (calls timed one by one with HIP events on the
+    # library's stream), then time the K steps right after.
+    steady = None
+    if args.settle_seconds > 0:
+        L.ozgemm_timing(True)
+        t0 = time.perf_counter()
+        ncalls = 0
+        while True:
+            batch = max(1, min(256, 4096 - ncalls))
+            for _ in range(batch):
+                call()
+            ncalls += batch
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= args.settle_seconds or ncalls >= 4096:
+                break
+        wall = time.perf_counter() - t0
+        per_call = L.ozgemm_phase_calls()
+        L.ozgemm_timing(False)
+        tot = sorted(sum(c) for c in per_call)
+        gem = sorted(c[2] for c in per_call)
+        steady = {
+            "seconds": round(wall, 3), "calls": ncalls,
+            "ms_per_call_median": round(statistics.median(tot), 4),
+            "ms_per_call_mean": round(statistics.fmean(tot), 4),
+            "gemm_ms_median": round(statistics.median(gem), 4),
+            "gemm_ms_mean": round(statistics.fmean(gem), 4),
+            "tflops_at_median": round(2.0 * m * n * q / (statistics.median(tot) * 1e-3) / 1e12, 3),
+            "gemm_peak_frac_at_median": round(2.0 * s * m * n * q / (statistics.median(gem) * 1e-3) / 1e12
+                                              / INT8_PEAK_TOPS, 4),
+        }
+
     L.ozgemm_timing(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+        call()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    phase_ms, calls = L.ozgemm_phase_ms()
+    per_call = L.ozgemm_phase_calls()
     L.ozgemm_timing(False)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tflops = 2.0 * m * n * q / (ms_per_step * 1e-3) / 1e12
-    per = [x / max(calls, 1) for x in phase_ms]
+    per = [statistics.fmean(c[p] for c in per_call) for p in range(4)]
+    totals = [sum(c) for c in per_call]
     gemm_ms = per[2]
     int8_ops = 2.0 * s * m * n * q
     achieved = int8_ops / (gemm_ms * 1e-3) / 1e12
@@ -178,6 +270,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_event_median": round(statistics.median(totals), 4),
+        "ms_per_step_event_mean": round(statistics.fmean(totals), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -197,6 +291,8 @@ def main():
         },
         "phases_ms": {"scale": round(per[0], 4), "residue": round(per[1], 4), "gemm": round(per[2], 4),
                       "crt": round(per[3], 4)},
+        "gemm_ms_median": round(statistics.median(c[2] for c in per_call), 4),
+        "steady_state": steady,
         "int8_tops_end_to_end": round(int8_ops / (ms_per_step * 1e-3) / 1e12, 2),
         "int8_peak_frac_end_to_end": round(int8_ops / (ms_per_step * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
         "memory_phases_GBs": {
@@ -214,17 +310,17 @@ def main():
         return Cd[c][:, r].cpu().numpy().T
 
     if not args.no_accuracy:
-        from fp64_gemm_emulation_ozii_amd.accuracy import correct_bits
-        rng = np.random.default_rng(3)
-        ri = rng.integers(0, m, size=24)
-        ci = rng.integers(0, n, size=24)
+        from fp64_gemm_emulation_ozii_amd.accuracy import correct_bits_many
+        from fp64_gemm_emulation_ozii_amd.synthetic import sample_entries
+        ri, ci = sample_entries(m, n, args.bits_entries, seed=3)
         Cg = Cd.T[torch.from_numpy(ri).to(dev), torch.from_numpy(ci).to(dev)].cpu().numpy()
-        out["correct_bits"] = round(correct_bits(Cg, A, B, ri, ci), 2)
+        out["correct_bits"] = round(correct_bits_many(Cg, A, B, ri, ci), 2)
         native = (torch.from_numpy(A[ri, :]).to(dev) * torch.from_numpy(B[:, ci].T.copy()).to(dev)).sum(1)
-        out["correct_bits_native_fp64_dot"] = round(correct_bits(native.cpu().numpy(), A, B, ri, ci), 2)
+        out["correct_bits_native_fp64_dot"] = round(correct_bits_many(native.cpu().numpy(), A, B, ri, ci), 2)
+        out["correct_bits_entries"] = int(len(ri))
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter, args.bound)
+        out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter, args.bound, args.cpu_workers)
     L.ozgemm_free()
     print(json.dumps(out), flush=True)
 

@@ -75,6 +75,83 @@ def correct_bits(values, A: np.ndarray, B: np.ndarray, rows, cols) -> float:
     return 64.0 if worst == 0 else -math.log2(float(worst))
 
 
+def _two_sum_err(a, b, s):
+    """Error of s = fl(a + b), exactly (Knuth's TwoSum)."""
+    bb = s - a
+    return (a - (s - bb)) + (b - bb)
+
+
+def _split(a):
+    """Dekker's split a = hi + lo with hi holding the top 26 bits (|a| < 2^995)."""
+    t = 134217729.0 * a  # 2^27 + 1
+    hi = t - (t - a)
+    return hi, a - hi
+
+
+def _two_prod_err(a, b, p):
+    """Error of p = fl(a b), exactly (Dekker's TwoProduct, no fma), barring
+    underflow."""
+    ah, al = _split(a)
+    bh, bl = _split(b)
+    return ((ah * bh - p) + ah * bl + al * bh) + al * bl
+
+
+def compensated_dots(a: np.ndarray, b: np.ndarray):
+    """Row-wise dot products of a and b (E x q) as unevaluated pairs (hi, lo):
+    TwoProduct on every term, then a pairwise TwoSum tree, with the product
+    and addition errors summed in ordinary float64.  |hi + lo - a.b| is of
+    order (log2 q + q 2^-53) 2^-106 |a|.|b| (Ogita, Rump and Oishi, 2005, for
+    the same error-free transformations), far below the 2^-60 a correct-bit
+    figure needs.  Entries must be scaled so that no product underflows or
+    overflows (|a|, |b| < 1 and not too small, see correct_bits_many)."""
+    p = a * b
+    lo = _two_prod_err(a, b, p).sum(axis=1)
+    x = p
+    while x.shape[1] > 1:
+        if x.shape[1] % 2:
+            x = np.concatenate([x, np.zeros((x.shape[0], 1))], axis=1)
+        u, v = x[:, 0::2], x[:, 1::2]
+        sm = u + v
+        lo = lo + _two_sum_err(u, v, sm).sum(axis=1)
+        x = sm
+    return x[:, 0], lo
+
+
+def correct_bits_many(values, A: np.ndarray, B: np.ndarray, rows, cols, chunk: int = 256):
+    """Worst-entry correct bits of values[k] = C[rows[k], cols[k]] for
+    thousands of entries: the reference (AB)_ij is a compensated dot product
+    kept unrounded (see compensated_dots), after scaling row i of A and column
+    j of B by exact powers of two so that their maxima lie in [1/2, 1).  The
+    measure |C - AB| / (|A||B|) does not change under that scaling.  Entries
+    whose scaled terms fall below 2^-1000 add under 2^-1000 to (|A||B|)_ij,
+    so dropping them to zero by underflow moves the figure by nothing
+    measurable.  Non-finite values count as wrong (0 bits)."""
+    vals = np.asarray(values, dtype=np.float64)
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    worst = 0.0
+    for c0 in range(0, len(rows), chunk):
+        r, c, v = rows[c0:c0 + chunk], cols[c0:c0 + chunk], vals[c0:c0 + chunk]
+        a = np.asarray(A[r, :], dtype=np.float64)
+        b = np.asarray(B[:, c].T, dtype=np.float64)
+        _, ea = np.frexp(np.max(np.abs(a), axis=1))
+        _, eb = np.frexp(np.max(np.abs(b), axis=1))
+        with np.errstate(under="ignore"):
+            a = np.ldexp(a, -ea[:, None])
+            b = np.ldexp(b, -eb[:, None])
+            vs = np.ldexp(v, -(ea + eb))
+            hi, lo = compensated_dots(a, b)
+            den = np.sum(np.abs(a * b), axis=1)
+            err = np.abs((vs - hi) - lo)
+        ok = den > 0
+        bad = ok & ~np.isfinite(vs)
+        if bad.any():
+            return 0.0
+        rel = np.where(ok, err / np.where(ok, den, 1.0), 0.0)
+        worst = max(worst, float(rel.max(initial=0.0)))
+    return 64.0 if worst == 0 else min(64.0, -math.log2(worst))
+
+
 def _parse_list(text: str, conv):
     return [conv(x) for x in text.split(",") if x.strip()]
 

@@ -24,6 +24,7 @@ OZGEMM_HIP_ERROR = 4
 OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_Q_MAX = 1 << 27
+OZGEMM_FAST_Q_LIMIT = 1 << 23  # OS II-fast needs q below this
 OZGEMM_MAX_ROWS = 2096896  # 2^21 - 256
 OZGEMM_ONE_PASS_Q_MIN = 4096  # B read once by ozgemm_dgemm for q in [MIN, MAX] (conservative budget)
 OZGEMM_ONE_PASS_Q_MAX = 8192
@@ -42,7 +43,7 @@ EXPORTS = (
     "ozgemm_stage_residue", "ozgemm_stage_gemm", "ozgemm_stage_crt", "ozgemm_timing", "ozgemm_phase_ms",
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
-    "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts",
+    "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts", "ozgemm_phase_calls",
 )
 
 _lib = None
@@ -84,6 +85,7 @@ def lib():
         "ozgemm_gemm_parts": (c_int, [c_int, c_int, c_int, c_int, ip]),
         "ozgemm_timing": (c_int, [c_int]),
         "ozgemm_phase_ms": (c_int, [ctypes.POINTER(ctypes.c_double), ip]),
+        "ozgemm_phase_calls": (c_int, [ctypes.POINTER(ctypes.c_double), c_int, ip]),
         "ozgemm_scheme1_beta": (c_int, [c_int]),
         "ozgemm_scheme1_outputs": (c_int, [c_int, c_int, c_int]),
         "ozgemm_scheme1_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
@@ -169,26 +171,41 @@ def ozgemm_config(s_max: int, max_m: int, max_n: int, max_q: int, stream=None, w
     need = ozgemm_workspace_bytes(max_m, max_n, max_q, s_max)
     if scheme1_k > 0:
         need = max(need, ozgemm_scheme1_workspace_bytes(max_m, max_n, max_q, scheme1_k, scheme1_variant))
+    hs = _stream(stream)
     if workspace is None:
         import torch
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         workspace_bytes = need
     elif workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    st = lib().ozgemm_config(s_max, max_m, max_n, max_q, _stream(stream), _ptr(workspace), workspace_bytes)
-    _check(st, "ozgemm_config")
+    st = lib().ozgemm_config(s_max, max_m, max_n, max_q, hs, _ptr(workspace), workspace_bytes)
+    _check(st, "ozgemm_config")  # on failure the previous configuration and its workspace stay
+    _release_workspace()
     _workspace = workspace
     return st
 
 
+def _release_workspace():
+    """Drop the workspace reference held here, after every kernel queued on
+    the device has finished: the configured stream may differ from the one the
+    tensor was allocated on, and the caching allocator would otherwise hand
+    the bytes to new work while queued calls still read and write them."""
+    global _workspace
+    if _workspace is not None:
+        import torch
+        torch.cuda.synchronize()
+    _workspace = None
+
+
 def ozgemm_set_stream(stream=None) -> int:
+    """Later calls go on `stream`.  Work already queued on the previous stream
+    is not ordered before them: the caller orders the two streams."""
     return _check(lib().ozgemm_set_stream(_stream(stream)), "ozgemm_set_stream")
 
 
 def ozgemm_free() -> int:
-    global _workspace
     st = lib().ozgemm_free()
-    _workspace = None
+    _release_workspace()
     return st
 
 
@@ -285,3 +302,14 @@ def ozgemm_phase_ms():
     calls = ctypes.c_int()
     _check(lib().ozgemm_phase_ms(buf, ctypes.byref(calls)), "ozgemm_phase_ms")
     return list(buf), calls.value
+
+
+def ozgemm_phase_calls():
+    """Per-call phase times: a list of [scale, residue, gemm, crt] ms, one per
+    timed call."""
+    calls = ctypes.c_int()
+    _check(lib().ozgemm_phase_calls(None, 0, ctypes.byref(calls)), "ozgemm_phase_calls")
+    n = calls.value
+    buf = (ctypes.c_double * max(4 * n, 1))()
+    _check(lib().ozgemm_phase_calls(buf, n, ctypes.byref(calls)), "ozgemm_phase_calls")
+    return [list(buf[4 * c:4 * c + 4]) for c in range(n)]
