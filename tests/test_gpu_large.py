@@ -1,11 +1,13 @@
 """GPU parity at full problem sizes, in the launch configuration the
 benchmark times (ozgemm_dgemm with s = 14).
 
-The oracle cannot run these whole, so each test checks (a) every row and
-column exponent against the oracle, and (b) a block of output entries --
-random rows and columns plus the first/last rows and columns and rows/columns
-of the last output tile -- against the oracle evaluated on exactly those rows
-of A and columns of B (the entries only depend on them).
+Most of these are too large for the oracle as a whole, so each such test
+checks (a) every row and column exponent against the oracle, and (b) a block
+of output entries -- random rows and columns plus the first/last rows and
+columns and rows/columns of the last output tile -- against the oracle
+evaluated on exactly those rows of A and columns of B (the entries only
+depend on them).  At 4096^3 the whole output is compared with the whole
+oracle result, evaluated in tiles by worker processes on the host's cores.
 """
 import numpy as np
 import pytest
@@ -14,7 +16,8 @@ from oracle import ozaki2 as oz
 from fp64_gemm_emulation_ozii_amd import ozgemm as L
 from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
 
-from gpu_util import dev_colmajor, log, same_doubles, within_tolerance
+from gpu_util import dev_colmajor, first_diff, log, same_doubles, within_tolerance
+from oracle_pool import host_workers, oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +40,10 @@ def sample_lines(size: int, count: int, seed: int, tile: int = 256):
     (16384, 1024, 16384, 1.0, 1),
     (16384, 384, 16384, 1.0, 1),
     (1024, 65536, 1024, 1.0, 8),
+    (16384, 16384, 16384, 0.0, 1),
     (16384, 16384, 16384, 4.0, 1),
+    (16384, 16384, 16384, 16.0, 1),
+    (16384, 16384, 16384, 32.0, 1),
     (384, 2**20, 384, 1.0, None),
     (1792, 2**17 + 300, 1792, 1.0, 0),
 ])
@@ -78,3 +84,27 @@ def test_sampled_block_and_exponents(m, q, n, phi, parts):
     ref = oz.dgemm_block(A, B, s, rows, cols)
     assert within_tolerance(Cg, ref, A[rows, :], B[:, cols])
     assert same_doubles(Cg, ref)
+
+
+@pytest.mark.timeout(900)
+def test_full_oracle_4096_cubed():
+    """4096^3, s = 14, phi = 1: every entry of C against the oracle."""
+    import torch
+    m = q = n = 4096
+    s = 14
+    log(f"full 4096^3: generate; oracle on {host_workers()} worker processes")
+    A, B = hpl_like(m, q, n, 1.0, seed=0)
+    L.ozgemm_config(s, m, n, q)
+    Ad = dev_colmajor(A)
+    Bd = dev_colmajor(B)
+    Cd = torch.empty((n, m), dtype=torch.float64, device="cuda")
+    L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
+    torch.cuda.synchronize()
+    C = Cd.cpu().numpy().T
+    del Ad, Bd, Cd
+    L.ozgemm_free()
+    torch.cuda.empty_cache()
+    ref = oracle_full(m, q, n, 1.0, 0, s, tiles=(4, 4))
+    log("  compare")
+    assert same_doubles(C, ref), first_diff(C, ref)
+    assert within_tolerance(C, ref, A, B)

@@ -590,3 +590,15 @@ def test_fast_bound_special_rows():
     ref = np.round(A * 8) @ np.round(B * 8)
     ok = ~np.isnan(Ci)
     assert np.array_equal(Ci[ok], ref[ok])
+
+
+def test_tiled_oracle_pool_equals_the_whole_oracle():
+    """The process-pool evaluation used for full-size parity (tests/oracle_pool.py)
+    reassembles exactly the whole oracle result, ragged tiles included."""
+    from oracle_pool import oracle_full
+    from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
+    m, q, n = 37, 150, 29
+    A, B = hpl_like(m, q, n, 1.0, seed=5)
+    whole = oz.dgemm(A, B, 14)
+    tiled = oracle_full(m, q, n, 1.0, 5, 14, tiles=(3, 2), workers=2, timeout=300)
+    assert np.array_equal(whole.view(np.uint64), tiled.view(np.uint64))
