@@ -322,18 +322,146 @@ def fast_exponents(A: np.ndarray, e: np.ndarray, kappa: int, kb: int) -> np.ndar
     return out
 
 
+# ----------------------------------------------------------------------------
+# OS II-accu bit budget (Ozaki II notes §9)
+# ----------------------------------------------------------------------------
+#
+# §9: "accu" estimates the range c_max >= max_ij (|A'||B'|)_ij with an extra
+# low-precision GEMM, so that k_A, k_B can be opened wider than a cheap bound
+# allows.  Readings taken here (the page gives no more detail):
+#
+# * the low-precision GEMM is the method's own exact int8 product.  Every
+#   x_il = |a_il| 2^-e_i in [0, 1) is rounded up into one of two int8 bands,
+#   x <= H/127 + Lo/(127 * 128): H = ceil(127 x) for x >= 2^-7, Lo =
+#   ceil(127 * 128 x) for 0 < x < 2^-7 (both in [1, 127]), zero otherwise.
+#   Then sum_l x_il y_lj <= (HH + (HL + LH)/128 + LL/128^2) / 127^2, where HH
+#   and HL + LH are int8 products (one of length q, one of length 2q) and
+#   LL <= 127 min(sum_l Lo_il, sum_l Lo_lj).  Everything is an exact integer,
+#   so the bound, and every decision taken from it, is reproducible;
+# * the bound decides per-row and per-column bit counts a_i, b_j with
+#   a_i + b_j + L_ij <= K2 = floor(log2(M/2 - 1)) for every (i, j), where
+#   2^L_ij >= the bound (L_ij = -inf for a zero bound): first each column
+#   takes half of what its largest L leaves, then each row the most its
+#   columns allow, then each column the most its rows allow; both capped at
+#   ACCU_KMAX.  |A'_il| <= 2^a_i x_il, so (|A'||B'|)_ij <= 2^(a_i + b_j + L_ij)
+#   <= M/2 - 1: the CRT result is the exact A'B' (§5);
+# * the shift of row i is a_i - e_i; the exponents handed to the residue and
+#   CRT steps are e'_i = ACCU_KMAX - a_i + e_i (shift base ACCU_KMAX), as for
+#   OS II-fast.
+
+#: Largest bit count of a row of A' or column of B' (|A'| < 2^76 < 2^78,
+#: the widest integers the residue step reduces exactly).
+ACCU_KMAX = 76
+
+#: Band resolution: H, Lo in [0, 127]; the low band covers x < 2^-ACCU_BAND.
+ACCU_RES = 127
+ACCU_BAND = 7
+
+#: L of a zero bound (no constraint on the row and column).
+ACCU_LZERO = -128
+
+
+def accu_bands(X: np.ndarray, e: np.ndarray):
+    """(H, Lo) int64 arrays with |x_rl| <= H/127 + Lo/(127 2^7) for
+    x_rl = |X_rl| 2^-e_r, rounded up exactly: x = M 2^-sh with the integer
+    significand M of |X_rl|, and ceil(c M / 2^sh) is an integer ceiling.
+    Rows with e_r = NONFINITE are zero."""
+    X = np.abs(np.asarray(X, dtype=np.float64))
+    e = np.asarray(e, dtype=np.int64)
+    H = np.zeros(X.shape, dtype=np.int64)
+    Lo = np.zeros(X.shape, dtype=np.int64)
+    live = (X > 0) & (e[:, None] != NONFINITE)
+    mant, ex = np.frexp(X[live])                     # X = mant 2^ex, mant in [0.5, 1)
+    M = (mant * 2.0**53).astype(np.int64).astype(object)  # X = M 2^(ex - 53), exactly
+    rows = np.nonzero(live)[0]
+    sh = (53 + e[rows] - ex).astype(object)          # x = M 2^-sh, sh >= 1 since x < 1
+    hi = (M << ACCU_BAND) >= (1 << sh)               # x >= 2^-7 (Python integers)
+    c = np.where(hi, ACCU_RES, ACCU_RES << ACCU_BAND).astype(object)
+    v = (-((-(c * M)) >> sh)).astype(np.int64)       # ceil(c x), an exact integer ceiling
+    hi = hi.astype(bool)
+    H[live] = np.where(hi, v, 0)
+    Lo[live] = np.where(hi, 0, v)
+    return H, Lo
+
+
+def ceil_log2_ratio(N: int, D: int) -> int:
+    """Smallest integer L with N <= D 2^L, for integers N, D > 0."""
+    L = N.bit_length() - D.bit_length()
+    if (D << L if L >= 0 else D) < (N if L >= 0 else N << -L):
+        L += 1
+    return L
+
+
+#: The two-band bound is N_ij / ACCU_DEN.
+ACCU_DEN = ACCU_RES * ACCU_RES << (2 * ACCU_BAND)
+
+
+def accu_bound(A: np.ndarray, B: np.ndarray, e: np.ndarray, f: np.ndarray) -> np.ndarray:
+    """Integers N_ij with sum_l x_il y_lj <= N_ij / ACCU_DEN: the two-band
+    int8 bound, N = 2^14 HH + 2^7 (HL + LH) + 127 min(sum_l Lo_il, sum_l Lo_lj).
+    The int8 products are exact in float64 (every partial sum is an integer
+    below 3 q 127^2 < 2^53)."""
+    Ha, La = accu_bands(A, e)
+    Hb, Lb = accu_bands(np.asarray(B).T, f)
+    assert A.shape[1] * 3 * ACCU_RES**2 < 2**53
+    HH = (Ha.astype(np.float64) @ Hb.T.astype(np.float64)).astype(np.int64)
+    X = (Ha.astype(np.float64) @ Lb.T.astype(np.float64) + La.astype(np.float64) @ Hb.T.astype(np.float64)
+         ).astype(np.int64)
+    RS, CS = La.sum(axis=1), Lb.sum(axis=1)
+    return (HH << (2 * ACCU_BAND)) + (X << ACCU_BAND) + ACCU_RES * np.minimum(RS[:, None], CS[None, :])
+
+
+def accu_bound_exponents(A: np.ndarray, B: np.ndarray, e: np.ndarray, f: np.ndarray) -> np.ndarray:
+    """L_ij = ceil(log2(N_ij / ACCU_DEN)) of :func:`accu_bound`, so that
+    2^L_ij >= sum_l x_il y_lj (ACCU_LZERO where the bound is 0)."""
+    N = accu_bound(A, B, e, f)
+    D = ACCU_DEN
+    L = np.full(N.shape, ACCU_LZERO, dtype=np.int64)
+    for (i, j) in zip(*np.nonzero(N)):
+        L[i, j] = ceil_log2_ratio(int(N[i, j]), D)
+    return L
+
+
+def accu_scaling(L: np.ndarray, K2: int):
+    """Bit counts (a_i, b_j) from the exponents L_ij of the bound, with
+    a_i + b_j + L_ij <= K2 everywhere: columns take half of what their
+    largest L leaves, rows the most their columns then allow, columns the
+    most their rows then allow; all capped at ACCU_KMAX."""
+    L = np.asarray(L, dtype=np.int64)
+    b = np.minimum((K2 - L.max(axis=0)) // 2, ACCU_KMAX)
+    a = np.minimum((K2 - L - b[None, :]).min(axis=1), ACCU_KMAX)
+    b = np.minimum((K2 - L - a[:, None]).min(axis=0), ACCU_KMAX)
+    return a, b
+
+
+def accu_exponents(A: np.ndarray, B: np.ndarray, M: int):
+    """Exponents (e'_i, f'_j) of OS II-accu for the shift base ACCU_KMAX:
+    e'_i = ACCU_KMAX - a_i + e_i (row shift a_i - e_i); NONFINITE kept."""
+    e = row_exponents(A).astype(np.int64)
+    f = col_exponents(B).astype(np.int64)
+    K2 = (M // 2 - 1).bit_length() - 1
+    L = accu_bound_exponents(A, B, e, f)
+    a, b = accu_scaling(L, K2)
+    ep = np.where(e == NONFINITE, NONFINITE, ACCU_KMAX - a + e)
+    fp = np.where(f == NONFINITE, NONFINITE, ACCU_KMAX - b + f)
+    return ep, fp
+
+
 def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False, bound: str = "conservative"):
     """C ~= A B by Ozaki Scheme II with s moduli (Ozaki II notes §7).
 
     ``bound`` selects the bit budget: "conservative" is §5's
     c_max <= q 2^(k_A + k_B) with k_A = k_B = k; "fast" is the §9 OS II-fast
-    Cauchy-Schwarz budget of :func:`cs_budget` and :func:`fast_exponents`.
+    Cauchy-Schwarz budget of :func:`cs_budget` and :func:`fast_exponents`;
+    "accu" is the §9 OS II-accu budget of :func:`accu_exponents` (the row
+    and column bit counts depend on the whole of A and B, so a block of the
+    result is not the result of the block's rows and columns).
 
     With ``stages=True`` also returns a dict of every intermediate:
     ``moduli, M, k, e, f, Ap, Bp, Ares (s x m x q int8), Bres (s x q x n int8),
-    Ct (s x m x n int32), rt (s x m x n uint8), X (object), C``.  In fast mode
-    ``k`` is the shift base kb and e, f are the exponents e' of
-    :func:`fast_exponents` (row shift kb - e'_i).
+    Ct (s x m x n int32), rt (s x m x n uint8), X (object), C``.  In fast and
+    accu mode ``k`` is the shift base and e, f are the exponents e' of
+    :func:`fast_exponents` or :func:`accu_exponents` (row shift k - e'_i).
     """
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
@@ -357,6 +485,11 @@ def dgemm(A: np.ndarray, B: np.ndarray, s: int, stages: bool = False, bound: str
         k = max(kA, kB)
         e = fast_exponents(A, e, kA, k)
         f = fast_exponents(B.T, f, kB, k)
+    elif bound == "accu":
+        if kbits(M, q) < 1:
+            raise ValueError(f"s={s} leaves no bits for q={q}")
+        k = ACCU_KMAX
+        e, f = accu_exponents(A, B, M)
     else:
         raise ValueError(f"unknown bound {bound!r}")
     Ap = truncate_rows(A, e, k)

@@ -602,3 +602,204 @@ def test_tiled_oracle_pool_equals_the_whole_oracle():
     whole = oz.dgemm(A, B, 14)
     tiled = oracle_full(m, q, n, 1.0, 5, 14, tiles=(3, 2), workers=2, timeout=300)
     assert np.array_equal(whole.view(np.uint64), tiled.view(np.uint64))
+
+
+# ---------------------------------------------------------------- OS II-accu
+
+def _frac_x(v: float, e: int) -> Fraction:
+    return abs(Fraction(float(v))) / Fraction(2) ** int(e)
+
+
+def _accu_inputs(seed=0, m=9, q=150, n=8, phi=2.0):
+    rng = np.random.default_rng(seed)
+    A = (rng.random((m, q)) - 0.5) * np.exp(phi * rng.standard_normal((m, q)))
+    B = (rng.random((q, n)) - 0.5) * np.exp(phi * rng.standard_normal((q, n)))
+    A[0, :] = 0.0                               # zero row
+    A[1, :] = np.ldexp(1.0, -(np.arange(q) // 2))  # powers of two on both sides of the band edge
+    A[2, :] = 2.0**-1074                        # smallest subnormals
+    A[3, 5] = 2.0**-1060                        # a subnormal in a normal row
+    B[:, 0] = 1.0                               # flat column: the bound is nearly tight
+    B[:, 1] = 0.0
+    B[7, 2] = np.nan
+    return A, B
+
+
+def test_accu_bands_round_up_exactly():
+    """H/127 + Lo/(127 2^7) >= x = |a| 2^-e, with H = ceil(127 x) on
+    x >= 2^-7 and Lo = ceil(127 2^7 x) below: checked with exact rationals,
+    band edges, subnormals and Inf/NaN rows included."""
+    A, _ = _accu_inputs()
+    A[4, 3] = np.inf
+    e = oz.row_exponents(A).astype(np.int64)
+    H, Lo = oz.accu_bands(A, e)
+    for r in range(A.shape[0]):
+        for l in range(A.shape[1]):
+            if e[r] == oz.NONFINITE:
+                assert H[r, l] == 0 and Lo[r, l] == 0
+                continue
+            x = _frac_x(A[r, l], e[r])
+            assert 0 <= x < 1
+            if x == 0:
+                assert H[r, l] == 0 and Lo[r, l] == 0
+            elif x >= Fraction(1, 128):
+                assert Lo[r, l] == 0 and H[r, l] == math.ceil(127 * x)
+            else:
+                assert H[r, l] == 0 and Lo[r, l] == math.ceil(127 * 128 * x)
+            assert 0 <= H[r, l] <= 127 and 0 <= Lo[r, l] <= 127
+
+
+def _check_bound_holds(A, B, N=None, L=None):
+    """sum_l x_il y_lj <= N_ij / ACCU_DEN (when N is given) and <= 2^L_ij
+    (when L is given; L = -128 means the sum is 0), exactly."""
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    for i in range(A.shape[0]):
+        if e[i] == oz.NONFINITE:
+            continue
+        x = [_frac_x(v, e[i]) for v in A[i]]
+        for j in range(B.shape[1]):
+            if f[j] == oz.NONFINITE:
+                continue
+            exact = sum(xi * _frac_x(v, f[j]) for xi, v in zip(x, B[:, j]))
+            if N is not None:
+                assert exact <= Fraction(int(N[i, j]), oz.ACCU_DEN), (i, j)
+            if L is not None:
+                if L[i, j] == oz.ACCU_LZERO:
+                    assert exact == 0, (i, j)
+                else:
+                    assert exact <= Fraction(2) ** int(L[i, j]), (i, j, float(exact), int(L[i, j]))
+
+
+@pytest.mark.parametrize("seed,phi", [(0, 2.0), (1, 0.5), (2, 6.0)])
+def test_accu_bound_is_an_upper_bound(seed, phi):
+    """The two-band int8 bound of OS II-accu never falls below the exact
+    sum_l x_il y_lj, and L_ij is the ceiling of its log2."""
+    A, B = _accu_inputs(seed, phi=phi)
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    N = oz.accu_bound(A, B, e, f)
+    L = oz.accu_bound_exponents(A, B, e, f)
+    _check_bound_holds(A, B, N, L)
+    assert np.all(L[0, :] == oz.ACCU_LZERO) and np.all(L[:, 1] == oz.ACCU_LZERO)
+    # N written out from the bands for a few entries; L is the ceiling of log2
+    Ha, La = oz.accu_bands(A, e)
+    Hb, Lb = oz.accu_bands(B.T, f)
+    for i, j in [(3, 0), (5, 3), (1, 4), (2, 0)]:
+        Nij = (int(Ha[i] @ Hb[j]) << 14) + ((int(Ha[i] @ Lb[j]) + int(La[i] @ Hb[j])) << 7) \
+            + 127 * min(int(La[i].sum()), int(Lb[j].sum()))
+        assert Nij == N[i, j]
+        bound = Fraction(Nij, 127 * 127 * 2**14)
+        assert Fraction(2) ** int(L[i, j] - 1) < bound <= Fraction(2) ** int(L[i, j])
+
+
+def test_accu_bound_is_close_to_the_exact_sum():
+    """On log-normal rows (phi = 1) the bound stays within a factor 4 of the
+    exact sum for every entry and within 2 for most: the bands keep about
+    seven bits of each magnitude over fourteen bits of range."""
+    A, B = hpl_like(12, 400, 10, 1.0, seed=4)
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    L = oz.accu_bound_exponents(A, B, e, f)
+    x = np.ldexp(np.abs(A), -e[:, None])
+    y = np.ldexp(np.abs(B), -f[None, :])
+    ratio = np.exp2(L) / (x @ y)
+    assert np.all(ratio >= 1.0 - 1e-12) and np.all(ratio <= 4.0) and np.median(ratio) <= 2.0
+
+
+def test_accu_planted_underestimates_are_caught(monkeypatch):
+    """Rounding the bands down, or dropping the low band of B (the HL and LL
+    terms), gives bounds below the exact sum, which the upper-bound check
+    detects: on all-ones rows the high band is within 1% of exact, and a
+    row whose maximum meets only low-band entries of the column needs HL."""
+    q = 64
+    A1, B1 = np.ones((2, q)), np.ones((q, 2))          # x = y = 1/2: 127 x = 63.5
+    A2 = np.full((1, q), 2.0**-20)
+    B2 = np.full((q, 1), 2.0**-20)
+    A2[0, 0], A2[0, 5] = 1.0, 0.0                      # A's maximum meets B's low band
+    B2[5, 0] = 1.0                                     # B's maximum meets a zero of A
+    real = oz.accu_bands
+    cases = []
+    for A, B in [(A1, B1), (A2, B2)]:
+        e = oz.row_exponents(A).astype(np.int64)
+        f = oz.col_exponents(B).astype(np.int64)
+        _check_bound_holds(A, B, N=oz.accu_bound(A, B, e, f))
+        cases.append((A, B, e, f))
+
+    def floor_bands(X, ex):
+        H, Lo = real(X, ex)
+        return np.maximum(H - 1, 0), np.maximum(Lo - 1, 0)
+
+    monkeypatch.setattr(oz, "accu_bands", floor_bands)
+    A, B, e, f = cases[0]
+    with pytest.raises(AssertionError):
+        _check_bound_holds(A, B, N=oz.accu_bound(A, B, e, f))
+
+    def no_low_band_of_b(X, ex):
+        H, Lo = real(X, ex)
+        return (H, 0 * Lo) if X.shape == B2.T.shape and np.array_equal(X, B2.T) else (H, Lo)
+
+    monkeypatch.setattr(oz, "accu_bands", no_low_band_of_b)
+    A, B, e, f = cases[1]
+    with pytest.raises(AssertionError):
+        _check_bound_holds(A, B, N=oz.accu_bound(A, B, e, f))
+
+
+@pytest.mark.parametrize("s", [8, 12, 14, 17])
+def test_accu_scaling_is_feasible_and_tight(s):
+    """a_i + b_j + L_ij <= K2 everywhere; every row and column meets the
+    budget with equality somewhere (or sits at the cap)."""
+    A, B = _accu_inputs(s, phi=2.0)
+    M = oz.crt_constants(oz.greedy_moduli(s))[0]
+    K2 = (M // 2 - 1).bit_length() - 1
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    L = oz.accu_bound_exponents(A, B, e, f)
+    a, b = oz.accu_scaling(L, K2)
+    slack = K2 - (a[:, None] + b[None, :] + L)
+    assert np.all(slack >= 0)
+    for i in range(L.shape[0]):
+        assert a[i] == oz.ACCU_KMAX or np.any(slack[i, :] == 0)
+    for j in range(L.shape[1]):
+        assert b[j] == oz.ACCU_KMAX or np.any(slack[:, j] == 0)
+
+
+@pytest.mark.parametrize("s,q", [(8, 40), (12, 150), (14, 200), (18, 33)])
+def test_accu_keeps_crt_exact(s, q):
+    """OS II-accu: |A'_i| < 2^a_i per entry, the CRT returns A'B' exactly and
+    2 |A'B'| < M, with Python integers."""
+    A, B = _accu_inputs(s + q, q=q, phi=1.5)
+    B[7, 2] = 0.5
+    C, st = oz.dgemm(A, B, s, stages=True, bound="accu")
+    M, k = st["M"], st["k"]
+    to_int = np.vectorize(int, otypes=[object])
+    Ap, Bp = to_int(st["Ap"]), to_int(st["Bp"])
+    e, f = st["e"], st["f"]
+    for i in range(A.shape[0]):
+        if e[i] != oz.NONFINITE:
+            assert all(abs(v) < 2 ** (k - int(e[i]) + int(oz.row_exponents(A)[i])) for v in Ap[i])
+    absP = np.abs(Ap).dot(np.abs(Bp))
+    assert all(2 * int(v) < M for v in absP.flat)
+    assert np.array_equal(st["X"], Ap.dot(Bp))
+
+
+def test_accu_gains_bits_over_fast_on_wide_rows():
+    A, B = hpl_like(24, 512, 24, 2.0, seed=9)
+    rows, cols = np.arange(24).repeat(24), np.tile(np.arange(24), 24)
+    for s in (12, 14):
+        fast = oz.correct_bits(oz.dgemm(A, B, s, bound="fast"), A, B, rows, cols)
+        accu = oz.correct_bits(oz.dgemm(A, B, s, bound="accu"), A, B, rows, cols)
+        assert accu >= fast + 0.5, (s, fast, accu)
+
+
+def test_accu_special_rows_and_integers():
+    rng = np.random.default_rng(6)
+    A = rng.standard_normal((5, 20))
+    B = rng.standard_normal((20, 4))
+    A[1, :] = 0.0
+    A[2, 3] = np.nan
+    B[:, 1] = 0.0
+    C = oz.dgemm(A, B, 12, bound="accu")
+    assert np.all(C[1, :] == 0.0) and np.all(np.isnan(C[2, :]))
+    assert np.all(C[[0, 3, 4]][:, 1] == 0.0)
+    Ai, Bi = integer_valued(7, 64, 5, 2**10, seed=3)
+    assert np.array_equal(oz.dgemm(Ai, Bi, 14, bound="accu"), Ai @ Bi)
