@@ -38,8 +38,8 @@ def parse():
     p.add_argument("--q", type=int, default=8192)
     p.add_argument("--s", type=int, default=14)
     p.add_argument("--phi", type=float, default=1.0)
-    p.add_argument("--bound", choices=["conservative", "fast"], default="conservative",
-                   help="bit budget: the k of the Ozaki II notes section 5, or OS II-fast (section 9)")
+    p.add_argument("--bound", choices=["conservative", "fast", "accu"], default="conservative",
+                   help="bit budget: the k of the Ozaki II notes section 5, or OS II-fast / OS II-accu (section 9)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     p.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (default: host CPUs, <= 16)")
@@ -185,7 +185,7 @@ def main():
     from fp64_gemm_emulation_ozii_amd.synthetic import hpl_like
 
     m, n, q, s, phi = args.m, args.n, args.q, args.s, args.phi
-    workload = f"ozaki2_dgemm_{m}x{n}x{q}_s{s}_phi{phi:g}" + ("_fast" if args.bound == "fast" else "")
+    workload = f"ozaki2_dgemm_{m}x{n}x{q}_s{s}_phi{phi:g}" + ("" if args.bound == "conservative" else f"_{args.bound}")
     A, B = hpl_like(m, q, n, phi, seed=args.seed)
     dev = torch.device("cuda:0")
     Ad = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)   # column-major A, lda = m
@@ -193,8 +193,8 @@ def main():
     Cd = torch.empty((n, m), dtype=torch.float64, device=dev)  # column-major C, ldc = m
     stream = torch.cuda.current_stream()
     L.ozgemm_config(s, m, n, q, stream=stream)
-    if args.bound == "fast":
-        L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST)
+    if args.bound != "conservative":
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if args.bound == "fast" else L.OZGEMM_BOUND_ACCU)
 
     def call():
         L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
@@ -319,7 +319,11 @@ def main():
         out["correct_bits_native_fp64_dot"] = round(correct_bits_many(native.cpu().numpy(), A, B, ri, ci), 2)
         out["correct_bits_entries"] = int(len(ri))
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.bound == "accu":
+        # OS II-accu's row and column bit counts depend on all of A and B, so a
+        # block of the oracle is not the oracle on the block's rows and columns
+        out["cpu_baseline"] = None
+    elif not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, s, q, args.cpu_seconds, block_getter, args.bound, args.cpu_workers)
     L.ozgemm_free()
     print(json.dumps(out), flush=True)

@@ -17,7 +17,8 @@ emulation and of the native FP64 dot products on the same entries, and the
 time of each phase in milliseconds (Scheme II: scale, residue, GEMM, CRT;
 Scheme I: split, products, accumulation).  ``--methods ozaki2,scheme1-rn,
 scheme1-hybrid --k 4,5,6,7,8`` compares the two schemes on the same inputs;
-``ozaki2-fast`` is Scheme II under the OS II-fast bit budget (§9).
+``ozaki2-fast`` and ``ozaki2-accu`` are Scheme II under the OS II-fast and
+OS II-accu bit budgets (§9).
 """
 from __future__ import annotations
 
@@ -160,7 +161,7 @@ def _runs(s_list, k_list, methods):
     """(method, parameter) pairs: Scheme II over s, Scheme I variants over k."""
     out = []
     for meth in methods:
-        if meth in ("ozaki2", "ozaki2-fast"):
+        if meth in ("ozaki2", "ozaki2-fast", "ozaki2-accu"):
             out += [(meth, s) for s in s_list]
         elif meth in ("scheme1-rn", "scheme1-hybrid"):
             out += [(meth, k) for k in k_list]
@@ -197,7 +198,8 @@ def run_sweep(m, n, q, s_list, phi_list, entries, seed, repeats, k_list=(), meth
 
         def call(meth, p):
             if meth.startswith("ozaki2"):
-                L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if meth == "ozaki2-fast" else L.OZGEMM_BOUND_CONSERVATIVE)
+                L.ozgemm_set_bound({"ozaki2-fast": L.OZGEMM_BOUND_FAST, "ozaki2-accu": L.OZGEMM_BOUND_ACCU}.get(
+                    meth, L.OZGEMM_BOUND_CONSERVATIVE))
                 L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, p)
             else:
                 v = L.OZGEMM_S1_RN if meth == "scheme1-rn" else L.OZGEMM_S1_HYBRID
@@ -252,7 +254,7 @@ def main(argv=None):
     p.add_argument("--repeats", type=int, default=5)
     p.add_argument("--k", type=str, default="4,5,6,7,8", help="Scheme I slice counts")
     p.add_argument("--methods", type=str, default="ozaki2",
-                   help="comma list of ozaki2, ozaki2-fast, scheme1-rn, scheme1-hybrid")
+                   help="comma list of ozaki2, ozaki2-fast, ozaki2-accu, scheme1-rn, scheme1-hybrid")
     p.add_argument("--out", type=str, default="")
     a = p.parse_args(argv)
     res = run_sweep(a.m, a.n, a.q, _parse_list(a.s, int), _parse_list(a.phi, float), a.entries, a.seed, a.repeats,

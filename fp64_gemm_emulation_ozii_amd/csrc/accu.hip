@@ -1,0 +1,297 @@
+// OS II-accu bit budget (Ozaki II notes §9): a range estimate of c_max from
+// an extra low-precision product, which lets every row of A and column of B
+// keep as many bits as the CRT range allows.
+//
+// Bound.  With x_il = |a_il| 2^-e_i and y_lj = |b_lj| 2^-f_j in [0, 1) (e, f
+// the frexp exponents of the row and column maxima), every x is rounded up
+// into one of two int8 bands: H = ceil(127 x) for x >= 2^-7, Lo =
+// ceil(127 2^7 x) for 0 < x < 2^-7, both in [1, 127]; so x <= H/127 +
+// Lo/(127 2^7).  Then
+//   sum_l x_il y_lj <= N_ij / (127^2 2^14),
+//   N_ij = 2^14 HH_ij + 2^7 (HL + LH)_ij + 127 min(RS_i, CS_j),
+// where HH = H_A H_B^T and HL + LH = H_A Lo_B^T + Lo_A H_B^T are exact int8
+// products on the matrix cores (the plan form of the product kernel: one of
+// length q, one of length 2q; exact in int32 while 2 127^2 q_pad < 2^31) and
+// RS_i, CS_j are the row sums of Lo (LL = Lo_A Lo_B^T <= 127 min(RS_i, CS_j)).
+// L_ij = ceil(log2(N_ij / (127^2 2^14))), or -128 (no constraint) for N = 0.
+//
+// Scaling.  Bit counts a_i, b_j with a_i + b_j + L_ij <= K2 =
+// floor(log2(M/2 - 1)) for all (i, j), so that (|A'||B'|)_ij <=
+// 2^(a_i + b_j + L_ij) < M/2 and the CRT result is exact (§5): each column
+// first takes half of what its largest L leaves, each row then the most its
+// columns allow, each column then the most its rows allow; all at most
+// ACCU_KMAX.  The exponents handed on are e'_i = ACCU_KMAX - a_i + e_i (row
+// shift a_i - e_i, shift base ACCU_KMAX), NONFINITE kept.
+//
+// Every quantity is an exact integer function of the inputs, so the result
+// does not depend on the order of any sum.
+#include "oz_internal.h"
+
+namespace oz {
+
+namespace {
+
+constexpr int TR = 32;              // rows per band tile
+constexpr int TK = 128;             // inner-dimension entries per band tile
+constexpr int LDS_STRIDE = TK + 1;  // doubles; odd stride spreads banks
+constexpr int RES = 127;            // band resolution
+constexpr double LOW_EDGE = 0x1p-7; // x below this goes to the low band
+constexpr int LZERO = -128;         // L of a zero bound
+constexpr int CHUNK = 256;          // columns per block of the row-minimum pass
+
+// ceil(c x) for 0 <= x < 1 and c = 127 or 127 * 128, exactly: p = RN(c x)
+// and the product's rounding error err = c x - p (exact by fma).  If p is an
+// integer, c x exceeds it exactly when err > 0; otherwise no integer lies
+// between p and c x (rounding is monotone and integers are doubles).
+__device__ __forceinline__ int ceil_mul(double c, double x) {
+  const double p = c * x;
+  const double err = __builtin_fma(c, x, -p);
+  const double cp = __builtin_ceil(p);
+  return (int)cp + ((cp == p && err > 0.0) ? 1 : 0);
+}
+
+__device__ __forceinline__ uint32_t pack4(const int* v) {
+  return (uint32_t)(v[0] & 0xff) | ((uint32_t)(v[1] & 0xff) << 8) | ((uint32_t)(v[2] & 0xff) << 16) |
+         ((uint32_t)(v[3] & 0xff) << 24);
+}
+
+// Bands of the rows of X (element (r, l) at X[r rs + l ls]) into two int8
+// planes (rows_pad x q_pad, K-contiguous, zero padding), and per tile of 128
+// inner-dimension entries the sum of each row's Lo values:
+// psum[blockIdx.x * rows_pad + r].
+template <bool ROWS_CONTIG>
+__global__ __launch_bounds__(256) void accu_band_kernel(const double* __restrict__ X, int rows, int q, long rs, long ls,
+                                                         const int32_t* __restrict__ ex, int8_t* __restrict__ Hp,
+                                                         int8_t* __restrict__ Lp, int q_pad, int rows_pad,
+                                                         int32_t* __restrict__ psum) {
+  __shared__ double tile[TR * LDS_STRIDE];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.y * TR;
+  const int l0 = blockIdx.x * TK;
+  if (rows < 1) {
+    for (int idx = tid; idx < TR * LDS_STRIDE; idx += 256) tile[idx] = 0.0;
+  } else if (ROWS_CONTIG) {
+    const int r = tid & (TR - 1);
+    const int lsub = tid >> 5;
+    const bool rok = (r0 + r) < rows;
+    const double* src = X + (long)min(r0 + r, rows - 1);
+    double v[TK / 8];
+#pragma unroll
+    for (int it = 0; it < TK / 8; ++it) v[it] = src[(long)min(l0 + lsub + 8 * it, q - 1) * ls];
+#pragma unroll
+    for (int it = 0; it < TK / 8; ++it) {
+      const int l = lsub + 8 * it;
+      tile[r * LDS_STRIDE + l] = (rok && (l0 + l) < q) ? v[it] : 0.0;
+    }
+  } else {
+    const int l = tid & (TK - 1);
+    const int rsub = tid >> 7;
+    const bool lok = (l0 + l) < q;
+    const double* src = X + (long)min(l0 + l, q - 1);
+    double v[TR / 2];
+#pragma unroll
+    for (int it = 0; it < TR / 2; ++it) v[it] = src[(long)min(r0 + rsub + 2 * it, rows - 1) * rs];
+#pragma unroll
+    for (int it = 0; it < TR / 2; ++it) {
+      const int r = rsub + 2 * it;
+      tile[r * LDS_STRIDE + l] = (lok && (r0 + r) < rows) ? v[it] : 0.0;
+    }
+  }
+  __syncthreads();
+
+  const int r = tid >> 3;            // 0..31
+  const int cseg = (tid & 7) * 16;   // 0..112
+  const int grow = r0 + r;           // < rows_pad
+  int e = 0;
+  bool live = false;
+  if (grow < rows) {
+    e = ex[grow];
+    live = e != OZGEMM_EXP_NONFINITE;
+  }
+  int h[16], lo[16];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double a = __builtin_fabs(tile[r * LDS_STRIDE + cseg + j]);
+    const double x = __builtin_ldexp(a, -e);  // exact unless below 2^-1022 (then in the low band)
+    const bool nz = live && a != 0.0;
+    const bool hi = x >= LOW_EDGE;
+    const int hv = ceil_mul((double)RES, x);
+    const int lv = max(ceil_mul((double)(RES << 7), x), 1);  // a != 0 lost to underflow still counts 1
+    h[j] = (nz && hi) ? hv : 0;
+    lo[j] = (nz && !hi) ? lv : 0;
+    sum += lo[j];
+  }
+  const long off = (long)grow * q_pad + l0 + cseg;
+  *reinterpret_cast<uint4*>(Hp + off) = make_uint4(pack4(h), pack4(h + 4), pack4(h + 8), pack4(h + 12));
+  *reinterpret_cast<uint4*>(Lp + off) = make_uint4(pack4(lo), pack4(lo + 4), pack4(lo + 8), pack4(lo + 12));
+  // the 8 threads of a row are 8 consecutive lanes of one wavefront
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
+  if ((tid & 7) == 0) psum[(long)blockIdx.x * rows_pad + grow] = sum;
+}
+
+// Row sums of Lo: out[r] = sum over the nchunks tiles of psum.
+__global__ __launch_bounds__(256) void accu_rowsum_kernel(const int32_t* __restrict__ psum, int rows_pad, int nchunks,
+                                                           int32_t* __restrict__ out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows_pad) return;
+  int s = 0;
+  for (int c = 0; c < nchunks; ++c) s += psum[(long)c * rows_pad + r];
+  out[r] = s;
+}
+
+// The product plan: output 0 = H_A H_B^T; output 1 = H_A Lo_B^T + Lo_A H_B^T.
+__global__ void accu_plan_kernel(int4* plan) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    plan[0] = make_int4(0, 0, 1, 0);
+    plan[1] = make_int4(0, 1, 2, 1);
+  }
+}
+
+// Smallest L with N <= D 2^L (N, D > 0, N < 2^62, D < 2^30).
+__device__ __forceinline__ int ceil_log2_ratio(long long N, long long D) {
+  const int bn = 64 - __builtin_clzll((unsigned long long)N);
+  const int bd = 64 - __builtin_clzll((unsigned long long)D);
+  int L = bn - bd;
+  const bool fits = L >= 0 ? ((D << L) >= N) : (D >= (N << -L));
+  return fits ? L : L + 1;
+}
+
+__device__ __forceinline__ int block_reduce(int v, bool take_max, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    const int w = __shfl_xor(v, o, 64);
+    v = take_max ? max(v, w) : min(v, w);
+  }
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = take_max ? max(v, red[w]) : min(v, red[w]);
+  return v;
+}
+
+// Column j (one block): L_ij from the two product planes and the Lo sums,
+// and the column's first bit count b1_j = min(KMAX, floor((K2 - max_i L_ij) / 2)).
+__global__ __launch_bounds__(256) void accu_combine_kernel(const int32_t* __restrict__ P, int m, int m_pad, long plane,
+                                                            const int32_t* __restrict__ RS,
+                                                            const int32_t* __restrict__ CS, int K2, int kmax,
+                                                            int8_t* __restrict__ L, int32_t* __restrict__ b1) {
+  __shared__ int red[4];
+  const int j = blockIdx.x;
+  const long col = (long)j * m_pad;
+  const long long D = (long long)RES * RES << 14;
+  const int cs = CS[j];
+  int mx = LZERO;
+  for (int i = threadIdx.x; i < m; i += 256) {
+    const long long N = ((long long)P[col + i] << 14) + ((long long)P[plane + col + i] << 7) +
+                        (long long)RES * min(RS[i], cs);
+    const int l = N > 0 ? ceil_log2_ratio(N, D) : LZERO;
+    L[col + i] = (int8_t)l;
+    mx = max(mx, l);
+  }
+  mx = block_reduce(mx, true, red);
+  if (threadIdx.x == 0) b1[j] = min(kmax, (K2 - mx) >> 1);  // arithmetic shift: floor
+}
+
+// Partial row minima of K2 - L_ij - b1_j over a chunk of CHUNK columns.
+__global__ __launch_bounds__(256) void accu_rowmin_kernel(const int8_t* __restrict__ L, int m, int n, int m_pad,
+                                                           const int32_t* __restrict__ b1, int K2,
+                                                           int32_t* __restrict__ pmin) {
+  __shared__ int bs[CHUNK];
+  const int j0 = blockIdx.y * CHUNK;
+  const int jn = min(CHUNK, n - j0);
+  for (int t = threadIdx.x; t < jn; t += 256) bs[t] = b1[j0 + t];
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= m) return;
+  int v = 1 << 30;
+  for (int t = 0; t < jn; ++t) v = min(v, K2 - (int)L[(long)(j0 + t) * m_pad + i] - bs[t]);
+  pmin[(long)blockIdx.y * m_pad + i] = v;
+}
+
+// Row bit counts a_i and exponents e'_i (in place).
+__global__ __launch_bounds__(256) void accu_rowfinal_kernel(const int32_t* __restrict__ pmin, int m, int m_pad,
+                                                             int nchunks, int kmax, int32_t* __restrict__ a,
+                                                             int32_t* __restrict__ e) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= m) return;
+  int v = kmax;
+  for (int c = 0; c < nchunks; ++c) v = min(v, pmin[(long)c * m_pad + i]);
+  a[i] = v;
+  const int ei = e[i];
+  e[i] = ei == OZGEMM_EXP_NONFINITE ? ei : kmax - v + ei;
+}
+
+// Column j (one block): b_j = min(KMAX, min_i (K2 - L_ij - a_i)) and f'_j (in place).
+__global__ __launch_bounds__(256) void accu_colfinal_kernel(const int8_t* __restrict__ L, int m, int m_pad,
+                                                             const int32_t* __restrict__ a, int K2, int kmax,
+                                                             int32_t* __restrict__ f) {
+  __shared__ int red[4];
+  const int j = blockIdx.x;
+  const long col = (long)j * m_pad;
+  int v = kmax;
+  for (int i = threadIdx.x; i < m; i += 256) v = min(v, K2 - (int)L[col + i] - a[i]);
+  v = block_reduce(v, false, red);
+  if (threadIdx.x == 0) {
+    const int fj = f[j];
+    f[j] = fj == OZGEMM_EXP_NONFINITE ? fj : kmax - v + fj;
+  }
+}
+
+}  // namespace
+
+size_t accu_scratch_bytes(int m_pad, int n_pad, int q_pad) {
+  const size_t mp = (size_t)m_pad, np = (size_t)n_pad;
+  const size_t chunks = (np + CHUNK - 1) / CHUNK;
+  return round_up(8 * mp * np, 256) + round_up(mp * np, 256) + round_up(4 * mp, 256) * 2 +
+         round_up(4 * np, 256) * 2 + round_up(4 * chunks * mp, 256) + round_up((size_t)(q_pad / TK) * 4 * np, 256) +
+         256;
+}
+
+hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const double* B, int n, int ldb, int m_pad,
+                                 int n_pad, int q_pad, int K2, int kmax, int8_t* Aplanes, int8_t* Bplanes,
+                                 int32_t* psumA, char* scratch, int32_t* e, int32_t* f, hipStream_t st) {
+  if (m < 1 || n < 1 || q < 1 || q_pad % TK || m_pad % 256 || n_pad % 256 || m_pad / TR > 65535 ||
+      n_pad / TR > 65535 || q_pad > ACCU_Q_MAX || 2L * RES * RES * q_pad >= (1L << 31) || kmax != ACCU_KMAX)
+    return hipErrorInvalidValue;
+  const size_t mp = (size_t)m_pad, np = (size_t)n_pad;
+  const int nk = q_pad / TK;
+  const int chunks = (n + CHUNK - 1) / CHUNK;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = scratch + off;
+    off = round_up(off + bytes, 256);
+    return p;
+  };
+  int32_t* P = reinterpret_cast<int32_t*>(take(8 * mp * np));  // two int32 planes [o][j][i]
+  int8_t* L = reinterpret_cast<int8_t*>(take(mp * np));
+  int32_t* RS = reinterpret_cast<int32_t*>(take(4 * mp));
+  int32_t* a = reinterpret_cast<int32_t*>(take(4 * mp));
+  int32_t* CS = reinterpret_cast<int32_t*>(take(4 * np));
+  int32_t* b1 = reinterpret_cast<int32_t*>(take(4 * np));
+  int32_t* pmin = reinterpret_cast<int32_t*>(take(4 * (size_t)chunks * mp));
+  int32_t* psumB = reinterpret_cast<int32_t*>(take((size_t)nk * 4 * np));
+  int4* plan = reinterpret_cast<int4*>(take(2 * sizeof(int4)));
+
+  // bands of A's rows (A column-major: rows contiguous) and of B's columns
+  hipLaunchKernelGGL(accu_band_kernel<true>, dim3(nk, m_pad / TR), dim3(256), 0, st, A, m, q, 1L, (long)lda, e,
+                     Aplanes, Aplanes + mp * q_pad, q_pad, m_pad, psumA);
+  hipLaunchKernelGGL(accu_band_kernel<false>, dim3(nk, n_pad / TR), dim3(256), 0, st, B, n, q, (long)ldb, 1L, f,
+                     Bplanes, Bplanes + np * q_pad, q_pad, n_pad, psumB);
+  hipLaunchKernelGGL(accu_rowsum_kernel, dim3(m_pad / 256), dim3(256), 0, st, psumA, m_pad, nk, RS);
+  hipLaunchKernelGGL(accu_rowsum_kernel, dim3(n_pad / 256), dim3(256), 0, st, psumB, n_pad, nk, CS);
+  hipLaunchKernelGGL(accu_plan_kernel, dim3(1), dim3(64), 0, st, plan);
+  hipError_t err = launch_gemm_multi(Aplanes, Bplanes, m_pad, n_pad, q_pad, plan, 2, P, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(accu_combine_kernel, dim3(n), dim3(256), 0, st, P, m, m_pad, (long)(mp * np), RS, CS, K2, kmax,
+                     L, b1);
+  hipLaunchKernelGGL(accu_rowmin_kernel, dim3((m + 255) / 256, chunks), dim3(256), 0, st, L, m, n, m_pad, b1, K2,
+                     pmin);
+  hipLaunchKernelGGL(accu_rowfinal_kernel, dim3((m + 255) / 256), dim3(256), 0, st, pmin, m, m_pad, chunks, kmax, a,
+                     e);
+  hipLaunchKernelGGL(accu_colfinal_kernel, dim3(n), dim3(256), 0, st, L, m, m_pad, a, K2, kmax, f);
+  return hipGetLastError();
+}
+
+}  // namespace oz

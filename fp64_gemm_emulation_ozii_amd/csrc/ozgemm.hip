@@ -158,7 +158,10 @@ int modinv_small(int a, int m) {  // a^-1 mod m, gcd(a, m) = 1
 // and B' for the active bit budget: the conservative one (k bits, §5) or
 // OS II-fast (exponents e' relative to kb = max(kappa_A, kappa_B), §9).
 void budget_k(int s, int q, int mode, int* k, int* kmag) {
-  if (mode == OZGEMM_BOUND_FAST) {
+  if (mode == OZGEMM_BOUND_ACCU) {  // per-row and per-column bit counts up to ACCU_KMAX (§9)
+    *k = ACCU_KMAX;
+    *kmag = ACCU_KMAX;
+  } else if (mode == OZGEMM_BOUND_FAST) {
     int ka, kb;
     fast_budget(s, &ka, &kb);
     *k = std::max(ka, kb);
@@ -235,7 +238,7 @@ struct Layout {
   size_t consts, pmax, e, f, ares, bres, rt, rt_bytes, total;
 };
 
-Layout make_layout(int max_m, int max_n, int max_q, int s_max, bool split_region = true) {
+Layout make_layout(int max_m, int max_n, int max_q, int s_max, bool split_region = true, size_t rt_min = 0) {
   const size_t mp = round_up((size_t)std::max(max_m, 1), ROW_PAD);
   const size_t np = round_up((size_t)std::max(max_n, 1), ROW_PAD);
   const size_t qp = round_up((size_t)std::max(max_q, 1), K_PAD);
@@ -253,8 +256,9 @@ Layout make_layout(int max_m, int max_n, int max_q, int s_max, bool split_region
   L.ares = take((size_t)s_max * mp * qp);
   L.bres = take((size_t)s_max * np * qp);
   // product residues; also the K part planes of skinny products (gemm_grid.h)
-  L.rt_bytes = std::max((size_t)s_max * mp * np,
-                        split_region ? (size_t)split_region_bytes((int)(qp / K_PAD), ROW_PAD * ROW_PAD) : 0);
+  L.rt_bytes = std::max({(size_t)s_max * mp * np,
+                         split_region ? (size_t)split_region_bytes((int)(qp / K_PAD), ROW_PAD * ROW_PAD) : 0,
+                         rt_min});
   L.rt = take(L.rt_bytes);
   L.total = off;
   return L;
@@ -382,18 +386,16 @@ int check_common(int m, int n, int q, const double* A, int lda, const double* B,
 // Limits of the method and of the active bit budget (any entry point).
 int check_method_range(int q, int s) {
   if (q > OZGEMM_Q_MAX) return OZGEMM_RANGE;
-  if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+  if (g.bound != OZGEMM_BOUND_FAST && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
   if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
+  if (g.bound == OZGEMM_BOUND_ACCU && (q > OZGEMM_ACCU_Q_MAX || s < 2)) return OZGEMM_RANGE;
   return 0;
 }
 
 int check_range(int m, int n, int q, int s) {
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
-  if (q > OZGEMM_Q_MAX) return OZGEMM_RANGE;
-  if (g.bound == OZGEMM_BOUND_CONSERVATIVE && q > 0 && kbits_exact(s, q) < 1) return OZGEMM_RANGE;
-  if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
-  return 0;
+  return check_method_range(q, s);
 }
 
 int nchunks_for(int m, int q) {
@@ -402,6 +404,18 @@ int nchunks_for(int m, int q) {
   nch = std::min(nch, (q + 31) / 32);
   nch = std::min(nch, NCH_MAX);
   return std::max(nch, 1);
+}
+
+// Room for OS II-accu's intermediates: the band planes use the residue
+// regions, the bound's int32 and L planes the product region, the partial
+// row sums of A's low band the partial row-max region; all of it is dead
+// until the residue step.
+bool accu_fits(const Layout& lay, int m, int n, int q) {
+  if (m < 1 || n < 1 || q < 1) return true;
+  int mpc, npc, qpc;
+  dims(m, n, q, &mpc, &npc, &qpc);
+  return lay.bres - lay.ares >= 2 * (size_t)mpc * qpc && lay.rt - lay.bres >= 2 * (size_t)npc * qpc &&
+         lay.rt_bytes >= accu_scratch_bytes(mpc, npc, qpc) && (size_t)qpc / K_PAD * 4 <= (size_t)NCH_MAX * 8;
 }
 
 int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb,
@@ -421,6 +435,17 @@ int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda
   if (n > 0) {
     OZ_CHECK(launch_col_exp(B, q, n, ldb, f, x.stream));
     if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
+  }
+  if (x.bound == OZGEMM_BOUND_ACCU && m > 0 && n > 0 && q > 0) {
+    int mpc, npc, qpc;
+    dims(m, n, q, &mpc, &npc, &qpc);
+    if (!accu_fits(x.lay, m, n, q)) return OZGEMM_WORKSPACE_TOO_SMALL;  // checked before any launch by callers
+    int ka2, kb2;
+    fast_budget(s, &ka2, &kb2);
+    OZ_CHECK(launch_accu_exponents(A, m, q, lda, B, n, ldb, mpc, npc, qpc, ka2 + kb2, ACCU_KMAX,
+                                   reinterpret_cast<int8_t*>(x.ws + x.lay.ares),
+                                   reinterpret_cast<int8_t*>(x.ws + x.lay.bres), reinterpret_cast<int32_t*>(pmax),
+                                   x.ws + x.lay.rt, e, f, x.stream));
   }
   return 0;
 }
@@ -583,7 +608,7 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   if (ev) OZ_CHECK(hipEventRecord((*ev)[0], x.stream));
   // B's exponents come out of its residue pass when the column fits (the
   // OS II-fast budget needs its norms first, so it keeps two passes)
-  const bool b_one_pass = x.bound != OZGEMM_BOUND_FAST && col_residue_fits(q);
+  const bool b_one_pass = x.bound == OZGEMM_BOUND_CONSERVATIVE && col_residue_fits(q);
   if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
   if (ev) OZ_CHECK(hipEventRecord((*ev)[1], x.stream));
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
@@ -692,6 +717,7 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
   if (st) return st;
   if ((st = check_range(m, n, q, s))) return st;
   if (m == 0 || n == 0) return OZGEMM_OK;
+  if (g.bound == OZGEMM_BOUND_ACCU && !accu_fits(g.lay, m, n, q)) return OZGEMM_WORKSPACE_TOO_SMALL;
   if ((st = ensure_crt_table())) return st;
   std::array<hipEvent_t, 5> ev{};
   const bool timed = g.timing && g.events.size() < TIMING_MAX_CALLS;
@@ -722,11 +748,16 @@ int ozgemm_stage_scale(int m, int n, int q, int s, const double* A, int lda, con
   if (!g.configured) return OZGEMM_NOT_CONFIGURED;
   if (m > g.max_m || n > g.max_n || q > g.max_q || s > g.s_max) return OZGEMM_RANGE;
   if (g.bound == OZGEMM_BOUND_FAST && q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
+  if (g.bound == OZGEMM_BOUND_ACCU) {
+    int st = check_method_range(q, s);
+    if (st) return st;
+    if (!accu_fits(g.lay, m, n, q)) return OZGEMM_WORKSPACE_TOO_SMALL;
+  }
   return run_scale(config_ctx(), m, n, q, s, A, lda, B, ldb, e, f);
 }
 
 int ozgemm_set_bound(int mode) {
-  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST) return -1;
+  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST && mode != OZGEMM_BOUND_ACCU) return -1;
   g.bound = mode;
   return OZGEMM_OK;
 }
@@ -734,10 +765,16 @@ int ozgemm_set_bound(int mode) {
 int ozgemm_bound_budget(int s, int q, int mode, int* kappa_a, int* kappa_b) {
   if (s < 1 || s > OZGEMM_S_MAX) return -1;
   if (q < 1 || q > OZGEMM_Q_MAX) return -2;
-  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST) return -3;
+  if (mode != OZGEMM_BOUND_CONSERVATIVE && mode != OZGEMM_BOUND_FAST && mode != OZGEMM_BOUND_ACCU) return -3;
   if (kappa_a == nullptr) return -4;
   if (kappa_b == nullptr) return -5;
-  if (mode == OZGEMM_BOUND_FAST) {
+  if (mode == OZGEMM_BOUND_ACCU) {
+    if (q > OZGEMM_ACCU_Q_MAX || s < 2 || kbits_exact(s, q) < 1) return OZGEMM_RANGE;
+    int ka, kb;
+    fast_budget(s, &ka, &kb);
+    *kappa_a = ka + kb;  // the budget a_i + b_j + L_ij <= K2 shares
+    *kappa_b = ACCU_KMAX;
+  } else if (mode == OZGEMM_BOUND_FAST) {
     if (q >= OZGEMM_FAST_Q_LIMIT) return OZGEMM_RANGE;  // 64-bit norm sums
     fast_budget(s, kappa_a, kappa_b);
   } else {

@@ -31,6 +31,8 @@ OZGEMM_ONE_PASS_Q_MAX = 8192
 OZGEMM_EXP_NONFINITE = 0x7FFFFFFF
 OZGEMM_BOUND_CONSERVATIVE = 0
 OZGEMM_BOUND_FAST = 1
+OZGEMM_BOUND_ACCU = 2
+OZGEMM_ACCU_Q_MAX = 1 << 16
 OZGEMM_S1_RN = 0
 OZGEMM_S1_HYBRID = 1
 OZGEMM_S1_K_MAX = 16

@@ -70,6 +70,8 @@ extern "C" {
 /* Bit budgets of Scheme II (ozgemm_set_bound) */
 #define OZGEMM_BOUND_CONSERVATIVE 0 /* c_max <= q 2^(k_A + k_B), k_A = k_B = k (Ozaki II notes §5) */
 #define OZGEMM_BOUND_FAST         1 /* Cauchy-Schwarz c_max bound, OS II-fast (Ozaki II notes §9) */
+#define OZGEMM_BOUND_ACCU         2 /* c_max bound from an extra exact int8 product, OS II-accu (Ozaki II notes §9) */
+#define OZGEMM_ACCU_Q_MAX   (1 << 16) /* OS II-accu needs q <= this: its bound products stay exact in int32 */
 
 /* Scheme I variants (Ozaki I notes, optimized algorithm) */
 #define OZGEMM_S1_RN      0  /* RN split, per-product FP64 accumulation (direction 1) */
@@ -161,13 +163,38 @@ int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
  *     A'B', and entries keep more bits whenever a row's norm is well below
  *     sqrt(q) times its maximum.  The stage exponents become
  *     e'_i = kb - d_i with kb = max(kappa_A, kappa_B), so that the row shift
- *     is kb - e'_i and the unscaling exponent e'_i + f'_j - 2 kb.
+ *     is kb - e'_i and the unscaling exponent e'_i + f'_j - 2 kb.  Needs
+ *     q < OZGEMM_FAST_Q_LIMIT.
+ *   OZGEMM_BOUND_ACCU: OS II-accu (Ozaki II notes §9): c_max is bounded by
+ *     an extra exact int8 product.  With x_il = |a_il| 2^-e_i in [0, 1)
+ *     (e_i the frexp exponent of the row maximum; y_lj likewise for the
+ *     columns of B), each x is rounded up into two int8 bands,
+ *     x <= H/127 + Lo/(127 2^7): H = ceil(127 x) for x >= 2^-7, Lo =
+ *     ceil(127 2^7 x) below.  Then sum_l x_il y_lj <= N_ij / (127^2 2^14)
+ *     with N = 2^14 H_A H_B^T + 2^7 (H_A Lo_B^T + Lo_A H_B^T) +
+ *     127 min(row sum of Lo_A, column sum of Lo_B), two int8 products run
+ *     on the product kernel (length q and 2q), and L_ij = ceil(log2 of the
+ *     bound).  Row bit counts a_i and column bit counts b_j satisfy
+ *     a_i + b_j + L_ij <= floor(log2(M/2 - 1)) for every (i, j): columns
+ *     first take half of what their largest L leaves, rows then the most
+ *     their columns allow, columns then the most their rows allow, all at
+ *     most 76.  Row i of A' is trunc(a_il 2^(a_i - e_i)), so (|A'||B'|)_ij <
+ *     M/2 and the CRT result is exact (§5).  The stage exponents are
+ *     e'_i = 76 - a_i + e_i (shift base 76).  Every quantity is an exact
+ *     integer, so results are reproducible.  Needs q <= OZGEMM_ACCU_Q_MAX,
+ *     s >= 2 and k(s, q) >= 1, and room in the workspace's product region
+ *     for two int32 planes and one int8 plane of m_pad x n_pad (about 9.02
+ *     m_pad n_pad bytes, which s_max >= 10 always gives; otherwise
+ *     OZGEMM_WORKSPACE_TOO_SMALL).
  * Returns 0, or -1 for an unknown mode. */
 int ozgemm_set_bound(int mode);
 
 /* Bit budget for (s, q) under `mode`: (k, k) for the conservative bound
  * (OZGEMM_RANGE if k < 1), (kappa_A, kappa_B) for OS II-fast (OZGEMM_RANGE
- * if q >= OZGEMM_FAST_Q_LIMIT). */
+ * if q >= OZGEMM_FAST_Q_LIMIT), (K2, 76) for OS II-accu: the budget
+ * a_i + b_j + L_ij <= K2 = floor(log2(M/2 - 1)) that the row and column bit
+ * counts share, and their cap (OZGEMM_RANGE if q > OZGEMM_ACCU_Q_MAX, s < 2
+ * or k < 1). */
 int ozgemm_bound_budget(int s, int q, int mode, int *kappa_a, int *kappa_b);
 
 /* ---------------------------------------------------------------------- */

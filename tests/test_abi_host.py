@@ -269,3 +269,47 @@ def test_fast_budget_q_limit_before_any_launch():
     assert lib.ozgemm_stage_scale(8, 8, lim, 14, FAKE, 8, FAKE, lim, e, e) == L.OZGEMM_RANGE
     assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE) == 0
     lib.ozgemm_free()
+
+
+@pytest.mark.parametrize("s", [2, 8, 14, 20])
+def test_accu_budget_matches_oracle(s):
+    M = oz.crt_constants(oz.greedy_moduli(s))[0]
+    if oz.kbits(M, 500) < 1:
+        assert L.lib().ozgemm_bound_budget(s, 500, L.OZGEMM_BOUND_ACCU, ctypes.byref(ctypes.c_int()),
+                                           ctypes.byref(ctypes.c_int())) == L.OZGEMM_RANGE
+        return
+    assert L.ozgemm_bound_budget(s, 500, L.OZGEMM_BOUND_ACCU) == ((M // 2 - 1).bit_length() - 1, oz.ACCU_KMAX)
+
+
+def test_accu_mode_constants_and_limits():
+    assert L.OZGEMM_ACCU_Q_MAX == 2**16
+    # the bound products stay exact in int32 up to that length
+    assert 2 * oz.ACCU_RES**2 * L.OZGEMM_ACCU_Q_MAX < 2**31
+    lib = L.lib()
+    out = (ctypes.byref(ctypes.c_int()), ctypes.byref(ctypes.c_int()))
+    assert lib.ozgemm_bound_budget(14, 2**16 + 1, L.OZGEMM_BOUND_ACCU, *out) == L.OZGEMM_RANGE
+    assert lib.ozgemm_bound_budget(14, 500, 3, *out) == -3
+    assert lib.ozgemm_set_bound(3) == -1
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_ACCU) == 0
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE) == 0
+
+
+@no_gpu_only
+def test_accu_checks_before_any_launch():
+    lib = L.lib()
+    ws = L.ozgemm_workspace_bytes(8, 8, 2**17, 14)
+    assert lib.ozgemm_config(14, 8, 8, 2**17, None, FAKE, ws) == 0
+    Cp = FAKE + (1 << 40)
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_ACCU) == 0
+    e = ctypes.c_void_p(FAKE + (1 << 41))
+    q = L.OZGEMM_ACCU_Q_MAX + 1
+    assert lib.ozgemm_dgemm(8, 8, q, FAKE, 8, FAKE, q, Cp, 8, 14) == L.OZGEMM_RANGE
+    assert lib.ozgemm_stage_scale(8, 8, q, 14, FAKE, 8, FAKE, q, e, e) == L.OZGEMM_RANGE
+    # s_max = 2 and a 1024 x 1024 output: no room for the bound's planes
+    ws = L.ozgemm_workspace_bytes(1024, 1024, 64, 2)
+    assert lib.ozgemm_config(2, 1024, 1024, 64, None, FAKE, ws) == 0
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_ACCU) == 0
+    assert lib.ozgemm_dgemm(1024, 1024, 64, FAKE, 1024, FAKE, 64, Cp, 1024, 2) == L.OZGEMM_WORKSPACE_TOO_SMALL
+    assert lib.ozgemm_stage_scale(1024, 1024, 64, 2, FAKE, 1024, FAKE, 64, e, e) == L.OZGEMM_WORKSPACE_TOO_SMALL
+    assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE) == 0
+    lib.ozgemm_free()
