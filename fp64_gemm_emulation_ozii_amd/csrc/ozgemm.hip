@@ -282,7 +282,7 @@ State g;
 
 // Where one Scheme II call keeps its intermediates and launches its kernels:
 // the configured workspace and stream (ozgemm_dgemm and the stage entry
-// points).
+// points), or the library's fixed device array (ozgemm_dgemm_noalloc).
 struct Ctx {
   char* ws;
   Layout lay;
@@ -566,7 +566,7 @@ int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const d
   return 0;
 }
 
-// Argument checks of ozgemm_dgemm (BLAS style).
+// Argument checks of ozgemm_dgemm and ozgemm_dgemm_noalloc (BLAS style).
 int check_dgemm_args(int m, int n, int q, const double* A, int lda, const double* B, int ldb, const double* C,
                      int ldc, int s) {
   const int st = check_common(m, n, q, A, lda, B, ldb);
@@ -625,6 +625,34 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   OZ_CHECK(launch_crt(rt, m, n, mp, np, e, f, cc, C, ldc, x.stream));
   if (ev) OZ_CHECK(hipEventRecord((*ev)[4], x.stream));
   return OZGEMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The fixed device array of ozgemm_dgemm_noalloc.  Host code never uses the
+// array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device, and is kept here.  The first
+// call on a device also copies the CRT weight table into the array's head.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[OZGEMM_NOALLOC_BYTES];
+
+int noalloc_scratch(char** out) {
+  constexpr int MAX_DEVICES = 64;
+  static char* ptr[MAX_DEVICES] = {};
+  int dev = 0;
+  OZ_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return hip_fail(hipErrorInvalidDevice);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    OZ_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return hip_fail(hipErrorInvalidSymbol);
+    std::vector<double> table(CRT_TABLE_DOUBLES, 0.0);
+    for (int s = 1; s <= OZGEMM_S_MAX; ++s) crt_weights(s, table.data() + (size_t)(s - 1) * OZGEMM_S_MAX * MAX_LIMBS);
+    // the table sits at offset 0 of every layout (Layout::consts)
+    OZ_CHECK(hipMemcpy(p, table.data(), CRT_TABLE_DOUBLES * sizeof(double), hipMemcpyHostToDevice));
+    ptr[dev] = static_cast<char*>(p);
+  }
+  *out = ptr[dev];
+  return 0;
 }
 
 }  // namespace
@@ -731,6 +759,29 @@ int ozgemm_dgemm(int m, int n, int q, const double* A, int lda, const double* B,
       for (auto& x : ev) (void)hipEventDestroy(x);
   }
   return st;
+}
+
+int ozgemm_dgemm_noalloc(int m, int n, int q, const double* A, int lda, const double* B, int ldb, double* C,
+                         int ldc, int s, void* hip_stream) {
+  int st = check_dgemm_args(m, n, q, A, lda, B, ldb, C, ldc, s);
+  if (st) return st;
+  if (m > OZ_MAX_ROWS || n > OZ_MAX_ROWS || (st = check_method_range(q, s))) return OZGEMM_RANGE;
+  size_t rt_min = 0;
+  if (g.bound == OZGEMM_BOUND_ACCU) {
+    int mp0, np0, qp0;
+    dims(m, n, q, &mp0, &np0, &qp0);
+    rt_min = accu_scratch_bytes(mp0, np0, qp0);
+  }
+  const Layout lay = make_layout(m, n, q, s, false, rt_min);
+  if (lay.total > OZGEMM_NOALLOC_BYTES) return OZGEMM_RANGE;
+  if (m == 0 || n == 0) return OZGEMM_OK;
+  char* base = nullptr;
+  if ((st = noalloc_scratch(&base))) return st;
+  int mp, np, qp;
+  dims(m, n, q, &mp, &np, &qp);
+  const Ctx x{base, lay, mp, (hipStream_t)hip_stream, g.bound};
+  return run_dgemm(x, reinterpret_cast<const double*>(base + lay.consts) + (size_t)(s - 1) * OZGEMM_S_MAX * MAX_LIMBS,
+                   m, n, q, A, lda, B, ldb, C, ldc, s, nullptr);
 }
 
 int ozgemm_stage_scale(int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb, int32_t* e,

@@ -25,6 +25,7 @@ OZGEMM_S_MAX = 20
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_Q_MAX = 1 << 27
 OZGEMM_FAST_Q_LIMIT = 1 << 23  # OS II-fast needs q below this
+OZGEMM_NOALLOC_BYTES = 128 << 20  # the fixed device array of ozgemm_dgemm_noalloc
 OZGEMM_MAX_ROWS = 2096896  # 2^21 - 256
 OZGEMM_ONE_PASS_Q_MIN = 4096  # B read once by ozgemm_dgemm for q in [MIN, MAX] (conservative budget)
 OZGEMM_ONE_PASS_Q_MAX = 8192
@@ -46,6 +47,7 @@ EXPORTS = (
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
     "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts", "ozgemm_phase_calls",
+    "ozgemm_dgemm_noalloc",
 )
 
 _lib = None
@@ -75,6 +77,7 @@ def lib():
         "ozgemm_free": (c_int, []),
         "ozgemm_strerror": (ctypes.c_char_p, [c_int]),
         "ozgemm_dgemm": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, c_int, c_int]),
+        "ozgemm_dgemm_noalloc": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, c_int, c_int, vp]),
         "ozgemm_moduli": (c_int, [c_int, ip]),
         "ozgemm_kbits": (c_int, [c_int, c_int]),
         "ozgemm_plane_dims": (c_int, [c_int, c_int, c_int, ip, ip, ip]),
@@ -218,6 +221,11 @@ def ozgemm_free() -> int:
 def ozgemm_dgemm(m, n, q, A, lda, B, ldb, C, ldc, s, check: bool = True) -> int:
     st = lib().ozgemm_dgemm(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, s)
     return _check(st, "ozgemm_dgemm") if check else st
+
+
+def ozgemm_dgemm_noalloc(m, n, q, A, lda, B, ldb, C, ldc, s, stream=None, check: bool = True) -> int:
+    st = lib().ozgemm_dgemm_noalloc(m, n, q, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, s, _stream(stream))
+    return _check(st, "ozgemm_dgemm_noalloc") if check else st
 
 
 def ozgemm_stage_scale(m, n, q, s, A, lda, B, ldb, e, f, check: bool = True) -> int:

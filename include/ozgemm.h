@@ -130,6 +130,35 @@ int ozgemm_dgemm(int m, int n, int q,
                  const double *A, int lda, const double *B, int ldb,
                  double *C, int ldc, int s);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): C <- A B
+ * exactly as ozgemm_dgemm computes it (same kernels, same bit budget as set
+ * by ozgemm_set_bound, same results), with every intermediate in a fixed
+ * device array of OZGEMM_NOALLOC_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends.  Needs no ozgemm_config; work goes
+ * on `hip_stream` (a hipStream_t, NULL for the null stream) and the call
+ * returns without synchronising.  The caller passes device pointers A, B, C
+ * as for ozgemm_dgemm.  Calls no hipMalloc, hipFree or other allocating
+ * routine.  The first call on a device looks up the array's address and
+ * copies a 16 KB constant table into it (a blocking host-to-device copy), so
+ * make one call outside any graph capture first.
+ * The array is shared by every call on that GPU and keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host
+ * threads) race on it and give wrong results.  Products are not cut into K
+ * parts here (q >= 2^17 walks sequential K blocks).
+ * Errors: those of ozgemm_dgemm (argument numbers 1..10; no
+ * OZGEMM_NOT_CONFIGURED), and OZGEMM_RANGE when the intermediates of this
+ * shape need more than OZGEMM_NOALLOC_BYTES: s (m_pad + n_pad) q_pad bytes of
+ * residue planes, s m_pad n_pad of product residues, 2 KB per padded row of
+ * A for partial row maxima, and small arrays (m_pad, n_pad: m, n rounded up
+ * to 256; q_pad: q rounded up to 128).  ozgemm_workspace_bytes(m, n, q, s)
+ * <= OZGEMM_NOALLOC_BYTES is enough; for example 2048 x 2048 x 1024 fits at
+ * s = 14, and 1024^3 at every s. */
+#define OZGEMM_NOALLOC_BYTES (128 << 20)
+int ozgemm_dgemm_noalloc(int m, int n, int q,
+                         const double *A, int lda, const double *B, int ldb,
+                         double *C, int ldc, int s, void *hip_stream);
+
 /* ---------------------------------------------------------------------- */
 /* Host-only introspection (no device needed)                              */
 /* ---------------------------------------------------------------------- */
