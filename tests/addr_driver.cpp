@@ -1,0 +1,371 @@
+// CPU emulation of every memory address the product, residue and CRT kernels
+// form, for one launch configuration per input line.  It restates the index
+// arithmetic of the kernels in csrc/ (gemm_i8.hip, residue.hip, crt.hip,
+// accu.hip) on the host, with the grid helpers of csrc/gemm_grid.h itself,
+// and checks that every global load and store stays inside its buffer and
+// every LDS access inside the block's allocation.
+//
+// Input lines (all sizes padded as the library pads them):
+//   gemm  <form> <m_pad> <n_pad> <q_pad> <s> <cus> <parts> <per> <k_begin> <k_slices> <swz_bug>
+//         form: main (residue output, one block per tile), persist (the same,
+//         cus blocks walking the tiles), acc (residue output added to the
+//         earlier K blocks' residues), short, ct (int32 output, MT = 32)
+//   plan  <m_pad> <n_pad> <q_pad> <nplanes_a> <nplanes_b> then nout lines "a0 b0 count out"
+//         (preceded by "<nout>")
+//   reduce <m_pad> <n_pad> <s> <parts>
+//   residue <rows> <rows_pad> <q> <q_pad> <s> <rs> <ls> <one_pass>
+//   crt <m> <n> <m_pad> <n_pad> <s> <ldc>
+// Output: one line "ok <accesses>" or "bad <what> ..." per input line.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../fp64_gemm_emulation_ozii_amd/csrc/gemm_grid.h"
+
+namespace {
+
+long g_checks = 0;
+std::string g_bad;
+
+void check(bool ok, const char* what, long a, long b) {
+  ++g_checks;
+  if (!ok && g_bad.empty()) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s %ld %ld", what, a, b);
+    g_bad = buf;
+  }
+}
+
+// [off, off + len) inside [0, size)
+void in_range(long off, long len, long size, const char* what) { check(off >= 0 && off + len <= size, what, off, size); }
+
+int swz128(int row, bool bug) { return bug ? (row & 7) : (((row >> 1) ^ (row << 2)) & 7); }
+int swz64(int row) { return (row >> 2) & 3; }
+
+struct Plan {
+  int a0, b0, count, out;
+};
+
+// The main product kernel: BM = BN = 256, BK = 128 (or 32 with the planted
+// swizzle bug), 2 x 2 wavefronts.  MT = 16 for residue output, 32 for int32.
+void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bool ct, bool acc_rt, int parts,
+               int k_begin, int k_slices, bool multi, const std::vector<Plan>& plan, int a_planes, int b_planes,
+               bool swz_bug) {
+  const int BM = 256, BN = 256, BK = swz_bug ? 32 : 128, WM = 2, WN = 2, NW = 4;
+  const int CPR = BK / 16, ROWS_PER_KB = 1024 / BK;
+  const int A_LOADS = BM * BK / 1024 / NW, B_LOADS = BN * BK / 1024 / NW, LPW = A_LOADS + B_LOADS;
+  const int WTM = BM / WM, WTN = BN / WN;
+  const int MT = ct ? 32 : 16, KSTEP = 1024 / MT, CPS = KSTEP / 16, FM = WTM / MT, FN = WTN / MT;
+  const int NKS = BK / KSTEP > 0 ? BK / KSTEP : 1, NF = FM + FN;
+  const bool staged = !ct && !acc_rt;  // residue-only output goes through LDS
+  const int CS = BM + 16;
+  const long OPERANDS = 2L * (BM + BN) * BK;
+  const long STAGE_OFF = persist ? (long)(BM + BN) * BK : 0;
+  const long SMEM = staged && STAGE_OFF + (long)BN * CS > OPERANDS ? STAGE_OFF + (long)BN * CS : OPERANDS;
+  const int tiles_m = m_pad / BM, tiles_n = n_pad / BN, tiles = tiles_m * tiles_n;
+  const int nk = q_pad / BK;
+  const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad, plane = (long)m_pad * n_pad;
+  const int nplanes = multi ? (int)plan.size() : s * (parts > 1 ? parts : 1);
+  const long nblocks = (long)nplanes * tiles;
+  const long out_planes = multi ? 0 : nplanes;
+  int out_max = 0;
+  for (const Plan& p : plan) out_max = p.out + 1 > out_max ? p.out + 1 : out_max;
+  const long out_size = (multi ? out_max : out_planes) * plane * (ct ? 4 : 1);
+  const long A_size = (long)(multi ? a_planes : s) * a_plane, B_size = (long)(multi ? b_planes : s) * b_plane;
+  const long kb_stride = (long)ROWS_PER_KB * q_pad;
+  const int grid = persist ? cus : (int)nblocks;
+  for (int b = 0; b < grid; ++b) {
+    for (long L = b; L < nblocks; L += grid) {
+      int tt, mi, nj;
+      oz::tile_of_block<4>((int)L, nplanes, tiles_m, tiles_n, tt, mi, nj);
+      check(tt >= 0 && tt < nplanes && mi >= 0 && mi < tiles_m && nj >= 0 && nj < tiles_n, "tile", L, nblocks);
+      const int m0 = mi * BM, n0 = nj * BN;
+      int out_t = tt, part = 0, a0, b0, count = 1;
+      if (!multi) {
+        part = tt / s;
+        tt -= part * s;
+        a0 = b0 = tt;
+      } else {
+        a0 = plan[tt].a0;
+        b0 = plan[tt].b0;
+        count = plan[tt].count;
+        out_t = plan[tt].out;
+      }
+      const long Ag = (long)a0 * a_plane + (long)m0 * q_pad, Bg = (long)b0 * b_plane + (long)n0 * q_pad;
+      const int kfirst = k_begin + part * k_slices;
+      const int nkt = multi ? nk * count : (k_slices < nk - kfirst ? k_slices : nk - kfirst);
+      check(nkt >= 1, "empty tile", L, nkt);
+      for (int kk = 0; kk < nkt; ++kk) {
+        long k0 = (long)(kfirst + kk) * BK, ga = Ag, gb = Bg;
+        if (multi) {
+          const int u = kk / nk;
+          k0 = (long)(kk - u * nk) * BK;
+          ga += u * a_plane;
+          gb -= u * b_plane;
+        }
+        for (int w = 0; w < NW; ++w)
+          for (int li = 0; li < LPW; ++li)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int lrow = lane / CPR;
+              const long src0 = (long)lrow * q_pad + (((lane % CPR) ^ swz128(lrow, swz_bug)) * 16);
+              const long src1 = (long)lrow * q_pad + (((lane % CPR) ^ swz128(lrow + ROWS_PER_KB, swz_bug)) * 16);
+              const long lds_base = (kk & 1) * (long)(BM + BN) * BK;
+              if (li < A_LOADS) {
+                const int blk = w * A_LOADS + li;
+                in_range(ga + blk * kb_stride + k0 + ((blk & 1) ? src1 : src0), 16, A_size, "gemm A load");
+                in_range(lds_base + blk * 1024L + lane * 16, 16, SMEM, "gemm A lds");
+              } else {
+                const int blk = w * B_LOADS + (li - A_LOADS);
+                in_range(gb + blk * kb_stride + k0 + ((blk & 1) ? src1 : src0), 16, B_size, "gemm B load");
+                in_range(lds_base + BM * (long)BK + blk * 1024L + lane * 16, 16, SMEM, "gemm B lds");
+              }
+            }
+      }
+      // fragment reads (every step of a slice, both buffers)
+      if (L == b)
+        for (int buf = 0; buf < 2; ++buf)
+          for (int ks = 0; ks < NKS; ++ks)
+            for (int w = 0; w < NW; ++w)
+              for (int f = 0; f < NF; ++f)
+                for (int lane = 0; lane < 64; ++lane) {
+                  const int wm = w / WN, wn = w % WN, kc = ks * CPS + lane / MT;
+                  check(kc < CPR, "fragment chunk", kc, CPR);
+                  const long base = buf * (long)(BM + BN) * BK;
+                  if (f < FN) {
+                    const int row = wn * WTN + f * MT + lane % MT;
+                    in_range(base + BM * (long)BK + row * (long)BK + ((kc ^ swz128(row, swz_bug)) * 16), 16, SMEM,
+                             "gemm B fragment");
+                  } else {
+                    const int row = wm * WTM + (f - FN) * MT + lane % MT;
+                    in_range(base + row * (long)BK + ((kc ^ swz128(row, swz_bug)) * 16), 16, SMEM, "gemm A fragment");
+                  }
+                }
+      // epilogue
+      const long ostride = ct ? 4 : 1;
+      for (int w = 0; w < NW; ++w) {
+        const int wm = w / WN, wn = w % WN;
+        for (int i = 0; i < FM; ++i)
+          for (int j = 0; j < FN; ++j)
+            for (int lane = 0; lane < 64; ++lane)
+              for (int g = 0; g < MT * MT / 64 / 4; ++g) {
+                const int lcol = wn * WTN + j * MT + lane % MT;
+                const int lrow4 = wm * WTM + i * MT + 8 * g + 4 * (lane / MT);
+                const long off = (long)out_t * plane + (long)(n0 + lcol) * m_pad + m0 + lrow4;
+                if (staged) {
+                  in_range(STAGE_OFF + (long)lcol * CS + lrow4, 4, SMEM, "gemm stage write");
+                } else {
+                  if (acc_rt) in_range(off, 4, out_size, "gemm residue read");
+                  in_range(off * ostride, 4 * ostride, out_size, "gemm direct store");
+                }
+              }
+      }
+      if (staged) {
+        const int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16, COLS_PER_STORE = 64 / LANES_PER_COL;
+        for (int w = 0; w < NW; ++w)
+          for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int lcol = w * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
+              const int rch = (lane % LANES_PER_COL) * 16;
+              in_range(STAGE_OFF + (long)lcol * CS + rch, 16, SMEM, "gemm stage read");
+              in_range((long)out_t * plane + (long)(n0 + lcol) * m_pad + m0 + rch, 16, out_size, "gemm staged store");
+            }
+      }
+    }
+  }
+  check(SMEM <= 160 * 1024, "lds size", SMEM, 160 * 1024);
+}
+
+// The short-K kernel: 256 x 128 tiles, 64-byte slices in three stages.
+void gemm_short(int m_pad, int n_pad, int q_pad, int s) {
+  const int BM = 256, BN = 128, BK = 64, NW = 4, STAGES = 3, WN = 2;
+  const int CPR = 4, A_LOADS = 4, B_LOADS = 2, LPW = 6, WTM = 128, WTN = 64, FM = 4, FN = 2, NF = 6;
+  const long STAGE = (long)(BM + BN) * BK, SMEM = STAGES * STAGE;
+  const int CS = BM + 16;
+  const int tiles_m = m_pad / BM, tiles_n = n_pad / BN;
+  const long nblocks = (long)tiles_m * tiles_n * s;
+  const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad, plane = (long)m_pad * n_pad;
+  const long kb_stride = 16L * q_pad;
+  const int nkt = q_pad / BK;
+  for (long L = 0; L < nblocks; ++L) {
+    int t, mi, nj;
+    oz::tile_of_block<4>((int)L, s, tiles_m, tiles_n, t, mi, nj);
+    const int m0 = mi * BM, n0 = nj * BN;
+    const long Ag = t * a_plane + (long)m0 * q_pad, Bg = t * b_plane + (long)n0 * q_pad;
+    for (int kk = 0; kk < nkt; ++kk)
+      for (int w = 0; w < NW; ++w)
+        for (int li = 0; li < LPW; ++li)
+          for (int lane = 0; lane < 64; ++lane) {
+            const long src = (long)(lane / CPR) * q_pad + (((lane % CPR) ^ swz64(lane / CPR)) * 16);
+            const long base = (kk % STAGES) * STAGE;
+            if (li < A_LOADS) {
+              const int blk = w * A_LOADS + li;
+              in_range(Ag + blk * kb_stride + (long)kk * BK + src, 16, s * a_plane, "short A load");
+              in_range(base + blk * 1024L + lane * 16, 16, SMEM, "short A lds");
+            } else {
+              const int blk = w * B_LOADS + (li - A_LOADS);
+              in_range(Bg + blk * kb_stride + (long)kk * BK + src, 16, s * b_plane, "short B load");
+              in_range(base + BM * (long)BK + blk * 1024L + lane * 16, 16, SMEM, "short B lds");
+            }
+          }
+    if (L == 0)
+      for (int buf = 0; buf < STAGES; ++buf)
+        for (int ks = 0; ks < 2; ++ks)
+          for (int w = 0; w < NW; ++w)
+            for (int f = 0; f < NF; ++f)
+              for (int lane = 0; lane < 64; ++lane) {
+                const int wm = w / WN, wn = w % WN, kc = ks * 2 + (lane >> 5);
+                const long base = buf * STAGE;
+                if (f < FN) {
+                  const int row = wn * WTN + f * 32 + (lane & 31);
+                  in_range(base + BM * (long)BK + row * (long)BK + ((kc ^ swz64(row)) * 16), 16, SMEM, "short B frag");
+                } else {
+                  const int row = wm * WTM + (f - FN) * 32 + (lane & 31);
+                  in_range(base + row * (long)BK + ((kc ^ swz64(row)) * 16), 16, SMEM, "short A frag");
+                }
+              }
+    for (int w = 0; w < NW; ++w) {
+      const int wm = w / WN, wn = w % WN;
+      for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
+          for (int lane = 0; lane < 64; ++lane)
+            for (int g = 0; g < 4; ++g)
+              in_range((long)(wn * WTN + j * 32 + (lane & 31)) * CS + wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5), 4,
+                       SMEM, "short stage write");
+      const int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16, COLS_PER_STORE = 64 / LANES_PER_COL;
+      for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int lcol = w * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
+          const int rch = (lane % LANES_PER_COL) * 16;
+          in_range((long)lcol * CS + rch, 16, SMEM, "short stage read");
+          in_range((long)t * plane + (long)(n0 + lcol) * m_pad + m0 + rch, 16, s * plane, "short store");
+        }
+    }
+  }
+}
+
+// Sum of the K parts' residues: 16 bytes per thread.
+void reduce(int m_pad, int n_pad, int s, int P) {
+  const long plane = (long)m_pad * n_pad, chunks = plane / 16, threads = chunks * s;
+  for (long gid = 0; gid < (threads + 255) / 256 * 256; gid += 1) {
+    if (gid >= chunks * s) continue;
+    const long t = gid / chunks, off = (gid - t * chunks) * 16;
+    for (int p = 0; p < P; ++p) in_range(((long)p * s + t) * plane + off, 16, (long)P * s * plane, "reduce load");
+    in_range(t * plane + off, 16, (long)s * plane, "reduce store");
+  }
+}
+
+// The residue kernels (and the accu band kernel, the same tile walk): a tile
+// of 32 rows x 128 entries per block, 16-byte stores per modulus.
+void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, bool one_pass) {
+  const long plane_stride = (long)rows_pad * q_pad;
+  const long src_size = rows < 1 ? 0 : (rows - 1) * rs + (q - 1) * ls + 1;
+  if (!one_pass) {
+    for (int by = 0; by < rows_pad / 32; ++by)
+      for (int bx = 0; bx < q_pad / 128; ++bx)
+        for (int tid = 0; tid < 256; ++tid) {
+          const int r0 = by * 32, l0 = bx * 128;
+          if (rows >= 1) {
+            if (rs == 1) {
+              const int r = tid & 31, lsub = tid >> 5;
+              for (int it = 0; it < 16; ++it) {
+                const long rr = r0 + r < rows - 1 ? r0 + r : rows - 1;
+                const long ll = l0 + lsub + 8 * it < q - 1 ? l0 + lsub + 8 * it : q - 1;
+                in_range(rr + ll * ls, 1, src_size, "residue load (rows contiguous)");
+              }
+            } else {
+              const int l = tid & 127, rsub = tid >> 7;
+              for (int it = 0; it < 16; ++it) {
+                const long ll = l0 + l < q - 1 ? l0 + l : q - 1;
+                const long rr = r0 + rsub + 2 * it < rows - 1 ? r0 + rsub + 2 * it : rows - 1;
+                in_range(ll + rr * rs, 1, src_size, "residue load (inner contiguous)");
+              }
+            }
+          }
+          const int r = tid >> 3, cseg = (tid & 7) * 16;
+          for (int t = 0; t < s; ++t)
+            in_range(t * plane_stride + (long)(r0 + r) * q_pad + l0 + cseg, 16, s * plane_stride, "residue store");
+          in_range((long)bx * rows_pad + r0 + r, 1, (long)(q_pad / 128) * rows_pad, "band partial sum");
+        }
+  } else {
+    for (int j = 0; j < rows_pad; ++j) {
+      if (j < rows)
+        for (int l = 0; l < q; ++l) in_range(j * rs + l, 1, src_size, "column residue load");
+      for (int seg = 0; seg < q_pad / 16; ++seg)
+        for (int t = 0; t < s; ++t)
+          in_range(t * plane_stride + (long)j * q_pad + 16L * seg, 16, s * plane_stride, "column residue store");
+    }
+  }
+}
+
+// CRT: four rows of one column per thread, two columns per thread pass.
+void crt(int m, int n, int m_pad, int n_pad, int s, long ldc) {
+  const long plane = (long)m_pad * n_pad;
+  const int NG = (s + 3) / 4;
+  const int gx = (m + 1023) / 1024, gy = (n + 1) / 2 < 65535 ? (n + 1) / 2 : 65535;
+  for (int bx = 0; bx < gx; ++bx)
+    for (int tx = 0; tx < 256; ++tx) {
+      const long i0 = ((long)bx * 256 + tx) * 4;
+      if (i0 >= m) continue;
+      for (int by = 0; by < gy; ++by)
+        for (long j = by; j < n; j += gy) {
+          for (int t = 0; t < 4 * NG; ++t)
+            if (t < 4 * (NG - 1) || t < s) in_range(j * m_pad + i0 + t * plane, 4, s * plane, "crt load");
+          for (int u = 0; u < 4; ++u)
+            if (i0 + u < m) in_range(j * ldc + i0 + u, 1, (n - 1) * ldc + m, "crt store");
+        }
+    }
+}
+
+}  // namespace
+
+int main() {
+  char cmd[16];
+  while (std::scanf("%15s", cmd) == 1) {
+    g_checks = 0;
+    g_bad.clear();
+    if (!std::strcmp(cmd, "gemm")) {
+      char form[16];
+      int mp, np, qp, s, cus, parts, per, kb, ks, bug;
+      if (std::scanf("%15s %d %d %d %d %d %d %d %d %d %d", form, &mp, &np, &qp, &s, &cus, &parts, &per, &kb, &ks,
+                     &bug) != 11)
+        return 1;
+      (void)per;
+      if (!std::strcmp(form, "short"))
+        gemm_short(mp, np, qp, s);
+      else
+        gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist"), !std::strcmp(form, "ct"), !std::strcmp(form, "acc"),
+                  parts, kb, ks, false, {}, 0, 0, bug != 0);
+    } else if (!std::strcmp(cmd, "plan")) {
+      int mp, np, qp, na, nb, nout;
+      if (std::scanf("%d %d %d %d %d %d", &mp, &np, &qp, &na, &nb, &nout) != 6) return 1;
+      std::vector<Plan> plan(nout);
+      for (auto& p : plan)
+        if (std::scanf("%d %d %d %d", &p.a0, &p.b0, &p.count, &p.out) != 4) return 1;
+      gemm_main(mp, np, qp, 1, 0, false, true, false, 1, 0, qp / 128, true, plan, na, nb, false);
+    } else if (!std::strcmp(cmd, "reduce")) {
+      int mp, np, s, P;
+      if (std::scanf("%d %d %d %d", &mp, &np, &s, &P) != 4) return 1;
+      reduce(mp, np, s, P);
+    } else if (!std::strcmp(cmd, "residue")) {
+      int rows, rows_pad, q, q_pad, s, one;
+      long rs, ls;
+      if (std::scanf("%d %d %d %d %d %ld %ld %d", &rows, &rows_pad, &q, &q_pad, &s, &rs, &ls, &one) != 8) return 1;
+      residue(rows, rows_pad, q, q_pad, s, rs, ls, one != 0);
+    } else if (!std::strcmp(cmd, "crt")) {
+      int m, n, mp, np, s;
+      long ldc;
+      if (std::scanf("%d %d %d %d %d %ld", &m, &n, &mp, &np, &s, &ldc) != 6) return 1;
+      crt(m, n, mp, np, s, ldc);
+    } else {
+      return 1;
+    }
+    if (g_bad.empty())
+      std::printf("ok %ld\n", g_checks);
+    else
+      std::printf("bad %s\n", g_bad.c_str());
+    std::fflush(stdout);
+  }
+  return 0;
+}
