@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--bound", choices=["conservative", "fast", "accu"], default="conservative",
                    help="bit budget: the k of the Ozaki II notes section 5, or OS II-fast / OS II-accu (section 9)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--panels", type=int, default=0,
+                   help="column panels of the CRT/product pipeline (ozgemm_set_panels): 0 or 1 off, P >= 2 forced")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     p.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (default: host CPUs, <= 16)")
     p.add_argument("--settle-seconds", type=float, default=2.0,
@@ -195,6 +197,7 @@ def main():
     L.ozgemm_config(s, m, n, q, stream=stream)
     if args.bound != "conservative":
         L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if args.bound == "fast" else L.OZGEMM_BOUND_ACCU)
+    L.ozgemm_set_panels(args.panels)
 
     def call():
         L.ozgemm_dgemm(m, n, q, Ad, m, Bd, q, Cd, m, s)
@@ -278,7 +281,8 @@ def main():
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": workload, "m": m, "n": n, "q": q, "s": s, "phi": phi, "seed": args.seed,
-                   "output_dtype": "f64", "layout": "column-major NN", "bit_budget": args.bound},
+                   "output_dtype": "f64", "layout": "column-major NN", "bit_budget": args.bound,
+                   "panels": args.panels},
         "roofline": {
             "bound": "mfma",
             "kernel": "gemm_i8_kernel",

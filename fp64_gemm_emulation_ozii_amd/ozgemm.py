@@ -22,6 +22,7 @@ OZGEMM_RANGE = 2
 OZGEMM_WORKSPACE_TOO_SMALL = 3
 OZGEMM_HIP_ERROR = 4
 OZGEMM_S_MAX = 20
+OZGEMM_PANELS_MAX = 16
 OZGEMM_Q_LIMIT = 1 << 17
 OZGEMM_Q_MAX = 1 << 27
 OZGEMM_FAST_Q_LIMIT = 1 << 23  # OS II-fast needs q below this
@@ -47,7 +48,7 @@ EXPORTS = (
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
     "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts", "ozgemm_phase_calls",
-    "ozgemm_dgemm_noalloc",
+    "ozgemm_dgemm_noalloc", "ozgemm_set_panels",
 )
 
 _lib = None
@@ -74,6 +75,7 @@ def lib():
         "ozgemm_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
         "ozgemm_config": (c_int, [c_int, c_int, c_int, c_int, vp, vp, c_size]),
         "ozgemm_set_stream": (c_int, [vp]),
+        "ozgemm_set_panels": (c_int, [c_int]),
         "ozgemm_free": (c_int, []),
         "ozgemm_strerror": (ctypes.c_char_p, [c_int]),
         "ozgemm_dgemm": (c_int, [c_int, c_int, c_int, vp, c_int, vp, c_int, vp, c_int, c_int]),
@@ -206,6 +208,11 @@ def ozgemm_set_stream(stream=None) -> int:
     """Later calls go on `stream`.  Work already queued on the previous stream
     is not ordered before them: the caller orders the two streams."""
     return _check(lib().ozgemm_set_stream(_stream(stream)), "ozgemm_set_stream")
+
+
+def ozgemm_set_panels(panels: int) -> int:
+    """Column panels of the ozgemm_dgemm pipeline: 0 automatic, 1 off, P forced."""
+    return _check(lib().ozgemm_set_panels(panels), "ozgemm_set_panels")
 
 
 def ozgemm_free() -> int:

@@ -64,6 +64,7 @@ extern "C" {
 #define OZGEMM_FAST_Q_LIMIT (1 << 23) /* OS II-fast needs q below this: its row-norm sums of q terms of at most 2^40 stay exact in 64 bits */
 #define OZGEMM_MAX_ROWS 2096896       /* largest m and n: 2^21 - 256, so that the rows padded to 256 form at most 65535 tiles of 32 */
 #define OZGEMM_EXP_NONFINITE 0x7fffffff /* exponent of a row/column holding Inf/NaN */
+#define OZGEMM_PANELS_MAX 16          /* most column panels of the pipeline (ozgemm_set_panels) */
 #define OZGEMM_ONE_PASS_Q_MIN 4096    /* ozgemm_dgemm reads B once for Q_MIN <= q <= Q_MAX (conservative budget) */
 #define OZGEMM_ONE_PASS_Q_MAX 8192
 
@@ -101,6 +102,26 @@ int ozgemm_config(int s_max, int max_m, int max_n, int max_q,
 
 /* Change the stream used by later calls. */
 int ozgemm_set_stream(void *hip_stream);
+
+/* Column-panel pipeline of ozgemm_dgemm (Ozaki II notes §8 and §11: the
+ * CRT of one part of C overlaps the products of the next part).  C is cut
+ * into P column panels of whole 256-column tiles; each panel's B residues
+ * and product residues are contiguous, its product is one launch, and its
+ * CRT runs on a second stream of the library (default priority, created at
+ * the first pipelined call and released by ozgemm_free or ozgemm_config),
+ * ordered by events, while the next panel's product runs.  The call's
+ * stream waits for the last CRT, so the call stays one unit of work on that
+ * stream (and can be captured into a graph like an unpipelined one).
+ * Results are identical to the unpipelined path.
+ *   panels = 0 or 1: no pipeline (the default);
+ *   2 <= panels <= OZGEMM_PANELS_MAX: that many panels whenever the shape
+ *     allows (q < 2^17, n_pad >= 512, one K part per panel product).
+ * It is off by default because on MI355X the persistent product grid holds
+ * every compute unit, so the CRT only fills gaps: measured 1.5-2% slower
+ * than the plain call at 16384 x 16384 x 1024 and 8192^3.
+ * The setting persists until changed; ozgemm_free resets it to 0.
+ * Returns 0, or -1 for panels outside 0..OZGEMM_PANELS_MAX. */
+int ozgemm_set_panels(int panels);
 
 /* Forget the configuration (the workspace stays the caller's). */
 int ozgemm_free(void);
@@ -367,7 +388,9 @@ int ozgemm_scheme1_stage_accumulate(int m, int n, int q, int k, int variant,
  * around its four phases (up to 4096 calls).  ozgemm_phase_ms adds, over the
  * calls since timing was enabled, the milliseconds of [scale, residue, gemm,
  * crt] into ms_out[0..3] (synchronising on the events) and the number of
- * calls into *calls.  ozgemm_phase_calls writes the same four times of each
+ * calls into *calls (for a pipelined call, see ozgemm_set_panels: residue =
+ * A's residues, gemm = B's residues, the products and the overlapped CRTs,
+ * crt = the last panel's CRT tail).  ozgemm_phase_calls writes the same four times of each
  * call, ms_out[4c + p] for call c < min(calls, max_calls), and the number of
  * recorded calls into *calls (either pointer may be NULL when max_calls is
  * 0).  Disabling discards the events. */
