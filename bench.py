@@ -8,8 +8,10 @@ HPL-like inputs with phi = 1 (seed 0).
 
 Prints ONE JSON line with the throughput (2 m n q / time, in emulated FP64
 TFLOPS), a roofline object for the dominant kernel (the int8 GEMM, priced
-against the MI355X dense int8 peak), and the CPU oracle timed on a bounded
-sample of the same workload.
+against the MI355X dense int8 peak), the CPU oracle timed on a bounded
+sample of the same workload, and as context the rate a register-only MFMA
+loop sustains under the power limit, correct bits, and the native FP64
+GEMM (torch.matmul) on the same inputs.
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ def parse():
     p.add_argument("--bits-entries", type=int, default=4096, help="sampled output entries for the correct bits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-accuracy", action="store_true")
+    p.add_argument("--no-native", action="store_true", help="skip the native FP64 matmul context figures")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the matrix-core rate probe")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run one plain device copy of this many bytes (calibrates HBM byte counters)")
     return p.parse_args()
@@ -97,6 +101,34 @@ def _oracle_worker_block(Arows):
     import numpy as np
     B = _W["B"]
     return oz.dgemm_block(Arows, B, _W["s"], np.arange(Arows.shape[0]), np.arange(B.shape[1]), bound=_W["bound"])
+
+
+def mfma_loop_ceiling(L, dev, target_ms: float = 200.0, runs: int = 3):
+    """Sustained int8 rate of a register-only MFMA loop on every CU
+    (ozgemm_mfma_ceiling), timed with HIP events: the median of `runs` runs
+    of about target_ms each."""
+    import torch
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(4 * blocks, dtype=torch.int32, device=dev)
+
+    def timed(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.ozgemm_mfma_ceiling(blocks, steps, 1, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    steps = 16384
+    timed(steps)                     # first launch: code load and clock ramp
+    ms = timed(steps)
+    steps = max(16384, min(1 << 26, int(steps * target_ms / max(ms, 1e-3))))
+    times = [timed(steps) for _ in range(runs)]
+    med = statistics.median(times)
+    ops = float(blocks) * 4 * steps * 2**20
+    tops = ops / (med * 1e-3) / 1e12
+    return {"tops": round(tops, 2), "ms": round(med, 3), "blocks": blocks, "steps": steps,
+            "instruction": "v_mfma_i32_16x16x64_i8", "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
 def host_cpus() -> int:
@@ -168,6 +200,7 @@ def cpu_baseline(A, B, s, q, target_s, Cg_full_getter, bound="conservative", wor
         "seconds": dt,
         "host_cpus": cpus,
         "nproc": os.cpu_count(),
+        "extrapolated_full_seconds": round(dt * m * n / entries, 1),  # the whole output, extrapolated
         "parity_entries": entries,
         "parity_bit_exact": exact,
     }
@@ -308,6 +341,15 @@ def main():
         },
     }
 
+    # The int8 rate the matrix cores sustain on their own under the power
+    # limit (register-only MFMA loop in the product kernel's issue order,
+    # about 200 ms per run on a chip that is already warm), beside the
+    # clock-rate figure the roofline uses
+    if not args.no_ceiling:
+        ceil = mfma_loop_ceiling(L, dev)
+        out["mfma_loop_ceiling"] = ceil
+        out["gemm_frac_of_mfma_loop_ceiling"] = round(achieved / ceil["tops"], 4)
+
     def block_getter(rows, cols):
         r = torch.from_numpy(rows).to(dev)
         c = torch.from_numpy(cols).to(dev)
@@ -322,6 +364,25 @@ def main():
         native = (torch.from_numpy(A[ri, :]).to(dev) * torch.from_numpy(B[:, ci].T.copy()).to(dev)).sum(1)
         out["correct_bits_native_fp64_dot"] = round(correct_bits_many(native.cpu().numpy(), A, B, ri, ci), 2)
         out["correct_bits_entries"] = int(len(ri))
+        if not args.no_native:
+            # context: the native FP64 GEMM of the same inputs (torch.matmul,
+            # the vendor BLAS), its time and its correct bits on the same entries
+            Cn = torch.empty((n, m), dtype=torch.float64, device=dev)   # C^T = B^T A^T, row-major
+            torch.matmul(Bd, Ad, out=Cn)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for e0, e1 in evs:
+                e0.record()
+                torch.matmul(Bd, Ad, out=Cn)
+                e1.record()
+            torch.cuda.synchronize()
+            nms = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+            Cv = Cn[torch.from_numpy(ci).to(dev), torch.from_numpy(ri).to(dev)].cpu().numpy()
+            out["native_fp64_matmul"] = {
+                "ms": round(nms, 4), "tflops": round(2.0 * m * n * q / (nms * 1e-3) / 1e12, 3),
+                "correct_bits": round(correct_bits_many(Cv, A, B, ri, ci), 2), "calls": len(evs),
+            }
+            del Cn
 
     if not args.no_cpu_baseline and args.bound == "accu":
         # OS II-accu's row and column bit counts depend on all of A and B, so a

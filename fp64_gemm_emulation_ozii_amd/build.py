@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libozgemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["ozgemm.hip", "scale.hip", "residue.hip", "gemm_i8.hip", "crt.hip", "scheme1.hip", "accu.hip"]
+SOURCES = ["ozgemm.hip", "scale.hip", "residue.hip", "gemm_i8.hip", "crt.hip", "scheme1.hip", "accu.hip", "probe.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -147,4 +147,9 @@ hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const d
                                  int n_pad, int q_pad, int K2, int kmax, int8_t* Aplanes, int8_t* Bplanes,
                                  int32_t* psumA, char* scratch, int32_t* e, int32_t* f, hipStream_t st);
 
+// Measurement aid (probe.hip): `blocks` workgroups of four wavefronts run
+// `steps` register-only steps of 32 v_mfma_i32_16x16x64_i8 each; sink
+// receives 4 blocks words.
+hipError_t launch_mfma_ceiling(int blocks, int steps, uint32_t seed, uint32_t* sink, hipStream_t st);
+
 }  // namespace oz

@@ -1189,4 +1189,12 @@ int ozgemm_phase_calls(double* ms_out, int max_calls, int* calls) {
   return OZGEMM_OK;
 }
 
+int ozgemm_mfma_ceiling(int blocks, int steps, unsigned seed, unsigned* sink, void* hip_stream) {
+  if (blocks < 1 || blocks > (1 << 20)) return -1;
+  if (steps < 1) return -2;
+  if (sink == nullptr) return -4;
+  OZ_CHECK(launch_mfma_ceiling(blocks, steps, seed, sink, (hipStream_t)hip_stream));
+  return OZGEMM_OK;
+}
+
 }  // extern "C"

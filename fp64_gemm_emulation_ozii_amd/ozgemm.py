@@ -48,7 +48,7 @@ EXPORTS = (
     "ozgemm_scheme1_beta", "ozgemm_scheme1_outputs", "ozgemm_scheme1_workspace_bytes", "ozgemm_scheme1_dgemm",
     "ozgemm_scheme1_stage_split", "ozgemm_scheme1_stage_products", "ozgemm_scheme1_stage_accumulate",
     "ozgemm_set_bound", "ozgemm_bound_budget", "ozgemm_gemm_parts", "ozgemm_phase_calls",
-    "ozgemm_dgemm_noalloc", "ozgemm_set_panels",
+    "ozgemm_dgemm_noalloc", "ozgemm_set_panels", "ozgemm_mfma_ceiling",
 )
 
 _lib = None
@@ -93,6 +93,7 @@ def lib():
         "ozgemm_timing": (c_int, [c_int]),
         "ozgemm_phase_ms": (c_int, [ctypes.POINTER(ctypes.c_double), ip]),
         "ozgemm_phase_calls": (c_int, [ctypes.POINTER(ctypes.c_double), c_int, ip]),
+        "ozgemm_mfma_ceiling": (c_int, [c_int, c_int, ctypes.c_uint, vp, vp]),
         "ozgemm_scheme1_beta": (c_int, [c_int]),
         "ozgemm_scheme1_outputs": (c_int, [c_int, c_int, c_int]),
         "ozgemm_scheme1_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
@@ -319,6 +320,18 @@ def ozgemm_phase_ms():
     calls = ctypes.c_int()
     _check(lib().ozgemm_phase_ms(buf, ctypes.byref(calls)), "ozgemm_phase_ms")
     return list(buf), calls.value
+
+
+def ozgemm_mfma_ceiling(blocks: int, steps: int, seed: int, sink, stream=None, check: bool = True) -> int:
+    """Launch the int8 matrix-core rate probe (asynchronous on `stream`, a
+    torch stream or None for the current one); sink: int32 device tensor of
+    at least 4 * blocks elements."""
+    import torch
+    if sink.numel() < 4 * blocks or sink.element_size() != 4 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous 4-byte tensor of at least 4 * blocks elements")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = lib().ozgemm_mfma_ceiling(blocks, steps, seed & 0xFFFFFFFF, _ptr(sink), s.cuda_stream)
+    return _check(st, "ozgemm_mfma_ceiling") if check else st
 
 
 def ozgemm_phase_calls():

@@ -398,6 +398,21 @@ int ozgemm_timing(int enable);
 int ozgemm_phase_ms(double *ms_out, int *calls);
 int ozgemm_phase_calls(double *ms_out, int max_calls, int *calls);
 
+/* Measurement aid: the rate the int8 matrix cores sustain on their own, the
+ * practical ceiling of the product step (Ozaki II notes §6: one int8 GEMM
+ * per modulus; §10 reports the method against the int8 rate).  `blocks`
+ * workgroups of four wavefronts each run `steps` steps of 32
+ * v_mfma_i32_16x16x64_i8 with operands in registers, in the product
+ * kernel's issue order (2^20 int8 operations per wavefront and step), on
+ * pseudo-random operands from `seed`.  Each wavefront writes the XOR of its
+ * accumulator words to sink[4 * block + wavefront] (device memory,
+ * 4 * blocks uint32, caller owned), which makes the result checkable.
+ * Asynchronous on hip_stream (NULL: the null stream); time it with events
+ * on that stream.  Needs no configuration.  Returns 0, -1 for blocks
+ * outside 1..2^20, -2 for steps < 1, -4 for sink == NULL, or
+ * OZGEMM_HIP_ERROR. */
+int ozgemm_mfma_ceiling(int blocks, int steps, unsigned seed, unsigned *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -313,3 +313,13 @@ def test_accu_checks_before_any_launch():
     assert lib.ozgemm_stage_scale(1024, 1024, 64, 2, FAKE, 1024, FAKE, 64, e, e) == L.OZGEMM_WORKSPACE_TOO_SMALL
     assert lib.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE) == 0
     lib.ozgemm_free()
+
+
+def test_mfma_ceiling_argument_checks():
+    """The matrix-core rate probe rejects bad arguments before any launch."""
+    lib = L.lib()
+    sink = ctypes.c_void_p(FAKE)
+    assert lib.ozgemm_mfma_ceiling(0, 4, 1, sink, None) == -1
+    assert lib.ozgemm_mfma_ceiling((1 << 20) + 1, 4, 1, sink, None) == -1
+    assert lib.ozgemm_mfma_ceiling(4, 0, 1, sink, None) == -2
+    assert lib.ozgemm_mfma_ceiling(4, 4, 1, None, None) == -4
