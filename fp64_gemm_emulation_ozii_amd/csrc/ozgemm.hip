@@ -871,6 +871,7 @@ int ozgemm_dgemm_noalloc(int m, int n, int q, const double* A, int lda, const do
   }
   const Layout lay = make_layout(m, n, q, s, false, rt_min);
   if (lay.total > OZGEMM_NOALLOC_BYTES) return OZGEMM_RANGE;
+  if (g.bound == OZGEMM_BOUND_ACCU && !accu_fits(lay, m, n, q)) return OZGEMM_RANGE;
   if (m == 0 || n == 0) return OZGEMM_OK;
   char* base = nullptr;
   if ((st = noalloc_scratch(&base))) return st;

@@ -3,8 +3,8 @@
 It must give the same result as ozgemm_dgemm (same kernels, intermediates in
 the library's fixed device array instead of the configured workspace), bit
 for bit, on calls in a row whose sizes shrink (the array keeps the previous
-call's contents), under both bit budgets; it refuses shapes whose
-intermediates exceed the array.
+call's contents), under each of the three bit budgets; it refuses shapes
+whose intermediates exceed the array.
 """
 import numpy as np
 import pytest
@@ -38,7 +38,11 @@ def both(A, B, s, stream):
     return c1[:n, :m].T, c2[:n, :m].T
 
 
-@pytest.mark.parametrize("bound", [L.OZGEMM_BOUND_CONSERVATIVE, L.OZGEMM_BOUND_FAST])
+BOUND_NAMES = {L.OZGEMM_BOUND_CONSERVATIVE: "conservative", L.OZGEMM_BOUND_FAST: "fast",
+               L.OZGEMM_BOUND_ACCU: "accu"}
+
+
+@pytest.mark.parametrize("bound", [L.OZGEMM_BOUND_CONSERVATIVE, L.OZGEMM_BOUND_FAST, L.OZGEMM_BOUND_ACCU])
 def test_noalloc_matches_dgemm_on_shrinking_calls(bound):
     import torch
     stream = torch.cuda.Stream()
@@ -54,7 +58,7 @@ def test_noalloc_matches_dgemm_on_shrinking_calls(bound):
                 c1, c2 = both(A, B, s, stream)
             assert same_doubles(c1, c2), first_diff(c1, c2)
             if m * n * q <= 300 * 257 * 129:
-                ref = oz.dgemm(A, B, s, bound="fast" if bound == L.OZGEMM_BOUND_FAST else "conservative")
+                ref = oz.dgemm(A, B, s, bound=BOUND_NAMES[bound])
                 assert same_doubles(c2, ref), first_diff(c2, ref)
                 assert within_tolerance(c2, ref, A, B)
     finally:
