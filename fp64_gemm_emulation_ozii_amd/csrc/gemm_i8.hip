@@ -452,7 +452,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
       for (int li = 0; li < LPW; ++li)
         if (RS * li + 1 < SLOTS) load1(1, li);
     reset_acc(acc);
-    wait_vmcnt<0>();  // slice 0, the half of slice 1 and this tile's stores
+    // Wait for slice 0 only: it went out before this tile's stores and
+    // slice 1's loads, and loads and stores retire from the counter in issue
+    // order.  The stores and slice 1 complete under step 0 of the next tile
+    // and are waited for at its first barrier.  (16384^2 x 1024: 1.6% off the
+    // product, against waiting for everything here.)
+    constexpr int STORES = STAGED ? (BN / NW) / (64 / (BM / 16)) : 0;  // 16-byte stores per wave above
+    if (nkt > 1)
+      wait_vmcnt<STORES + HALF_LOADS>();
+    else
+      wait_vmcnt<STORES>();
     __builtin_amdgcn_s_barrier();
   }
 }
