@@ -170,9 +170,10 @@ int ozgemm_dgemm(int m, int n, int q,
  * Errors: those of ozgemm_dgemm (argument numbers 1..10; no
  * OZGEMM_NOT_CONFIGURED), and OZGEMM_RANGE when the intermediates of this
  * shape need more than OZGEMM_NOALLOC_BYTES: s (m_pad + n_pad) q_pad bytes of
- * residue planes, s m_pad n_pad of product residues, 2 KB per padded row of
- * A for partial row maxima, and small arrays (m_pad, n_pad: m, n rounded up
- * to 256; q_pad: q rounded up to 128).  ozgemm_workspace_bytes(m, n, q, s)
+ * residue planes, s m_pad n_pad of product residues (under OS II-accu at
+ * least the bound's planes, about 9.02 m_pad n_pad bytes), 2 KB per padded
+ * row of A for partial row maxima, and small arrays (m_pad, n_pad: m, n
+ * rounded up to 256; q_pad: q rounded up to 128).  ozgemm_workspace_bytes(m, n, q, s)
  * <= OZGEMM_NOALLOC_BYTES is enough; for example 2048 x 2048 x 1024 fits at
  * s = 14, and 1024^3 at every s. */
 #define OZGEMM_NOALLOC_BYTES (128 << 20)
