@@ -622,7 +622,14 @@ int choose_panels(int mp, int np, int qp, int s, int cus) {
 int ensure_side() {
   if (g.side != nullptr) return 0;
   OZ_CHECK(hipStreamCreateWithFlags(&g.side, hipStreamNonBlocking));
-  for (auto& x : g.side_ev) OZ_CHECK(hipEventCreateWithFlags(&x, hipEventDisableTiming));
+  for (auto& x : g.side_ev) {
+    const hipError_t err = hipEventCreateWithFlags(&x, hipEventDisableTiming);
+    if (err != hipSuccess) {
+      x = nullptr;
+      release_side();  // all or nothing: the next pipelined call starts over
+      return hip_fail(err);
+    }
+  }
   return 0;
 }
 
