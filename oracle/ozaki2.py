@@ -339,12 +339,15 @@ def fast_exponents(A: np.ndarray, e: np.ndarray, kappa: int, kb: int) -> np.ndar
 #   LL <= 127 min(sum_l Lo_il, sum_l Lo_lj).  Everything is an exact integer,
 #   so the bound, and every decision taken from it, is reproducible;
 # * the bound decides per-row and per-column bit counts a_i, b_j with
-#   a_i + b_j + L_ij <= K2 = floor(log2(M/2 - 1)) for every (i, j), where
-#   2^L_ij >= the bound (L_ij = -inf for a zero bound): first each column
-#   takes half of what its largest L leaves, then each row the most its
-#   columns allow, then each column the most its rows allow; both capped at
-#   ACCU_KMAX.  |A'_il| <= 2^a_i x_il, so (|A'||B'|)_ij <= 2^(a_i + b_j + L_ij)
-#   <= M/2 - 1: the CRT result is the exact A'B' (§5);
+#   2^(a_i + b_j) N_ij / (127^2 2^14) <= M/2 - 1 for every (i, j), compared
+#   exactly: T_ij = floor(log2((M/2 - 1) 127^2 2^14 / N_ij)) is the largest
+#   integer sum a_i + b_j that entry allows, and with K2 = floor(log2(M/2 -
+#   1)) the budget reads a_i + b_j + L_ij <= K2 for L_ij = K2 - T_ij (L_ij =
+#   -inf for a zero bound).  First each column takes half of what its largest
+#   L leaves, then each row the most its columns allow, then each column the
+#   most its rows allow; both capped at ACCU_KMAX.  |A'_il| <= 2^a_i x_il, so
+#   (|A'||B'|)_ij <= 2^(a_i + b_j) N_ij / (127^2 2^14) <= M/2 - 1: the CRT
+#   result is the exact A'B' (§5);
 # * the shift of row i is a_i - e_i; the exponents handed to the residue and
 #   CRT steps are e'_i = ACCU_KMAX - a_i + e_i (shift base ACCU_KMAX), as for
 #   OS II-fast.
@@ -422,6 +425,22 @@ def accu_bound_exponents(A: np.ndarray, B: np.ndarray, e: np.ndarray, f: np.ndar
     return L
 
 
+def accu_budget_exponents(A: np.ndarray, B: np.ndarray, e: np.ndarray, f: np.ndarray, M: int) -> np.ndarray:
+    """L_ij = K2 - T_ij with T_ij = floor(log2((M/2 - 1) ACCU_DEN / N_ij)),
+    the largest integer t with 2^t N_ij / ACCU_DEN <= M/2 - 1, and K2 =
+    floor(log2(M/2 - 1)) (ACCU_LZERO where N_ij = 0).  The budget
+    a_i + b_j + L_ij <= K2 is then exactly 2^(a_i + b_j) N_ij / ACCU_DEN <=
+    M/2 - 1.  Python integers throughout: floor(log2(V / N)) is the bit length
+    of V // N, less one."""
+    N = accu_bound(A, B, e, f)
+    V = (M // 2 - 1) * ACCU_DEN
+    K2 = (M // 2 - 1).bit_length() - 1
+    L = np.full(N.shape, ACCU_LZERO, dtype=np.int64)
+    for (i, j) in zip(*np.nonzero(N)):
+        L[i, j] = K2 - ((V // int(N[i, j])).bit_length() - 1)
+    return L
+
+
 def accu_scaling(L: np.ndarray, K2: int):
     """Bit counts (a_i, b_j) from the exponents L_ij of the bound, with
     a_i + b_j + L_ij <= K2 everywhere: columns take half of what their
@@ -440,7 +459,7 @@ def accu_exponents(A: np.ndarray, B: np.ndarray, M: int):
     e = row_exponents(A).astype(np.int64)
     f = col_exponents(B).astype(np.int64)
     K2 = (M // 2 - 1).bit_length() - 1
-    L = accu_bound_exponents(A, B, e, f)
+    L = accu_budget_exponents(A, B, e, f, M)
     a, b = accu_scaling(L, K2)
     ep = np.where(e == NONFINITE, NONFINITE, ACCU_KMAX - a + e)
     fp = np.where(f == NONFINITE, NONFINITE, ACCU_KMAX - b + f)

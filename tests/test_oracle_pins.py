@@ -753,7 +753,7 @@ def test_accu_scaling_is_feasible_and_tight(s):
     K2 = (M // 2 - 1).bit_length() - 1
     e = oz.row_exponents(A).astype(np.int64)
     f = oz.col_exponents(B).astype(np.int64)
-    L = oz.accu_bound_exponents(A, B, e, f)
+    L = oz.accu_budget_exponents(A, B, e, f, M)
     a, b = oz.accu_scaling(L, K2)
     slack = K2 - (a[:, None] + b[None, :] + L)
     assert np.all(slack >= 0)
@@ -761,6 +761,57 @@ def test_accu_scaling_is_feasible_and_tight(s):
         assert a[i] == oz.ACCU_KMAX or np.any(slack[i, :] == 0)
     for j in range(L.shape[1]):
         assert b[j] == oz.ACCU_KMAX or np.any(slack[:, j] == 0)
+
+
+def _check_budget_exact(N, L, M):
+    """With T = K2 - L: 2^T N / ACCU_DEN <= M/2 - 1 < 2^(T+1) N / ACCU_DEN
+    wherever N > 0 (Python integers), and L = ACCU_LZERO where N = 0."""
+    K2 = (M // 2 - 1).bit_length() - 1
+    V = (M // 2 - 1) * oz.ACCU_DEN
+    for (i, j), n in np.ndenumerate(N):
+        if n == 0:
+            assert L[i, j] == oz.ACCU_LZERO, (i, j)
+            continue
+        T = K2 - int(L[i, j])
+        assert int(n) << T <= V, ("budget exceeded", i, j)
+        assert int(n) << (T + 1) > V, ("budget not maximal", i, j)
+
+
+@pytest.mark.parametrize("s", [4, 9, 14, 17, 20])
+def test_accu_budget_is_exact_and_maximal(s):
+    """The accu budget compares the two-band bound with M/2 - 1 exactly: the
+    row and column bit counts of entry (i, j) may sum to T_ij and not one
+    more.  It is never tighter than the power-of-two ceiling of the bound."""
+    A, B = _accu_inputs(s, phi=2.0)
+    M = oz.crt_constants(oz.greedy_moduli(s))[0]
+    K2 = (M // 2 - 1).bit_length() - 1
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    N = oz.accu_bound(A, B, e, f)
+    Lb = oz.accu_budget_exponents(A, B, e, f, M)
+    _check_budget_exact(N, Lb, M)
+    Lc = oz.accu_bound_exponents(A, B, e, f)
+    assert np.all(Lb <= Lc)
+    # at least one entry gains a bit over the ceiling rule for these inputs
+    assert np.any(Lb < Lc) or s == 4
+
+
+def test_accu_budget_planted_mistakes_are_caught():
+    """The old power-of-two ceiling (feasible, not maximal) and a budget one
+    bit too wide (not feasible) both fail the exactness check."""
+    A, B = _accu_inputs(3, phi=1.0)
+    M = oz.crt_constants(oz.greedy_moduli(14))[0]
+    e = oz.row_exponents(A).astype(np.int64)
+    f = oz.col_exponents(B).astype(np.int64)
+    N = oz.accu_bound(A, B, e, f)
+    Lceil = oz.accu_bound_exponents(A, B, e, f)  # the budget K2 - ceil(log2(N / ACCU_DEN))
+    Lb = oz.accu_budget_exponents(A, B, e, f, M)
+    assert np.any(Lceil != Lb)
+    with pytest.raises(AssertionError):
+        _check_budget_exact(N, Lceil, M)
+    wide = np.where(Lb == oz.ACCU_LZERO, Lb, Lb - 1)
+    with pytest.raises(AssertionError):
+        _check_budget_exact(N, wide, M)
 
 
 @pytest.mark.parametrize("s,q", [(8, 40), (12, 150), (14, 200), (18, 33)])
