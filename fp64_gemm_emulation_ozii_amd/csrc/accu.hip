@@ -13,19 +13,23 @@
 // products on the matrix cores (the plan form of the product kernel: one of
 // length q, one of length 2q; exact in int32 while 2 127^2 q_pad < 2^31) and
 // RS_i, CS_j are the row sums of Lo (LL = Lo_A Lo_B^T <= 127 min(RS_i, CS_j)).
-// L_ij = ceil(log2(N_ij / (127^2 2^14))), or -128 (no constraint) for N = 0.
 //
-// Scaling.  Bit counts a_i, b_j with a_i + b_j + L_ij <= K2 =
-// floor(log2(M/2 - 1)) for all (i, j), so that (|A'||B'|)_ij <=
-// 2^(a_i + b_j + L_ij) < M/2 and the CRT result is exact (§5): each column
-// first takes half of what its largest L leaves, each row then the most its
-// columns allow, each column then the most its rows allow; all at most
-// ACCU_KMAX.  The exponents handed on are e'_i = ACCU_KMAX - a_i + e_i (row
+// Budget.  Entry (i, j) admits a_i + b_j <= T_ij = floor(log2(V / N_ij)),
+// V = (M/2 - 1) 127^2 2^14, the largest t with 2^t N_ij / (127^2 2^14) <=
+// M/2 - 1, compared exactly; it is kept as L_ij = K2 - T_ij with K2 =
+// floor(log2(M/2 - 1)), or -128 (no constraint) for N = 0.
+//
+// Scaling.  Bit counts a_i, b_j with a_i + b_j + L_ij <= K2 for all (i, j),
+// so that (|A'||B'|)_ij <= 2^(a_i + b_j) N_ij / (127^2 2^14) < M/2 and the CRT
+// result is exact (§5): each column first takes half of what its largest L
+// leaves, each row then the most its columns allow, each column then the most
+// its rows allow; all at most ACCU_KMAX.  The exponents handed on are e'_i = ACCU_KMAX - a_i + e_i (row
 // shift a_i - e_i, shift base ACCU_KMAX), NONFINITE kept.
 //
 // Every quantity is an exact integer function of the inputs, so the result
 // does not depend on the order of any sum.
 #include "oz_internal.h"
+#include "accu_budget.h"
 
 namespace oz {
 
@@ -149,15 +153,6 @@ __global__ void accu_plan_kernel(int4* plan) {
   }
 }
 
-// Smallest L with N <= D 2^L (N, D > 0, N < 2^62, D < 2^30).
-__device__ __forceinline__ int ceil_log2_ratio(long long N, long long D) {
-  const int bn = 64 - __builtin_clzll((unsigned long long)N);
-  const int bd = 64 - __builtin_clzll((unsigned long long)D);
-  int L = bn - bd;
-  const bool fits = L >= 0 ? ((D << L) >= N) : (D >= (N << -L));
-  return fits ? L : L + 1;
-}
-
 __device__ __forceinline__ int block_reduce(int v, bool take_max, int* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int o = 32; o > 0; o >>= 1) {
@@ -171,22 +166,23 @@ __device__ __forceinline__ int block_reduce(int v, bool take_max, int* red) {
   return v;
 }
 
-// Column j (one block): L_ij from the two product planes and the Lo sums,
-// and the column's first bit count b1_j = min(KMAX, floor((K2 - max_i L_ij) / 2)).
+// Column j (one block): L_ij = K2 - floor(log2(V / N_ij)) from the two product
+// planes and the Lo sums, and the column's first bit count
+// b1_j = min(KMAX, floor((K2 - max_i L_ij) / 2)).
 __global__ __launch_bounds__(256) void accu_combine_kernel(const int32_t* __restrict__ P, int m, int m_pad, long plane,
                                                             const int32_t* __restrict__ RS,
                                                             const int32_t* __restrict__ CS, int K2, int kmax,
-                                                            int8_t* __restrict__ L, int32_t* __restrict__ b1) {
+                                                            uint64_t vtop, int bv, int8_t* __restrict__ L,
+                                                            int32_t* __restrict__ b1) {
   __shared__ int red[4];
   const int j = blockIdx.x;
   const long col = (long)j * m_pad;
-  const long long D = (long long)RES * RES << 14;
   const int cs = CS[j];
   int mx = LZERO;
   for (int i = threadIdx.x; i < m; i += 256) {
     const long long N = ((long long)P[col + i] << 14) + ((long long)P[plane + col + i] << 7) +
                         (long long)RES * min(RS[i], cs);
-    const int l = N > 0 ? ceil_log2_ratio(N, D) : LZERO;
+    const int l = N > 0 ? K2 - floor_log2_ratio((uint64_t)N, vtop, bv) : LZERO;
     L[col + i] = (int8_t)l;
     mx = max(mx, l);
   }
@@ -250,10 +246,12 @@ size_t accu_scratch_bytes(int m_pad, int n_pad, int q_pad) {
 }
 
 hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const double* B, int n, int ldb, int m_pad,
-                                 int n_pad, int q_pad, int K2, int kmax, int8_t* Aplanes, int8_t* Bplanes,
-                                 int32_t* psumA, char* scratch, int32_t* e, int32_t* f, hipStream_t st) {
+                                 int n_pad, int q_pad, int K2, uint64_t vtop, int bv, int kmax, int8_t* Aplanes,
+                                 int8_t* Bplanes, int32_t* psumA, char* scratch, int32_t* e, int32_t* f,
+                                 hipStream_t st) {
   if (m < 1 || n < 1 || q < 1 || q_pad % TK || m_pad % 256 || n_pad % 256 || m_pad / TR > 65535 ||
-      n_pad / TR > 65535 || q_pad > ACCU_Q_MAX || 2L * RES * RES * q_pad >= (1L << 31) || kmax != ACCU_KMAX)
+      n_pad / TR > 65535 || q_pad > ACCU_Q_MAX || 2L * RES * RES * q_pad >= (1L << 31) || kmax != ACCU_KMAX ||
+      bv < 64 || (vtop >> 63) == 0)
     return hipErrorInvalidValue;
   const size_t mp = (size_t)m_pad, np = (size_t)n_pad;
   const int nk = q_pad / TK;
@@ -285,7 +283,7 @@ hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const d
   hipError_t err = launch_gemm_multi(Aplanes, Bplanes, m_pad, n_pad, q_pad, plan, 2, P, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(accu_combine_kernel, dim3(n), dim3(256), 0, st, P, m, m_pad, (long)(mp * np), RS, CS, K2, kmax,
-                     L, b1);
+                     vtop, bv, L, b1);
   hipLaunchKernelGGL(accu_rowmin_kernel, dim3((m + 255) / 256, chunks), dim3(256), 0, st, L, m, n, m_pad, b1, K2,
                      pmin);
   hipLaunchKernelGGL(accu_rowfinal_kernel, dim3((m + 255) / 256), dim3(256), 0, st, pmin, m, m_pad, chunks, kmax, a,

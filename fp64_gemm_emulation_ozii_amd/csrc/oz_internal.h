@@ -137,15 +137,17 @@ hipError_t launch_fill_zero(double* C, int m, int n, int ldc, hipStream_t st);
 
 // OS II-accu (accu.hip): replace the row and column exponents e, f (frexp
 // exponents of the maxima) by the exponents e', f' of the accu bit budget
-// (shift base kmax, budget K2 = floor(log2(M/2 - 1))).  Aplanes / Bplanes
+// (shift base kmax, K2 = floor(log2(M/2 - 1)); V = (M/2 - 1) 127^2 2^14 has
+// bv bits, the top 64 of them in vtop, see accu_budget_consts).  Aplanes / Bplanes
 // hold 2 m_pad q_pad / 2 n_pad q_pad bytes of band planes, psumA
 // 4 m_pad q_pad / 128 bytes, scratch accu_scratch_bytes(...) bytes; q_pad <= 2^16.
 constexpr int ACCU_KMAX = 76;         // |A'| < 2^76: the residue step's widest exact integers
 constexpr int ACCU_Q_MAX = 1 << 16;   // 2 127^2 q_pad < 2^31: the bound products are exact in int32
 size_t accu_scratch_bytes(int m_pad, int n_pad, int q_pad);
 hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const double* B, int n, int ldb, int m_pad,
-                                 int n_pad, int q_pad, int K2, int kmax, int8_t* Aplanes, int8_t* Bplanes,
-                                 int32_t* psumA, char* scratch, int32_t* e, int32_t* f, hipStream_t st);
+                                 int n_pad, int q_pad, int K2, uint64_t vtop, int bv, int kmax, int8_t* Aplanes,
+                                 int8_t* Bplanes, int32_t* psumA, char* scratch, int32_t* e, int32_t* f,
+                                 hipStream_t st);
 
 // Measurement aid (probe.hip): `blocks` workgroups of four wavefronts run
 // `steps` register-only steps of 32 v_mfma_i32_16x16x64_i8 each; sink

@@ -140,6 +140,28 @@ void fast_budget(int s, int* kappa_a, int* kappa_b) {
   *kappa_b = K2 - K2 / 2;
 }
 
+// OS II-accu budget constants (Ozaki II notes §9): K2 = floor(log2(M/2 - 1))
+// and V = (M/2 - 1) 127^2 2^14, the numerator that the accu kernels compare
+// 2^(a_i + b_j) times the two-band bound with: its bit length bv and its top
+// 64 bits (bits bv - 64 .. bv - 1).  V < 2^192 for s <= 20.
+void accu_budget_consts(int s, int* K2, uint64_t* vtop, int* bv) {
+  Big M = product_M(s);
+  Big V;
+  big_divmod_small(M, 2, &V);
+  big_sub_small(V, 1);
+  *K2 = big_bitlen(V) - 1;
+  big_mul_small(V, 127u * 127u);
+  big_mul_small(V, 1u << 14);
+  const int b = big_bitlen(V);
+  uint64_t top = 0;
+  for (int k = 0; k < 64; ++k) {
+    const int bit = b - 64 + k;
+    if (bit >= 0 && ((V.w[bit / 32] >> (bit % 32)) & 1u)) top |= 1ull << k;
+  }
+  *bv = b;
+  *vtop = top;
+}
+
 int modinv_small(int a, int m) {  // a^-1 mod m, gcd(a, m) = 1
   int t = 0, newt = 1, r = m, newr = a % m;
   while (newr) {
@@ -459,9 +481,10 @@ int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda
     int mpc, npc, qpc;
     dims(m, n, q, &mpc, &npc, &qpc);
     if (!accu_fits(x.lay, m, n, q)) return OZGEMM_WORKSPACE_TOO_SMALL;  // checked before any launch by callers
-    int ka2, kb2;
-    fast_budget(s, &ka2, &kb2);
-    OZ_CHECK(launch_accu_exponents(A, m, q, lda, B, n, ldb, mpc, npc, qpc, ka2 + kb2, ACCU_KMAX,
+    int K2 = 0, bv = 0;
+    uint64_t vtop = 0;
+    accu_budget_consts(s, &K2, &vtop, &bv);
+    OZ_CHECK(launch_accu_exponents(A, m, q, lda, B, n, ldb, mpc, npc, qpc, K2, vtop, bv, ACCU_KMAX,
                                    reinterpret_cast<int8_t*>(x.ws + x.lay.ares),
                                    reinterpret_cast<int8_t*>(x.ws + x.lay.bres), reinterpret_cast<int32_t*>(pmax),
                                    x.ws + x.lay.rt, e, f, x.stream));

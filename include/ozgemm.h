@@ -224,13 +224,15 @@ int ozgemm_plane_dims(int m, int n, int q, int *m_pad, int *n_pad, int *q_pad);
  *     ceil(127 2^7 x) below.  Then sum_l x_il y_lj <= N_ij / (127^2 2^14)
  *     with N = 2^14 H_A H_B^T + 2^7 (H_A Lo_B^T + Lo_A H_B^T) +
  *     127 min(row sum of Lo_A, column sum of Lo_B), two int8 products run
- *     on the product kernel (length q and 2q), and L_ij = ceil(log2 of the
- *     bound).  Row bit counts a_i and column bit counts b_j satisfy
- *     a_i + b_j + L_ij <= floor(log2(M/2 - 1)) for every (i, j): columns
- *     first take half of what their largest L leaves, rows then the most
- *     their columns allow, columns then the most their rows allow, all at
- *     most 76.  Row i of A' is trunc(a_il 2^(a_i - e_i)), so (|A'||B'|)_ij <
- *     M/2 and the CRT result is exact (§5).  The stage exponents are
+ *     on the product kernel (length q and 2q).  Row bit counts a_i and
+ *     column bit counts b_j satisfy 2^(a_i + b_j) N_ij / (127^2 2^14) <=
+ *     M/2 - 1 for every (i, j), compared exactly (a_i + b_j + L_ij <= K2
+ *     with K2 = floor(log2(M/2 - 1)) and L_ij = K2 - floor(log2((M/2 - 1)
+ *     127^2 2^14 / N_ij))): columns first take half of what their largest
+ *     L leaves, rows then the most their columns allow, columns then the
+ *     most their rows allow, all at most 76.  Row i of A' is
+ *     trunc(a_il 2^(a_i - e_i)), so (|A'||B'|)_ij < M/2 and the CRT result
+ *     is exact (§5).  The stage exponents are
  *     e'_i = 76 - a_i + e_i (shift base 76).  Every quantity is an exact
  *     integer, so results are reproducible.  Needs q <= OZGEMM_ACCU_Q_MAX,
  *     s >= 2 and k(s, q) >= 1, and room in the workspace's product region
