@@ -41,10 +41,35 @@ __device__ __forceinline__ int32_t exponent_of_bits(uint64_t b) {
   return top - 1073;
 }
 
+// OS II-fast norm bound (Ozaki II notes §9, Cauchy-Schwarz): the squared
+// norm of a row x (or column) scaled by 2^-e is bounded by the exact integer
+// S = sum ceil(|x| 2^(NORM_GRID - e))^2 in units of 2^(-2 NORM_GRID); any
+// summation order gives the same S.
+constexpr int NORM_GRID = 20;
+
+// ceil(|x| 2^(NORM_GRID - e))^2 as an exact integer (|x| < 2^e).
+__device__ __forceinline__ uint64_t norm_term(double x, int e) {
+  const double t = __builtin_ceil(__builtin_ldexp(__builtin_fabs(x), NORM_GRID - e));
+  const uint64_t u = (uint64_t)t;
+  return u * u;
+}
+
+// e'_i from e_i and the squared-norm bound S (units 2^-2 NORM_GRID): the
+// row is scaled by 2^d, d = kappa - c - e with 4^c the smallest power of
+// four >= S 2^(-2 NORM_GRID), and handed on as e' = kb - d.
+__device__ __forceinline__ int32_t fast_exponent(int32_t e, uint64_t S, int kappa, int kb) {
+  if (e == OZGEMM_EXP_NONFINITE) return e;
+  if (S == 0) return 0;
+  const int b = (S == 1) ? 0 : 64 - __clzll((long long)(S - 1));  // ceil(log2 S)
+  const int c = (b + 1) / 2 - NORM_GRID;
+  return kb - (kappa - c - e);
+}
+
 struct ResidueConsts {
   int s;
   int k;                        // shift base: row shift is k - e_i
   int kmag;                     // |A'| < 2^kmag (selects the residue arithmetic)
+  int col_kappa;                // B in one pass under OS II-fast: kappa_B (-1: the exponent as it is)
   int m[OZGEMM_S_MAX];          // moduli
   int lo[OZGEMM_S_MAX];         // -floor(m/2)
   int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1

@@ -209,6 +209,12 @@ void make_consts(int s, int q, int mode, ResidueConsts* rc, GemmConsts* gc, CrtC
   rc->s = gc->s = cc->s = s;
   rc->k = cc->k = k;
   rc->kmag = kmag;
+  rc->col_kappa = -1;
+  if (mode == OZGEMM_BOUND_FAST) {
+    int ka = 0, kb = 0;
+    fast_budget(s, &ka, &kb);
+    rc->col_kappa = kb;  // the columns of B share kappa_B; the shift base k is max(kappa_A, kappa_B)
+  }
   for (int t = 0; t < s; ++t) {
     const int m = mods[t];
     rc->m[t] = gc->m[t] = m;
@@ -681,9 +687,10 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   cc.wtab = wtab;
   int st = 0;
   if (ev) OZ_CHECK(hipEventRecord((*ev)[0], x.stream));
-  // B's exponents come out of its residue pass when the column fits (the
-  // OS II-fast budget needs its norms first, so it keeps two passes)
-  const bool b_one_pass = x.bound == OZGEMM_BOUND_CONSERVATIVE && col_residue_fits(q);
+  // B's exponents come out of its residue pass when the column fits (under
+  // OS II-fast with the column's norm bound too); OS II-accu needs them
+  // before its bound, so it keeps two passes
+  const bool b_one_pass = x.bound != OZGEMM_BOUND_ACCU && col_residue_fits(q);
   if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
   if (ev) OZ_CHECK(hipEventRecord((*ev)[1], x.stream));
   OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));

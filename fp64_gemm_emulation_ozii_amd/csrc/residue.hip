@@ -249,8 +249,20 @@ __global__ __launch_bounds__(256) void col_residue_kernel(const double* __restri
     if (lane == 0) wmax[wave] = mx;
     __syncthreads();
     e = exponent_of_bits(umax64(umax64(wmax[0], wmax[1]), umax64(wmax[2], wmax[3])));
-    if (tid == 0) ex[j] = e;
     zero_row = (e == OZGEMM_EXP_NONFINITE);
+    if (c.col_kappa >= 0) {  // uniform: OS II-fast, the column's norm bound from the same registers
+      uint64_t S = 0;
+      if (!zero_row) {
+#pragma unroll
+        for (int i = 0; i < COL_QMAX / 256; ++i) S += norm_term(v[i], e);  // zero past q
+      }
+      for (int off = 32; off > 0; off >>= 1) S += (uint64_t)__shfl_xor((unsigned long long)S, off, 64);
+      __syncthreads();  // every wave has read wmax
+      if (lane == 0) wmax[wave] = S;
+      __syncthreads();
+      e = fast_exponent(e, wmax[0] + wmax[1] + wmax[2] + wmax[3], c.col_kappa, c.k);
+    }
+    if (tid == 0) ex[j] = e;
   }
   __syncthreads();
   const int shift = zero_row ? 0 : c.k - e;

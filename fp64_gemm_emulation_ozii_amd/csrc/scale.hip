@@ -93,24 +93,6 @@ __global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__
   if (lane == 0) f[j] = exponent_of_bits(v);
 }
 
-constexpr int NORM_GRID = 20;
-
-// ceil(|x| 2^(NORM_GRID - e))^2 as an exact integer (|x| < 2^e).
-__device__ __forceinline__ uint64_t norm_term(double x, int e) {
-  const double t = __builtin_ceil(__builtin_ldexp(__builtin_fabs(x), NORM_GRID - e));
-  const uint64_t u = (uint64_t)t;
-  return u * u;
-}
-
-// e'_i from e_i and the squared-norm bound S (units 2^-2 NORM_GRID).
-__device__ __forceinline__ int32_t fast_exponent(int32_t e, uint64_t S, int kappa, int kb) {
-  if (e == OZGEMM_EXP_NONFINITE) return e;
-  if (S == 0) return 0;
-  const int b = (S == 1) ? 0 : 64 - __clzll((long long)(S - 1));  // ceil(log2 S)
-  const int c = (b + 1) / 2 - NORM_GRID;
-  return kb - (kappa - c - e);
-}
-
 __global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
                                                                 long lda, int chunk,
                                                                 const int32_t* __restrict__ e,

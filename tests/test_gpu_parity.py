@@ -250,10 +250,12 @@ def test_long_inner_dimension_refuses_int32_planes():
 
 @pytest.mark.parametrize("q", [L.OZGEMM_ONE_PASS_Q_MIN - 1, L.OZGEMM_ONE_PASS_Q_MIN, L.OZGEMM_ONE_PASS_Q_MIN + 37,
                                L.OZGEMM_ONE_PASS_Q_MAX, L.OZGEMM_ONE_PASS_Q_MAX + 1])
-def test_b_one_pass_boundary(q):
+@pytest.mark.parametrize("bound", ["conservative", "fast"])
+def test_b_one_pass_boundary(q, bound):
     """For OZGEMM_ONE_PASS_Q_MIN <= q <= OZGEMM_ONE_PASS_Q_MAX ozgemm_dgemm
-    takes B's column exponents inside its residue pass (B read once);
-    outside that range the scale step does.
+    takes B's column exponents (under OS II-fast with the columns' norm
+    bounds) inside its residue pass (B read once); outside that range the
+    scale step does.
     Columns of B that are all zero, subnormal only, near overflow or hold a
     NaN exercise that exponent; C must equal the oracle bit for bit either
     way, and the stage entry points (always two passes) must agree."""
@@ -268,15 +270,17 @@ def test_b_one_pass_boundary(q):
     B[:q - 1, 13] = 2.0 ** -1075 * 0.0
     L.ozgemm_free()
     configure(256, 512, q, 20)
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if bound == "fast" else L.OZGEMM_BOUND_CONSERVATIVE)
     try:
-        log(f"one-pass boundary q={q}")
+        log(f"one-pass boundary q={q} bound={bound}")
         C, _ = run_dgemm(A, B, 14)
         g = run_stages(A, B, 14, want_ct=False, want_prime=False)
     finally:
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
         L.ozgemm_free()
         torch.cuda.empty_cache()
         configure(1536, 1536, 1536, 20)
-    ref = oz.dgemm(A, B, 14, stages=True)
+    ref = oz.dgemm(A, B, 14, stages=True, bound=bound)
     assert same_doubles(C, ref[0]), first_diff(C, ref[0])
     assert np.array_equal(g["f"], ref[1]["f"]), first_diff(g["f"], ref[1]["f"])
     assert same_doubles(g["C"], C)
