@@ -15,7 +15,8 @@
 // is A_t B_t^T.  A block computes a BM x BN output tile with four wavefronts
 // (2 x 2), each owning (BM/2) x (BN/2) built from 16x16 int32 tiles of
 // v_mfma_i32_16x16x64_i8 (residue-only products) or 32x32 tiles of
-// v_mfma_i32_32x32x32_i8 (int32 output).  In the multi-product form an output plane is the
+// v_mfma_i32_32x32x32_i8 (int32 output); residue-only products whose blocks
+// walk few K slices use eight wavefronts (2 x 4, two per SIMD) instead.  In the multi-product form an output plane is the
 // sum of `count` products (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one
 // long K loop.
 //
@@ -113,6 +114,17 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 //    stream, and the last of them still has half a slice to land.
 //    (Measured at 8192^3 x 14 planes: 7.1 ms with the loads issued as one
 //    burst per slice, 6.3 ms with this order.)
+//  * Eight wavefronts (WM x WN = 2 x 4, 128 x 64 each, two per SIMD, 128
+//    accumulators): 32 MFMA slots and 12 fragment reads per step, which do
+//    not divide evenly.  A fragment i is re-read right after its last MFMA
+//    (slot 4 i + 3), so its old and new values can share registers, B
+//    fragment j after slot 8 j + 1, and the 8 loads per slice go after slots
+//    2, 6, ..., 30.  Each wavefront reads 1.5x the LDS bytes per MFMA, but
+//    one wavefront's waits, barrier arrival and epilogue run beside the
+//    other's MFMAs.  Same-box A/B against four wavefronts (s = 14): 3-5%
+//    faster at 16384^2 x 1024, 2.2% at 16384^2 x 2048, 1.3-1.4% at 1024^3
+//    and 2048^3 (8 and 16 K slices per block); 1.3-1.7% slower at
+//    8192^2 x 4096 and 16384^3, within +-2% at 8192^3 (32-128 slices).
 // K parts (gemm_grid.h): plane index p s + t of a residue-only launch is
 // part p of modulus t, covering K slices [k_begin + p k_slices, + k_slices)
 // clipped to q_pad; it writes its residue to plane p s + t of rt.  With one
@@ -123,9 +135,28 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 // block's residue to the residue already in rt, mod m_t.
 constexpr int KBLOCK_K = 1 << 16;
 
+// Slot plan of one K step (see above): fragment f of the next step is read
+// after MFMA slot read_slot, load li of a slice after slot load_slot of its
+// window.  Four wavefronts: rs = slots / fragments.  Eight: fn B fragments
+// (f < fn), then the A fragments.
+constexpr int read_slot(bool eight, int rs, int fn, int f) {
+  return eight ? (f < fn ? 8 * f + 1 : fn * (f - fn) + fn - 1) : rs * f;
+}
+constexpr int load_slot(bool eight, int rs, int li) { return eight ? 4 * li + 2 : rs * li + 1; }
+// loads of a slice that fall in the last step of the slice before it
+constexpr int early_loads(bool eight, int rs, int lpw, int slots) {
+  int h = 0;
+  for (int li = 0; li < lpw; ++li) h += load_slot(eight, rs, li) < slots;
+  return h;
+}
+
+// Residue-only launches whose blocks walk at most this many K slices use
+// eight wavefronts per block.
+constexpr int EIGHT_WAVE_MAX_SLICES = 16;
+
 template <int BM, int BN, int BK, int WM, int WN, bool WRITE_CT, bool WRITE_RT, bool MULTI, bool ACC_RT = false,
           bool PERSIST = false>
-__global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_kernel(
+__global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_i8_kernel(
     const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
     int32_t* __restrict__ Ct, uint8_t* __restrict__ rt, const int4* __restrict__ plan, int k_begin, int k_slices,
     int nblocks) {
@@ -144,13 +175,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int NKS = BK / KSTEP;               // K steps per slice
   constexpr int NF = FM + FN;                   // fragments per step
   constexpr int SLOTS = FM * FN;                // MFMAs per step
-  constexpr int RS = SLOTS / NF;                // slots per fragment read
+  constexpr int RS = SLOTS / NF;                // slots per fragment read (four wavefronts)
+  constexpr bool EIGHT = NW == 8;
+  static_assert(NW == 4 || (EIGHT && MT == 16 && FM == 8 && FN == 4), "four wavefronts, or eight of 128 x 64");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
-  static_assert(SLOTS % NF == 0 && NKS >= 2, "slot plan: whole reads per step, two steps per slice");
-  static_assert(RS * (LPW - 1) + 1 < SLOTS * NKS, "every load has a slot in its window");
-  // loads of a slice issued in the window before it: those with
-  // RS li + 1 < SLOTS (8 with MT = 32, all 16 with MT = 16)
-  constexpr int HALF_LOADS = (SLOTS - 2) / RS + 1 < LPW ? (SLOTS - 2) / RS + 1 : LPW;
+  static_assert((EIGHT || SLOTS % NF == 0) && NKS >= 2, "slot plan: whole reads per step, two steps per slice");
+  static_assert(load_slot(EIGHT, RS, LPW - 1) < SLOTS * NKS, "every load has a slot in its window");
+  // loads of a slice issued in the window before it: those whose slot falls
+  // in the last step of the slice before (8 with MT = 32, all with MT = 16)
+  constexpr int HALF_LOADS = early_loads(EIGHT, RS, LPW, SLOTS);
   static_assert(HALF_LOADS == (MT == 32 ? 8 : LPW), "prologue load count");
   typedef int acc_t __attribute__((ext_vector_type(ACC_N)));
 
@@ -297,7 +330,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   if (nkt > 1) {
 #pragma unroll
     for (int li = 0; li < LPW; ++li)
-      if (RS * li + 1 < SLOTS) load1(1, li);
+      if (load_slot(EIGHT, RS, li) < SLOTS) load1(1, li);
     wait_vmcnt<HALF_LOADS>();  // slice 0 (loads return in order)
   } else {
     wait_vmcnt<0>();
@@ -337,11 +370,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
           else
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);  // the slot's MFMA issues before its read
-          if (r % RS == 0) nxt[r / RS] = read1(rbuf, rks, r / RS);
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            if (read_slot(EIGHT, RS, FN, f) == r) nxt[f] = read1(rbuf, rks, f);
           const int slot = last ? r : SLOTS + ks * SLOTS + r;
 #pragma unroll
           for (int li = 0; li < LPW; ++li)
-            if (RS * li + 1 == slot && lslice < nkt) load1(lslice, li);
+            if (load_slot(EIGHT, RS, li) == slot && lslice < nkt) load1(lslice, li);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (last) __builtin_amdgcn_s_waitcnt(0xc07f);  // no LDS read in flight (see above)
@@ -450,7 +485,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
     if (nkt > 1)
 #pragma unroll
       for (int li = 0; li < LPW; ++li)
-        if (RS * li + 1 < SLOTS) load1(1, li);
+        if (load_slot(EIGHT, RS, li) < SLOTS) load1(1, li);
     reset_acc(acc);
     // Wait for slice 0 only: it went out before this tile's stores and
     // slice 1's loads, and loads and stores retire from the counter in issue
@@ -717,15 +752,26 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   const dim3 grid(nblocks), block(WM * WN * 64);
   const int nk = q_pad / BK;
   // residue-only products walk their tiles with one block per compute unit
-  // (the persistent form) when there are more tiles than units
+  // (the persistent form) when there are more tiles than units; blocks that
+  // walk few K slices run eight wavefronts
   auto launch_rt = [&](uint8_t* out, int total, int per) {
+    constexpr int WN8 = 4;
+    const bool eight = per <= EIGHT_WAVE_MAX_SLICES;
     if (total == nblocks && per == nk && nk <= SHORT_NK) {  // one part, short K: two blocks per CU
       const int total_short = (m_pad / 256) * (n_pad / 128) * c.s;
       hipLaunchKernelGGL(gemm_i8_short_kernel, dim3(total_short), block, 0, st, Ares, Bres, m_pad, n_pad, q_pad, c,
                          out, total_short);
-    } else if (cus > 0 && total > cus)
+    } else if (cus > 0 && total > cus && eight)
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, false, true, false, false, true>), dim3(cus),
+                         dim3(WM * WN8 * 64), 0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per,
+                         total);
+    else if (cus > 0 && total > cus)
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false, false, true>), dim3(cus), block,
                          0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per, total);
+    else if (eight)
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, false, true, false>), dim3(total),
+                         dim3(WM * WN8 * 64), 0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per,
+                         total);
     else
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, false, true, false>), dim3(total), block, 0, st,
                          Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per, total);

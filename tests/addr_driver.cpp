@@ -8,7 +8,8 @@
 // Input lines (all sizes padded as the library pads them):
 //   gemm  <form> <m_pad> <n_pad> <q_pad> <s> <cus> <parts> <per> <k_begin> <k_slices> <swz_bug>
 //         form: main (residue output, one block per tile), persist (the same,
-//         cus blocks walking the tiles), acc (residue output added to the
+//         cus blocks walking the tiles), main8 / persist8 (the same with
+//         eight wavefronts of 128 x 64), acc (residue output added to the
 //         earlier K blocks' residues), short, ct (int32 output, MT = 32)
 //   plan  <m_pad> <n_pad> <q_pad> <nplanes_a> <nplanes_b> then nout lines "a0 b0 count out"
 //         (preceded by "<nout>")
@@ -49,11 +50,12 @@ struct Plan {
 };
 
 // The main product kernel: BM = BN = 256, BK = 128 (or 32 with the planted
-// swizzle bug), 2 x 2 wavefronts.  MT = 16 for residue output, 32 for int32.
+// swizzle bug), 2 x 2 wavefronts (2 x 4 with `eight`).  MT = 16 for residue
+// output, 32 for int32.
 void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bool ct, bool acc_rt, int parts,
                int k_begin, int k_slices, bool multi, const std::vector<Plan>& plan, int a_planes, int b_planes,
-               bool swz_bug) {
-  const int BM = 256, BN = 256, BK = swz_bug ? 32 : 128, WM = 2, WN = 2, NW = 4;
+               bool swz_bug, bool eight = false) {
+  const int BM = 256, BN = 256, BK = swz_bug ? 32 : 128, WM = 2, WN = eight ? 4 : 2, NW = WM * WN;
   const int CPR = BK / 16, ROWS_PER_KB = 1024 / BK;
   const int A_LOADS = BM * BK / 1024 / NW, B_LOADS = BN * BK / 1024 / NW, LPW = A_LOADS + B_LOADS;
   const int WTM = BM / WM, WTN = BN / WN;
@@ -334,9 +336,11 @@ int main() {
       (void)per;
       if (!std::strcmp(form, "short"))
         gemm_short(mp, np, qp, s);
-      else
-        gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist"), !std::strcmp(form, "ct"), !std::strcmp(form, "acc"),
-                  parts, kb, ks, false, {}, 0, 0, bug != 0);
+      else {
+        const bool eight = !std::strcmp(form, "main8") || !std::strcmp(form, "persist8");
+        gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist") || !std::strcmp(form, "persist8"),
+                  !std::strcmp(form, "ct"), !std::strcmp(form, "acc"), parts, kb, ks, false, {}, 0, 0, bug != 0, eight);
+      }
     } else if (!std::strcmp(cmd, "plan")) {
       int mp, np, qp, na, nb, nout;
       if (std::scanf("%d %d %d %d %d %d", &mp, &np, &qp, &na, &nb, &nout) != 6) return 1;

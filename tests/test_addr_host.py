@@ -55,7 +55,9 @@ SHAPES = [(1, 1, 1), (257, 255, 129), (300, 770, 1000), (513, 300, 4097)]
 def test_product_forms_stay_in_bounds(driver, m, n, q):
     lines = [gemm_line("main", m, n, q, 3), gemm_line("ct", m, n, q, 2),
              # the persistent walk, with few compute units so that blocks take several tiles
-             gemm_line("persist", m, n, q, 3, cus=5), gemm_line("persist", m, n, q, 14, cus=7)]
+             gemm_line("persist", m, n, q, 3, cus=5), gemm_line("persist", m, n, q, 14, cus=7),
+             # eight wavefronts per block (blocks that walk few K slices)
+             gemm_line("main8", m, n, q, 3), gemm_line("persist8", m, n, q, 14, cus=7)]
     if pad(q, 128) <= 512:
         lines.append(gemm_line("short", m, n, q, 5))
     for r in run(driver, lines):
@@ -66,6 +68,8 @@ def test_k_parts_and_their_reduction(driver):
     # 256 x 256 x 8192 in 8 parts of 8 slices, and a ragged last part
     lines = [gemm_line("main", 256, 256, 8192, 14, parts=8, per=8),
              gemm_line("persist", 256, 256, 8192, 14, cus=9, parts=8, per=8),
+             gemm_line("persist8", 256, 256, 8192, 14, cus=9, parts=8, per=8),
+             gemm_line("main8", 200, 100, 8000, 3, parts=6, per=11),
              gemm_line("main", 200, 100, 8000, 3, parts=6, per=11),
              "reduce 256 256 14 8", "reduce 512 768 3 6"]
     for r in run(driver, lines):
