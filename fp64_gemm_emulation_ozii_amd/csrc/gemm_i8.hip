@@ -39,7 +39,6 @@ namespace oz {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 // Physical 16-byte chunk of logical chunk kc in tile row `row` is kc ^ swz(row).
 // A wavefront's 16-byte LDS reads are served 16 lanes at a time from 64
@@ -501,196 +500,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-// Short inner dimension (nk <= SHORT_NK slices of 128): with few K steps
-// per tile, the epilogue of a one-wave-per-SIMD block (residue reduction,
-// staging, stores) is a large share of a tile's time and nothing overlaps
-// it.  This form keeps two blocks on each compute unit so that one block's
-// epilogue runs beside the other's MFMAs: a 256 x 128 tile per block, four
-// wavefronts of 128 x 64 (8 MFMAs and 6 fragment reads per 32-wide step,
-// 128 accumulators), K slices of 64 bytes in three LDS stages (72 KB),
-// each slice loaded two slices ahead.  The smaller wave tile reads 1.5x the
-// LDS bytes per MFMA, so its K loop is slower than the main kernel's; it
-// wins while K <= 512 (measured at 16384^2 x K, s = 14: 16-17% faster at
-// K = 128 and 256, 10% at 512, 3% slower at 1024).
-constexpr int SHORT_NK = 4;
-
-// 64-byte rows: 16-byte chunk c of row r sits at physical chunk c ^ swz64(r).
-// A fragment read sends 16 consecutive rows to one bank group of 256 bytes,
-// where row r's chunk occupies slot 4 (r mod 4) + physical chunk; (r >> 2) & 3
-// takes each value once on the rows of equal r mod 4 in a 16-row window, so
-// the 16 slots are distinct.  It depends on r mod 16 only, and a 1 KB
-// wavefront load fills exactly 16 rows, so every load uses the same lane
-// offsets.
-__host__ __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
-
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_short_kernel(
-    const int8_t* __restrict__ Ares, const int8_t* __restrict__ Bres, int m_pad, int n_pad, int q_pad, GemmConsts c,
-    uint8_t* __restrict__ rt, int nblocks) {
-  constexpr int BM = 256, BN = 128, BK = 64, WM = 2, WN = 2, NW = WM * WN, STAGES = 3;
-  constexpr int CPR = BK / 16;                  // 4 chunks per row
-  constexpr int ROWS_PER_KB = 1024 / BK;        // 16 rows per wavefront load
-  constexpr int A_LOADS = BM * BK / 1024 / NW;  // 4
-  constexpr int B_LOADS = BN * BK / 1024 / NW;  // 2
-  constexpr int LPW = A_LOADS + B_LOADS;        // loads per wavefront per slice
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int NKS = BK / 32;                  // 2 steps per slice
-  constexpr int NF = FM + FN;                   // 6 fragments per step
-  constexpr int SLOTS = FM * FN;                // 8 MFMAs per step
-  constexpr int STAGE = (BM + BN) * BK;
-  constexpr int CS = BM + 16;                   // staged output column stride
-  static_assert(NKS == 2 && NF <= SLOTS && 2 * LPW <= SLOTS * NKS, "slot plan");
-  static_assert(BN * CS <= STAGES * STAGE && BM % 256 == 0 && BN % (4 * NW) == 0, "staging");
-
-  __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int tiles_m = m_pad / BM, tiles_n = n_pad / BN;
-  int t, mi, nj;
-  tile_of_block<4>(blockIdx.x, nblocks / (tiles_m * tiles_n), tiles_m, tiles_n, t, mi, nj);
-  const int m0 = mi * BM, n0 = nj * BN, out_t = t;
-  const int8_t* Ag = Ares + (long)t * m_pad * q_pad + (long)m0 * q_pad;
-  const int8_t* Bg = Bres + (long)t * n_pad * q_pad + (long)n0 * q_pad;
-  const int nkt = q_pad / BK;  // 64-byte K slices
-
-  // wavefront load: lane l -> row l / 4 of a 16-row block, physical chunk l mod 4
-  const int lane_src = (lane / CPR) * q_pad + (((lane % CPR) ^ swz64(lane / CPR)) * 16);
-  const long kb_stride = (long)ROWS_PER_KB * q_pad;
-  auto load1 = [&](int kk, int li) {
-    int8_t* As = smem + (kk % STAGES) * STAGE;
-    int8_t* Bs = As + BM * BK;
-    const int k0 = kk * BK;
-    if (li < A_LOADS) {
-      const int blk = wave * A_LOADS + li;
-      __builtin_amdgcn_global_load_lds(Ag + blk * kb_stride + k0 + lane_src, As + blk * 1024, 16, 0, 0);
-    } else {
-      const int blk = wave * B_LOADS + (li - A_LOADS);
-      __builtin_amdgcn_global_load_lds(Bg + blk * kb_stride + k0 + lane_src, Bs + blk * 1024, 16, 0, 0);
-    }
-  };
-  const int lrow = lane & 31;
-  const int lkc = lane >> 5;
-  // fragment f of step ks of the slice in stage buf: f < FN are B columns
-  auto read1 = [&](int buf, int ks, int f) -> v4i {
-    const int8_t* As = smem + buf * STAGE;
-    const int8_t* Bs = As + BM * BK;
-    const int kc = ks * 2 + lkc;
-    if (f < FN) {
-      const int row = wn * WTN + f * 32 + lrow;
-      return *reinterpret_cast<const v4i*>(&Bs[row * BK + ((kc ^ swz64(row)) * 16)]);
-    }
-    const int row = wm * WTM + (f - FN) * 32 + lrow;
-    return *reinterpret_cast<const v4i*>(&As[row * BK + ((kc ^ swz64(row)) * 16)]);
-  };
-
-  // this plane's modulus (selected without dynamic indexing of the argument);
-  // the accumulators start at -(m_t - 1)/2, or 0 for m_t = 256, for the
-  // biased reduction of the epilogue
-  int mt = c.m[0];
-#pragma unroll
-  for (int u = 1; u < OZGEMM_S_MAX; ++u) mt = (u == t) ? c.m[u] : mt;
-  const ModBias mb = mod_bias(mt);
-  v16i acc[FM][FN];
-  {
-    v16i start = {};
-    start += mb.bias;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = start;
-  }
-
-  // Prologue: slices 0, 1, 2 (as many as exist); wait for slice 0 only
-  // (loads return in order).  The window after the barrier of slice kt
-  // (its last step, then step 0 of slice kt + 1: 16 slots) loads slice
-  // kt + 3 into the stage that barrier retired; load li follows slot 2 li + 1.
-  const int pro = nkt < STAGES ? nkt : STAGES;
-  for (int kk = 0; kk < pro; ++kk)
-#pragma unroll
-    for (int li = 0; li < LPW; ++li) load1(kk, li);
-  if (pro == 3)
-    wait_vmcnt<2 * LPW>();
-  else if (pro == 2)
-    wait_vmcnt<LPW>();
-  else
-    wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-
-  v4i cur[NF], nxt[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) cur[f] = read1(0, 0, f);
-  for (int kt = 0; kt < nkt; ++kt) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bool last = ks == NKS - 1;
-      const int lslice = last ? kt + 3 : kt + 2;
-      if (last) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's reads of slice kt are done
-        if (kt + 2 < nkt)
-          wait_vmcnt<LPW>();  // slice kt + 1 has landed; slice kt + 2 may still be in flight
-        else
-          wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-      }
-      const int rbuf = last ? (kt + 1) % STAGES : kt % STAGES;  // (past the end: read, unused)
-      const int rks = last ? 0 : ks + 1;
-#pragma unroll
-      for (int r = 0; r < SLOTS; ++r) {
-        const int i = r / FN, j = r % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
-        if (r < NF) nxt[r] = read1(rbuf, rks, r);
-        const int slot = last ? r : SLOTS + r;
-#pragma unroll
-        for (int li = 0; li < LPW; ++li)
-          if (2 * li + 1 == slot && lslice < nkt) load1(lslice, li);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
-    }
-  }
-  wait_vmcnt<0>();
-
-  // epilogue: residues mod m_t, staged as the tile's columns, written as
-  // whole column segments
-  const double inv = 1.0 / (double)mt;  // correctly rounded
-  const long plane = (long)m_pad * n_pad;
-  uint8_t* stage = reinterpret_cast<uint8_t*>(smem);
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int lcol = wn * WTN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int lrow4 = wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5);
-        const v16i& v = acc[i][j];
-        const uint32_t r0 = mod_product_biased(v[4 * g], mb.negm, inv, mb.magic);
-        const uint32_t r1 = mod_product_biased(v[4 * g + 1], mb.negm, inv, mb.magic);
-        const uint32_t r2 = mod_product_biased(v[4 * g + 2], mb.negm, inv, mb.magic);
-        const uint32_t r3 = mod_product_biased(v[4 * g + 3], mb.negm, inv, mb.magic);
-        *reinterpret_cast<uint32_t*>(stage + lcol * CS + lrow4) = low_bytes(r0, r1, r2, r3);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_s_barrier();
-  constexpr int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16, COLS_PER_STORE = 64 / LANES_PER_COL;
-#pragma unroll
-  for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it) {
-    const int lcol = wave * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
-    const int rch = (lane % LANES_PER_COL) * 16;
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + lcol * CS + rch);
-    *reinterpret_cast<uint4*>(rt + (long)out_t * plane + (long)(n0 + lcol) * m_pad + m0 + rch) = v;
-  }
-}
-
 // Sum of the K parts' residues (gemm_grid.h): dst plane t = (sum over p < P
 // of src plane p s + t) mod m_t, 16 bytes per thread.  The bytes of a word are
 // summed in two 16-bit lanes each (even and odd bytes; P <= 64 keeps a sum
@@ -757,11 +566,7 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   auto launch_rt = [&](uint8_t* out, int total, int per) {
     constexpr int WN8 = 4;
     const bool eight = per <= EIGHT_WAVE_MAX_SLICES;
-    if (total == nblocks && per == nk && nk <= SHORT_NK) {  // one part, short K: two blocks per CU
-      const int total_short = (m_pad / 256) * (n_pad / 128) * c.s;
-      hipLaunchKernelGGL(gemm_i8_short_kernel, dim3(total_short), block, 0, st, Ares, Bres, m_pad, n_pad, q_pad, c,
-                         out, total_short);
-    } else if (cus > 0 && total > cus && eight)
+    if (cus > 0 && total > cus && eight)
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, false, true, false, false, true>), dim3(cus),
                          dim3(WM * WN8 * 64), 0, st, Ares, Bres, m_pad, n_pad, q_pad, c, Ct, out, nullptr, 0, per,
                          total);

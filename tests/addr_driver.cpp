@@ -10,7 +10,7 @@
 //         form: main (residue output, one block per tile), persist (the same,
 //         cus blocks walking the tiles), main8 / persist8 (the same with
 //         eight wavefronts of 128 x 64), acc (residue output added to the
-//         earlier K blocks' residues), short, ct (int32 output, MT = 32)
+//         earlier K blocks' residues), ct (int32 output, MT = 32)
 //   plan  <m_pad> <n_pad> <q_pad> <nplanes_a> <nplanes_b> then nout lines "a0 b0 count out"
 //         (preceded by "<nout>")
 //   reduce <m_pad> <n_pad> <s> <parts>
@@ -43,7 +43,6 @@ void check(bool ok, const char* what, long a, long b) {
 void in_range(long off, long len, long size, const char* what) { check(off >= 0 && off + len <= size, what, off, size); }
 
 int swz128(int row, bool bug) { return bug ? (row & 7) : (((row >> 1) ^ (row << 2)) & 7); }
-int swz64(int row) { return (row >> 2) & 3; }
 
 struct Plan {
   int a0, b0, count, out;
@@ -179,74 +178,6 @@ void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bo
   check(SMEM <= 160 * 1024, "lds size", SMEM, 160 * 1024);
 }
 
-// The short-K kernel: 256 x 128 tiles, 64-byte slices in three stages.
-void gemm_short(int m_pad, int n_pad, int q_pad, int s) {
-  const int BM = 256, BN = 128, BK = 64, NW = 4, STAGES = 3, WN = 2;
-  const int CPR = 4, A_LOADS = 4, B_LOADS = 2, LPW = 6, WTM = 128, WTN = 64, FM = 4, FN = 2, NF = 6;
-  const long STAGE = (long)(BM + BN) * BK, SMEM = STAGES * STAGE;
-  const int CS = BM + 16;
-  const int tiles_m = m_pad / BM, tiles_n = n_pad / BN;
-  const long nblocks = (long)tiles_m * tiles_n * s;
-  const long a_plane = (long)m_pad * q_pad, b_plane = (long)n_pad * q_pad, plane = (long)m_pad * n_pad;
-  const long kb_stride = 16L * q_pad;
-  const int nkt = q_pad / BK;
-  for (long L = 0; L < nblocks; ++L) {
-    int t, mi, nj;
-    oz::tile_of_block<4>((int)L, s, tiles_m, tiles_n, t, mi, nj);
-    const int m0 = mi * BM, n0 = nj * BN;
-    const long Ag = t * a_plane + (long)m0 * q_pad, Bg = t * b_plane + (long)n0 * q_pad;
-    for (int kk = 0; kk < nkt; ++kk)
-      for (int w = 0; w < NW; ++w)
-        for (int li = 0; li < LPW; ++li)
-          for (int lane = 0; lane < 64; ++lane) {
-            const long src = (long)(lane / CPR) * q_pad + (((lane % CPR) ^ swz64(lane / CPR)) * 16);
-            const long base = (kk % STAGES) * STAGE;
-            if (li < A_LOADS) {
-              const int blk = w * A_LOADS + li;
-              in_range(Ag + blk * kb_stride + (long)kk * BK + src, 16, s * a_plane, "short A load");
-              in_range(base + blk * 1024L + lane * 16, 16, SMEM, "short A lds");
-            } else {
-              const int blk = w * B_LOADS + (li - A_LOADS);
-              in_range(Bg + blk * kb_stride + (long)kk * BK + src, 16, s * b_plane, "short B load");
-              in_range(base + BM * (long)BK + blk * 1024L + lane * 16, 16, SMEM, "short B lds");
-            }
-          }
-    if (L == 0)
-      for (int buf = 0; buf < STAGES; ++buf)
-        for (int ks = 0; ks < 2; ++ks)
-          for (int w = 0; w < NW; ++w)
-            for (int f = 0; f < NF; ++f)
-              for (int lane = 0; lane < 64; ++lane) {
-                const int wm = w / WN, wn = w % WN, kc = ks * 2 + (lane >> 5);
-                const long base = buf * STAGE;
-                if (f < FN) {
-                  const int row = wn * WTN + f * 32 + (lane & 31);
-                  in_range(base + BM * (long)BK + row * (long)BK + ((kc ^ swz64(row)) * 16), 16, SMEM, "short B frag");
-                } else {
-                  const int row = wm * WTM + (f - FN) * 32 + (lane & 31);
-                  in_range(base + row * (long)BK + ((kc ^ swz64(row)) * 16), 16, SMEM, "short A frag");
-                }
-              }
-    for (int w = 0; w < NW; ++w) {
-      const int wm = w / WN, wn = w % WN;
-      for (int i = 0; i < FM; ++i)
-        for (int j = 0; j < FN; ++j)
-          for (int lane = 0; lane < 64; ++lane)
-            for (int g = 0; g < 4; ++g)
-              in_range((long)(wn * WTN + j * 32 + (lane & 31)) * CS + wm * WTM + i * 32 + 8 * g + 4 * (lane >> 5), 4,
-                       SMEM, "short stage write");
-      const int COLS_PER_WAVE = BN / NW, LANES_PER_COL = BM / 16, COLS_PER_STORE = 64 / LANES_PER_COL;
-      for (int it = 0; it < COLS_PER_WAVE / COLS_PER_STORE; ++it)
-        for (int lane = 0; lane < 64; ++lane) {
-          const int lcol = w * COLS_PER_WAVE + it * COLS_PER_STORE + lane / LANES_PER_COL;
-          const int rch = (lane % LANES_PER_COL) * 16;
-          in_range((long)lcol * CS + rch, 16, SMEM, "short stage read");
-          in_range((long)t * plane + (long)(n0 + lcol) * m_pad + m0 + rch, 16, s * plane, "short store");
-        }
-    }
-  }
-}
-
 // Sum of the K parts' residues: 16 bytes per thread.
 void reduce(int m_pad, int n_pad, int s, int P) {
   const long plane = (long)m_pad * n_pad, chunks = plane / 16, threads = chunks * s;
@@ -334,13 +265,9 @@ int main() {
                      &bug) != 11)
         return 1;
       (void)per;
-      if (!std::strcmp(form, "short"))
-        gemm_short(mp, np, qp, s);
-      else {
-        const bool eight = !std::strcmp(form, "main8") || !std::strcmp(form, "persist8");
-        gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist") || !std::strcmp(form, "persist8"),
-                  !std::strcmp(form, "ct"), !std::strcmp(form, "acc"), parts, kb, ks, false, {}, 0, 0, bug != 0, eight);
-      }
+      const bool eight = !std::strcmp(form, "main8") || !std::strcmp(form, "persist8");
+      gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist") || !std::strcmp(form, "persist8"),
+                !std::strcmp(form, "ct"), !std::strcmp(form, "acc"), parts, kb, ks, false, {}, 0, 0, bug != 0, eight);
     } else if (!std::strcmp(cmd, "plan")) {
       int mp, np, qp, na, nb, nout;
       if (std::scanf("%d %d %d %d %d %d", &mp, &np, &qp, &na, &nb, &nout) != 6) return 1;

@@ -18,8 +18,10 @@ log line; the split choice is also checked through ozgemm_gemm_parts):
   * sequential K blocks (q >= 2^17 and a workspace too small for two K
     parts' planes): 4096 x 2304 x (2^17 + 300), s = 14;
   * K parts: 256 x 256 x 130907 (16 parts, ragged K), s = 14;
-  * one block per tile: 256 x 256 x 640, s = 14;
-  * short-K kernel: 2048 x 2048 x 512 and 2048 x 2048 x 500, s = 14;
+  * one block per tile, eight wavefronts per block (at most 16 K slices):
+    256 x 256 x 640, s = 14;
+  * persistent form with eight wavefronts: 2048 x 2048 x 512 and
+    2048 x 2048 x 500, s = 14;
   * int32 planes and residues together (the unbiased debug form):
     512 x 512 x 130944, s = 14, both outputs checked.
 """
@@ -111,14 +113,14 @@ def test_extremes_k_parts():
 
 def test_extremes_block_per_tile():
     m, n, q, s = 256, 256, 640, 14
-    log(f"extremes, one block per tile: {m} x {n} x {q}, s = {s}")
+    log(f"extremes, one block per tile, eight wavefronts: {m} x {n} x {q}, s = {s}")
     assert run_case(m, n, q, s, seed=4) <= 1
 
 
 @pytest.mark.parametrize("q", [512, 500])
 def test_extremes_short_k(q):
     m, n, s = 2048, 2048, 14
-    log(f"extremes, short-K kernel: {m} x {n} x {q}, s = {s}")
+    log(f"extremes, persistent form, eight wavefronts: {m} x {n} x {q}, s = {s}")
     assert run_case(m, n, q, s, seed=5 + q) <= 1
 
 

@@ -5,8 +5,8 @@ call only enqueues kernels on the configured stream, so it can be captured.
 Each graph is replayed several times with other eager GPU work and
 synchronisations between the replays, and every replay must reproduce the
 eager result bit for bit.  The shapes cover the persistent product grid
-with K parts and the parts' reduction, the short-K product kernel, a long
-inner dimension, and the one-pass residue kernel of B.
+with K parts and the parts' reduction, both wavefront counts of the product
+kernel, a long inner dimension, and the one-pass residue kernel of B.
 """
 import numpy as np
 import pytest
@@ -19,10 +19,11 @@ from gpu_util import dev_colmajor, log
 pytestmark = pytest.mark.gpu
 
 
-# 768 x 65536 x 512: 12 K parts, 1008 blocks on the persistent grid, then the
-# parts' reduction; 1536 x 1024 x 1536: persistent grid, one part; 900 x 300 x
-# 1300: short-K kernel; 300 x (2^17 + 300) x 200: long K as parts;
-# 1024 x 5000 x 700: B's exponents taken in its residue pass (ragged K)
+# 768 x 65536 x 512: 12 K parts, 1008 blocks on the persistent grid (four
+# wavefronts), then the parts' reduction; 1536 x 1024 x 1536: persistent
+# grid, one part, eight wavefronts; 900 x 300 x 1300: three K slices (eight
+# wavefronts); 300 x (2^17 + 300) x 200: long K as parts; 1024 x 5000 x 700:
+# B's exponents taken in its residue pass (ragged K), one block per tile
 @pytest.mark.parametrize("m,q,n,s", [(768, 65536, 512, 14), (1536, 1024, 1536, 14), (900, 300, 1300, 14),
                                      (300, 2**17 + 300, 200, 12), (1024, 5000, 700, 14)])
 def test_dgemm_replays_from_a_graph(m, q, n, s):

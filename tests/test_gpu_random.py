@@ -3,7 +3,7 @@ against the oracles.
 
 24 cases drawn from numpy.random.default_rng(20261202):
   * shapes m, n in 1..300 and q in 1..6000 (some long enough for K parts,
-    some short enough for the short-K kernel);
+    some short enough for the eight-wavefront product form);
   * s in 6..20 where the bit budget leaves k >= 1;
   * phi in {0, 0.5, 1, 2, 8} (the HPL-like generator);
   * the conservative or the OS II-fast bit budget;
