@@ -81,7 +81,8 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 
 // BM x BN output tile per block of WM x WN wavefronts; each wavefront owns a
 // (BM/WM) x (BN/WN) sub-tile of MT x MT tiles of one int8 MFMA:
-//  * MT = 16, v_mfma_i32_16x16x64_i8, for the residue-only products.  On
+//  * MT = 16, v_mfma_i32_16x16x64_i8, for the residue-only products and
+//    the plan products (eight wavefronts, 128 accumulators each).  On
 //    random int8 operands the chip's power limit lets this instruction
 //    sustain about 15% more operations per second than the 32x32x32 one
 //    (3.65 against 3.15 POP/s in a register-only loop); the 8192^3 product
@@ -89,9 +90,11 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 //    (l mod 16) of A (column (l mod 16) of B) from K chunk l / 16 of the
 //    64-wide K step and receives rows 4 (l / 16) + r, r = 0..3, of column
 //    (l mod 16).
-//  * MT = 32, v_mfma_i32_32x32x32_i8, for the int32-output forms (the debug
-//    planes and Scheme I's plan products, whose plan form spills its
-//    accumulators with 16-wide tiles).  Lane l supplies 16 bytes of row
+//  * MT = 32, v_mfma_i32_32x32x32_i8, for the int32 planes of the stage
+//    entry point's debug form (with four wavefronts the 16-wide tiles of
+//    the plan form kept their accumulators in scratch; with eight they fit
+//    in registers, and Scheme I at 4096^3, k = 8, runs 1% (RN) and 8%
+//    (Hybrid) faster than with the 32-wide tiles).  Lane l supplies 16 bytes of row
 //    (l mod 32) from K chunk l / 32 of the 32-wide step and receives rows
 //    8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
 // Both operands use the same lane -> K mapping, so the product is the dot
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int B_LOADS = BN * BK / 1024 / NW;
   constexpr int LPW = A_LOADS + B_LOADS;        // loads per wavefront per slice
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int MT = WRITE_RT && !WRITE_CT ? 16 : 32;  // MFMA tile (see above)
+  constexpr int MT = (WRITE_RT && !WRITE_CT) || (MULTI && NW == 8) ? 16 : 32;  // MFMA tile (see above)
   constexpr int KSTEP = 1024 / MT;              // K bytes per MFMA: 64 or 32
   constexpr int CPS = KSTEP / 16;               // 16-byte K chunks per step
   constexpr int ACC_N = MT * MT / 64;           // accumulators per lane per tile: 4 or 16
@@ -622,7 +625,7 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
 
 hipError_t launch_gemm_multi(const int8_t* Aplanes, const int8_t* Bplanes, int m_pad, int n_pad, int q_pad,
                              const int4* plan, int nout, int32_t* P, hipStream_t st) {
-  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 4;  // eight wavefronts
   if (m_pad % BM || n_pad % BN || q_pad % BK || nout < 1) return hipErrorInvalidValue;
   GemmConsts none{};
   none.s = 1;

@@ -12,7 +12,7 @@
 //         eight wavefronts of 128 x 64), acc (residue output added to the
 //         earlier K blocks' residues), ct (int32 output, MT = 32)
 //   plan  <m_pad> <n_pad> <q_pad> <nplanes_a> <nplanes_b> then nout lines "a0 b0 count out"
-//         (preceded by "<nout>")
+//         (preceded by "<nout>"): int32 output, eight wavefronts
 //   reduce <m_pad> <n_pad> <s> <parts>
 //   residue <rows> <rows_pad> <q> <q_pad> <s> <rs> <ls> <one_pass>
 //   crt <m> <n> <m_pad> <n_pad> <s> <ldc>
@@ -50,7 +50,8 @@ struct Plan {
 
 // The main product kernel: BM = BN = 256, BK = 128 (or 32 with the planted
 // swizzle bug), 2 x 2 wavefronts (2 x 4 with `eight`).  MT = 16 for residue
-// output, 32 for int32.
+// output and for int32 output with eight wavefronts (the plan form), 32 for
+// int32 output with four (the debug form).
 void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bool ct, bool acc_rt, int parts,
                int k_begin, int k_slices, bool multi, const std::vector<Plan>& plan, int a_planes, int b_planes,
                bool swz_bug, bool eight = false) {
@@ -58,7 +59,7 @@ void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bo
   const int CPR = BK / 16, ROWS_PER_KB = 1024 / BK;
   const int A_LOADS = BM * BK / 1024 / NW, B_LOADS = BN * BK / 1024 / NW, LPW = A_LOADS + B_LOADS;
   const int WTM = BM / WM, WTN = BN / WN;
-  const int MT = ct ? 32 : 16, KSTEP = 1024 / MT, CPS = KSTEP / 16, FM = WTM / MT, FN = WTN / MT;
+  const int MT = ct && !eight ? 32 : 16, KSTEP = 1024 / MT, CPS = KSTEP / 16, FM = WTM / MT, FN = WTN / MT;
   const int NKS = BK / KSTEP > 0 ? BK / KSTEP : 1, NF = FM + FN;
   const bool staged = !ct && !acc_rt;  // residue-only output goes through LDS
   const int CS = BM + 16;
@@ -274,7 +275,7 @@ int main() {
       std::vector<Plan> plan(nout);
       for (auto& p : plan)
         if (std::scanf("%d %d %d %d", &p.a0, &p.b0, &p.count, &p.out) != 4) return 1;
-      gemm_main(mp, np, qp, 1, 0, false, true, false, 1, 0, qp / 128, true, plan, na, nb, false);
+      gemm_main(mp, np, qp, 1, 0, false, true, false, 1, 0, qp / 128, true, plan, na, nb, false, true);
     } else if (!std::strcmp(cmd, "reduce")) {
       int mp, np, s, P;
       if (std::scanf("%d %d %d %d", &mp, &np, &s, &P) != 4) return 1;
