@@ -12,13 +12,14 @@
 //
 // Operands are K-contiguous int8 planes: A_t is m_pad x q_pad (row i at
 // i*q_pad), B_t is n_pad x q_pad (column j of B at j*q_pad), so each product
-// is A_t B_t^T.  A block computes a BM x BN output tile with four wavefronts
-// (2 x 2), each owning (BM/2) x (BN/2) built from 16x16 int32 tiles of
-// v_mfma_i32_16x16x64_i8 (residue-only products) or 32x32 tiles of
-// v_mfma_i32_32x32x32_i8 (int32 output); residue-only products whose blocks
-// walk few K slices use eight wavefronts (2 x 4, two per SIMD) instead.  In the multi-product form an output plane is the
-// sum of `count` products (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one
-// long K loop.
+// is A_t B_t^T.  A block computes a 256 x 256 output tile with four
+// wavefronts (2 x 2, one per SIMD), each owning 128 x 128 built from 16x16
+// int32 tiles of v_mfma_i32_16x16x64_i8 (residue-only products) or 32x32
+// tiles of v_mfma_i32_32x32x32_i8 (the int32 debug planes), or with eight
+// wavefronts (2 x 4, two per SIMD) of 128 x 64 16x16 tiles: residue-only
+// products whose blocks walk few K slices, and the multi-product (plan)
+// form, in which an output plane is the sum of `count` products
+// (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one long K loop.
 //
 // LDS: each tile row (BK bytes) is stored as 16-byte chunks whose position
 // is XOR-permuted by a function of the row, so that the rows an MFMA operand
@@ -126,7 +127,9 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 //    other's MFMAs.  Same-box A/B against four wavefronts (s = 14): 3-5%
 //    faster at 16384^2 x 1024, 2.2% at 16384^2 x 2048, 1.3-1.4% at 1024^3
 //    and 2048^3 (8 and 16 K slices per block); 1.3-1.7% slower at
-//    8192^2 x 4096 and 16384^3, within +-2% at 8192^3 (32-128 slices).
+//    8192^2 x 4096 and 16384^3, within +-2% at 8192^3 (32-128 slices).  At
+//    K <= 512 it also beats a kernel of two 256 x 128 blocks per CU (6-10%
+//    at K = 512), whose smaller tile loads 1.5x the bytes per MAC.
 // K parts (gemm_grid.h): plane index p s + t of a residue-only launch is
 // part p of modulus t, covering K slices [k_begin + p k_slices, + k_slices)
 // clipped to q_pad; it writes its residue to plane p s + t of rt.  With one
