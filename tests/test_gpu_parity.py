@@ -234,19 +234,21 @@ def test_short_inner_dimension(m, q, n, s):
     assert same_doubles(C, ref[0])
 
 
-@pytest.mark.parametrize("m,n,q", [(1100, 1000, 2048), (1100, 1000, 2049), (300, 520, 2048), (300, 520, 2049)])
-def test_eight_wave_boundary(m, n, q):
+@pytest.mark.parametrize("m,n,q,parts", [(1100, 1000, 2048, 1), (1100, 1000, 2049, 1), (300, 520, 2048, 1),
+                                         (300, 520, 2049, 1), (256, 200, 4096, 2), (256, 200, 4224, 2)])
+def test_eight_wave_boundary(m, n, q, parts):
     """Residue-only products whose blocks walk at most 16 K slices of 128
-    (q <= 2048) run eight wavefronts per block, longer ones four: q = 2048
-    and 2049 on either side, each in the persistent grid (20 tiles x 14
-    moduli > 256 compute units) and with one block per tile (6 x 14).
+    run eight wavefronts per block, longer ones four: q = 2048 and 2049 on
+    either side, each in the persistent grid (20 tiles x 14 moduli > 256
+    compute units) and with one block per tile (6 x 14); and a single tile
+    cut into two K parts of 16 slices (q = 4096) and of 17 (q = 4224).
     Every stage must match the oracle."""
     import torch
     A, B = hpl_like(m, q, n, 1.0, seed=m + n + q)
     L.ozgemm_free()
-    configure(1536, 1536, 2176, 20)
+    configure(1536, 1536, 4224, 20)
     try:
-        assert L.ozgemm_gemm_parts(m, n, q, 14) == 1
+        assert L.ozgemm_gemm_parts(m, n, q, 14) == parts
         log(f"eight-wave boundary m={m} n={n} q={q}")
         g = run_stages(A, B, 14, want_ct=False)  # int32 planes would take the four-wavefront debug form
         C, _ = run_dgemm(A, B, 14)
