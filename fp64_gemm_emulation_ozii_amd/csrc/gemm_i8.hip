@@ -12,14 +12,13 @@
 //
 // Operands are K-contiguous int8 planes: A_t is m_pad x q_pad (row i at
 // i*q_pad), B_t is n_pad x q_pad (column j of B at j*q_pad), so each product
-// is A_t B_t^T.  A block computes a 256 x 256 output tile with four
-// wavefronts (2 x 2, one per SIMD), each owning 128 x 128 built from 16x16
-// int32 tiles of v_mfma_i32_16x16x64_i8 (residue-only products) or 32x32
-// tiles of v_mfma_i32_32x32x32_i8 (the int32 debug planes), or with eight
-// wavefronts (2 x 4, two per SIMD) of 128 x 64 16x16 tiles: residue-only
-// products whose blocks walk few K slices, and the multi-product (plan)
-// form, in which an output plane is the sum of `count` products
-// (A_{a0+u}, B_{b0-u}), u = 0..count-1, walked as one long K loop.
+// is A_t B_t^T.  A block computes a 256 x 256 output tile from 16x16 int32
+// tiles of v_mfma_i32_16x16x64_i8, with four wavefronts (2 x 2, one per
+// SIMD, 128 x 128 each: residue-only products that walk many K slices) or
+// eight (2 x 4, two per SIMD, 128 x 64 each: residue-only products that
+// walk few, and every int32-output form).  In the multi-product (plan) form
+// an output plane is the sum of `count` products (A_{a0+u}, B_{b0-u}),
+// u = 0..count-1, walked as one long K loop.
 //
 // LDS: each tile row (BK bytes) is stored as 16-byte chunks whose position
 // is XOR-permuted by a function of the row, so that the rows an MFMA operand
@@ -81,25 +80,20 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 }
 
 // BM x BN output tile per block of WM x WN wavefronts; each wavefront owns a
-// (BM/WM) x (BN/WN) sub-tile of MT x MT tiles of one int8 MFMA:
-//  * MT = 16, v_mfma_i32_16x16x64_i8, for the residue-only products and
-//    the plan products (eight wavefronts, 128 accumulators each).  On
-//    random int8 operands the chip's power limit lets this instruction
-//    sustain about 15% more operations per second than the 32x32x32 one
-//    (3.65 against 3.15 POP/s in a register-only loop); the 8192^3 product
-//    phase runs 4-5% faster with it.  Lane l supplies 16 bytes of row
-//    (l mod 16) of A (column (l mod 16) of B) from K chunk l / 16 of the
-//    64-wide K step and receives rows 4 (l / 16) + r, r = 0..3, of column
-//    (l mod 16).
-//  * MT = 32, v_mfma_i32_32x32x32_i8, for the int32 planes of the stage
-//    entry point's debug form (with four wavefronts the 16-wide tiles of
-//    the plan form kept their accumulators in scratch; with eight they fit
-//    in registers, and Scheme I at 4096^3, k = 8, runs 1% (RN) and 8%
-//    (Hybrid) faster than with the 32-wide tiles).  Lane l supplies 16 bytes of row
-//    (l mod 32) from K chunk l / 32 of the 32-wide step and receives rows
-//    8 (r / 4) + 4 (l / 32) + (r mod 4), r = 0..15, of column (l mod 32).
-// Both operands use the same lane -> K mapping, so the product is the dot
-// product over the step whatever order the hardware takes the bytes in.
+// (BM/WM) x (BN/WN) sub-tile of MT x MT = 16 x 16 tiles of
+// v_mfma_i32_16x16x64_i8.  On random int8 operands the chip's power limit
+// lets this instruction sustain about 15% more operations per second than
+// v_mfma_i32_32x32x32_i8 (3.65 against 3.15 POP/s in a register-only loop);
+// the 8192^3 product phase runs 4-5% faster with it.  The int32-output
+// forms used 32 x 32 tiles while they ran four wavefronts, whose 256
+// accumulators went to scratch with 16-wide tiles; with eight wavefronts
+// the 128 accumulators fit in registers, and Scheme I at 4096^3, k = 8,
+// runs 1% (RN) and 8% (Hybrid) faster.  Lane l supplies 16 bytes of row
+// (l mod 16) of A (column (l mod 16) of B) from K chunk l / 16 of the
+// 64-wide K step and receives rows 4 (l / 16) + r, r = 0..3, of column
+// (l mod 16).  Both operands use the same lane -> K mapping, so the product
+// is the dot product over the step whatever order the hardware takes the
+// bytes in.
 //
 // Data movement and instruction order:
 //  * K slices of BK bytes go from HBM straight into LDS (global_load_lds, 16
@@ -107,12 +101,12 @@ __device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t
 //  * One barrier per slice, placed before the last K step's MFMAs: it
 //    publishes slice kt + 1 (this wave's loads of it have landed) and retires
 //    buffer kt mod 2 (this wave's reads of it are in registers).
-//  * Every step is a fixed sequence of MFMA slots (16 with MT = 32, 64 with
-//    MT = 16).  The fragments of the next step are read from LDS, one after
-//    every RS-th slot, and the 16 loads of the slice two ahead go after
-//    slots 1, 1 + RS, 1 + 2 RS, ... of the window that follows the barrier
-//    (the last step of slice kt, then the next slice's steps): over the
-//    first 1024 MFMA cycles of the window with either instruction.
+//  * Every step is a fixed sequence of MFMA slots (64 with four
+//    wavefronts).  The fragments of the next step are read from LDS, one
+//    after every RS-th slot, and the 16 loads of the slice two ahead go
+//    after slots 1, 1 + RS, 1 + 2 RS, ... of the window that follows the
+//    barrier (the last step of slice kt, then the next slice's steps): over
+//    its first 1024 MFMA cycles.
 //    Spreading the loads this way keeps their issue from stalling the MFMA
 //    stream, and the last of them still has half a slice to land.
 //    (Measured at 8192^3 x 14 planes: 7.1 ms with the loads issued as one
@@ -172,24 +166,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int B_LOADS = BN * BK / 1024 / NW;
   constexpr int LPW = A_LOADS + B_LOADS;        // loads per wavefront per slice
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int MT = (WRITE_RT && !WRITE_CT) || (MULTI && NW == 8) ? 16 : 32;  // MFMA tile (see above)
-  constexpr int KSTEP = 1024 / MT;              // K bytes per MFMA: 64 or 32
+  constexpr int MT = 16;                        // MFMA tile (see above)
+  constexpr int KSTEP = 1024 / MT;              // K bytes per MFMA: 64
   constexpr int CPS = KSTEP / 16;               // 16-byte K chunks per step
-  constexpr int ACC_N = MT * MT / 64;           // accumulators per lane per tile: 4 or 16
+  constexpr int ACC_N = MT * MT / 64;           // accumulators per lane per tile: 4
   constexpr int FM = WTM / MT, FN = WTN / MT;
   constexpr int NKS = BK / KSTEP;               // K steps per slice
   constexpr int NF = FM + FN;                   // fragments per step
   constexpr int SLOTS = FM * FN;                // MFMAs per step
   constexpr int RS = SLOTS / NF;                // slots per fragment read (four wavefronts)
   constexpr bool EIGHT = NW == 8;
-  static_assert(NW == 4 || (EIGHT && MT == 16 && FM == 8 && FN == 4), "four wavefronts, or eight of 128 x 64");
+  static_assert(NW == 4 || (EIGHT && FM == 8 && FN == 4), "four wavefronts, or eight of 128 x 64");
+  static_assert(EIGHT || (WRITE_RT && !WRITE_CT), "int32 output runs eight wavefronts");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && BM * BK % (1024 * NW) == 0, "tile/wave mismatch");
   static_assert((EIGHT || SLOTS % NF == 0) && NKS >= 2, "slot plan: whole reads per step, two steps per slice");
   static_assert(load_slot(EIGHT, RS, LPW - 1) < SLOTS * NKS, "every load has a slot in its window");
   // loads of a slice issued in the window before it: those whose slot falls
-  // in the last step of the slice before (8 with MT = 32, all with MT = 16)
+  // in the last step of the slice before (all of them)
   constexpr int HALF_LOADS = early_loads(EIGHT, RS, LPW, SLOTS);
-  static_assert(HALF_LOADS == (MT == 32 ? 8 : LPW), "prologue load count");
+  static_assert(HALF_LOADS == LPW, "prologue load count");
   typedef int acc_t __attribute__((ext_vector_type(ACC_N)));
 
   // Staged residue output: the words are first placed in LDS as the tile's
@@ -370,10 +365,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int r = 0; r < SLOTS; ++r) {
           const int i = r / FN, j = r % FN;
-          if constexpr (MT == 16)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur[FN + i], cur[j], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);  // the slot's MFMA issues before its read
 #pragma unroll
           for (int f = 0; f < NF; ++f)
@@ -559,7 +551,7 @@ __global__ __launch_bounds__(256) void rt_parts_reduce_kernel(const uint8_t* __r
 hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_pad, int q_pad, const GemmConsts& c,
                        int32_t* Ct, uint8_t* rt, const SplitChoice& split, uint8_t* parts, int cus,
                        hipStream_t st) {
-  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2;
+  constexpr int BM = 256, BN = 256, BK = 128, WM = 2, WN = 2, WN8 = 4;  // four or eight wavefronts
   static_assert(BK == SPLIT_K_SLICE, "K parts are counted in kernel slices");
   if (m_pad % BM || n_pad % BN || q_pad % BK) return hipErrorInvalidValue;
   const int tiles = (n_pad / BN) * (m_pad / BM);
@@ -570,7 +562,6 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
   // (the persistent form) when there are more tiles than units; blocks that
   // walk few K slices run eight wavefronts
   auto launch_rt = [&](uint8_t* out, int total, int per) {
-    constexpr int WN8 = 4;
     const bool eight = per <= EIGHT_WAVE_MAX_SLICES;
     if (cus > 0 && total > cus && eight)
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, false, true, false, false, true>), dim3(cus),
@@ -615,12 +606,13 @@ hipError_t launch_gemm(const int8_t* Ares, const int8_t* Bres, int m_pad, int n_
     }
     return hipGetLastError();
   }
+  // int32 planes (the stage entry point's debug output): eight wavefronts
   if (Ct != nullptr && rt != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, true, false>), grid, block, 0, st, Ares, Bres,
-                       m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, true, true, false>), grid, dim3(WM * WN8 * 64), 0, st,
+                       Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
   else if (Ct != nullptr)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, true, false, false>), grid, block, 0, st, Ares,
-                       Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN8, true, false, false>), grid, dim3(WM * WN8 * 64), 0, st,
+                       Ares, Bres, m_pad, n_pad, q_pad, c, Ct, rt, nullptr, 0, nk, nblocks);
   else if (rt != nullptr)
     launch_rt(rt, nblocks, nk);
   return hipGetLastError();

@@ -10,7 +10,9 @@
 //         form: main (residue output, one block per tile), persist (the same,
 //         cus blocks walking the tiles), main8 / persist8 (the same with
 //         eight wavefronts of 128 x 64), acc (residue output added to the
-//         earlier K blocks' residues), ct (int32 output, MT = 32)
+//         earlier K blocks' residues), ct (int32 output, eight wavefronts),
+//         ct4 (int32 output with four wavefronts of 32 x 32 tiles: an earlier
+//         form, kept for the planted swizzle case)
 //   plan  <m_pad> <n_pad> <q_pad> <nplanes_a> <nplanes_b> then nout lines "a0 b0 count out"
 //         (preceded by "<nout>"): int32 output, eight wavefronts
 //   reduce <m_pad> <n_pad> <s> <parts>
@@ -49,9 +51,8 @@ struct Plan {
 };
 
 // The main product kernel: BM = BN = 256, BK = 128 (or 32 with the planted
-// swizzle bug), 2 x 2 wavefronts (2 x 4 with `eight`).  MT = 16 for residue
-// output and for int32 output with eight wavefronts (the plan form), 32 for
-// int32 output with four (the debug form).
+// swizzle bug), 2 x 2 wavefronts (2 x 4 with `eight`).  MT = 16, except 32
+// for int32 output with four wavefronts (the earlier form of `ct4`).
 void gemm_main(int m_pad, int n_pad, int q_pad, int s, int cus, bool persist, bool ct, bool acc_rt, int parts,
                int k_begin, int k_slices, bool multi, const std::vector<Plan>& plan, int a_planes, int b_planes,
                bool swz_bug, bool eight = false) {
@@ -266,9 +267,10 @@ int main() {
                      &bug) != 11)
         return 1;
       (void)per;
-      const bool eight = !std::strcmp(form, "main8") || !std::strcmp(form, "persist8");
+      const bool eight = !std::strcmp(form, "main8") || !std::strcmp(form, "persist8") || !std::strcmp(form, "ct");
       gemm_main(mp, np, qp, s, cus, !std::strcmp(form, "persist") || !std::strcmp(form, "persist8"),
-                !std::strcmp(form, "ct"), !std::strcmp(form, "acc"), parts, kb, ks, false, {}, 0, 0, bug != 0, eight);
+                !std::strcmp(form, "ct") || !std::strcmp(form, "ct4"), !std::strcmp(form, "acc"), parts, kb, ks, false,
+                {}, 0, 0, bug != 0, eight);
     } else if (!std::strcmp(cmd, "plan")) {
       int mp, np, qp, na, nb, nout;
       if (std::scanf("%d %d %d %d %d %d", &mp, &np, &qp, &na, &nb, &nout) != 6) return 1;

@@ -127,6 +127,8 @@ def test_residue_and_crt_index_ranges(driver, rows, q):
 
 def test_planted_swizzle_overrun_is_caught(driver):
     """32-byte K slices with the row & 7 swizzle address chunks 0..7 of a
-    two-chunk row: the emulation reports the access outside the buffer."""
-    res = run(driver, [gemm_line("ct", 256, 256, 256, 2, bug=1), gemm_line("ct", 256, 256, 256, 2)])
+    two-chunk row: the emulation reports the access outside the buffer (on
+    the four-wavefront int32 form with 32 x 32 tiles that the faulting
+    probe used; the same form without the planted slice is in bounds)."""
+    res = run(driver, [gemm_line("ct4", 256, 256, 256, 2, bug=1), gemm_line("ct4", 256, 256, 256, 2)])
     assert res[0].startswith("bad") and res[1].startswith("ok")
