@@ -224,8 +224,8 @@ def test_k_parts(m, q, n, s, parts):
 
 @pytest.mark.parametrize("m,q,n,s", [(700, 512, 900, 14), (1100, 129, 520, 11), (257, 384, 1536, 16)])
 def test_short_inner_dimension(m, q, n, s):
-    """K <= 512: residue-only products run as two 256 x 128 blocks per compute
-    unit (three 64-byte K stages); several row and column tiles, ragged."""
+    """K <= 512 (at most four K slices per block): residue-only products run
+    eight wavefronts per block; several row and column tiles, ragged."""
     A, B = hpl_like(m, q, n, 1.0, seed=m * 7 + q)
     log(f"short K m={m} q={q} n={n} s={s}")
     ref = oz.dgemm(A, B, s, stages=True)
