@@ -20,7 +20,6 @@ constexpr int SCALE_CHUNK = 128;  // columns of A per partial row-max block
 
 inline size_t round_up(size_t x, size_t r) { return (x + r - 1) / r * r; }
 
-// Per-modulus constants for the residue kernel (Ozaki II notes §6).
 // |x| as its IEEE bit pattern: for non-negative doubles the unsigned integer
 // order is the numeric order, and Inf/NaN patterns sort above every finite
 // value (the scale step and the column residue kernel take maxima on these).
@@ -65,16 +64,16 @@ __device__ __forceinline__ int32_t fast_exponent(int32_t e, uint64_t S, int kapp
   return kb - (kappa - c - e);
 }
 
+// Per-modulus constants for the residue kernel (Ozaki II notes §6).
 struct ResidueConsts {
   int s;
   int k;                        // shift base: row shift is k - e_i
   int kmag;                     // |A'| < 2^kmag (selects the residue arithmetic)
   int col_kappa;                // B in one pass under OS II-fast: kappa_B (-1: the exponent as it is)
   int m[OZGEMM_S_MAX];          // moduli
-  int lo[OZGEMM_S_MAX];         // -floor(m/2)
-  int hi[OZGEMM_S_MAX];         // ceil(m/2) - 1
   double inv[OZGEMM_S_MAX];     // RN(1/m)
-  double c32[OZGEMM_S_MAX];     // 2^32 mod m
+  double c26[OZGEMM_S_MAX];     // 2^26 mod m
+  double c52[OZGEMM_S_MAX];     // 2^52 mod m
 };
 
 // Per-modulus constants for the GEMM epilogue.

@@ -218,10 +218,9 @@ void make_consts(int s, int q, int mode, ResidueConsts* rc, GemmConsts* gc, CrtC
   for (int t = 0; t < s; ++t) {
     const int m = mods[t];
     rc->m[t] = gc->m[t] = m;
-    rc->lo[t] = -(m / 2);
-    rc->hi[t] = (m + 1) / 2 - 1;
     rc->inv[t] = gc->inv[t] = 1.0 / (double)m;
-    rc->c32[t] = (double)((1ull << 32) % (unsigned long long)m);
+    rc->c26[t] = (double)((1ull << 26) % (unsigned long long)m);
+    rc->c52[t] = (double)((1ull << 52) % (unsigned long long)m);
   }
   const Big M = product_M(s);
   const int bits = big_bitlen(M);

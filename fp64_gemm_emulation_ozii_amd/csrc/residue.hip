@@ -20,13 +20,16 @@
 // 2^(k-52) 1.01 / m of A'/m + 1/2.  For odd m, A'/m + 1/2 = (2A' + m) / 2m has
 // an odd numerator, so it is at least 1/2m away from every integer, and for
 // m = 256 every step is exact: with k <= 50 the floor is therefore always
-// the exact one and r = fma(-q, m, A') needs no correction.  For
-// 50 < k <= 53 the quotient can be off by one and one +-m correction is
-// applied.  When k > 53 (|A'| < 2^78 since k <= 77 for s <= 20), A' is split
-// once per element as A' = h 2^32 + l with h = floor(A' 2^-32) (|h| < 2^46)
-// and 0 <= l < 2^32, both exact; per modulus, r_h = smod(h) needs no
-// correction (|h| < 2^50), v = r_h (2^32 mod m) + l is an exact integer below
-// 2^34, and r = smod(v) again needs none.
+// the exact one and r = fma(-q, m, A') needs no correction.  Wider A'
+// (|A'| < 2^78 since k <= 77 for s <= 20) is split once per element as
+// A' = a2 2^52 + a1 2^26 + a0 with a2 = floor(A' 2^-52) and a0, a1 in
+// [0, 2^26), all exact (a2 = 0 and one split while |A'| < 2^53); per modulus
+// v = a2 (2^52 mod m) + a1 (2^26 mod m) + a0 is an exact integer congruent to
+// A' with |v| < 2^35, so the uncorrected reduction of v is the residue: 5 or
+// 6 FP64 operations per modulus, where a +-m correction (50 < k <= 53) or a
+// second reduction of the high part (k > 53) took 8.  Same calls at 8192^3:
+// 2.5% faster at s = 15 under the conservative budget, 0.7-0.9% under
+// OS II-fast at s = 14 and 15.
 #include "oz_internal.h"
 
 namespace oz {
@@ -37,17 +40,6 @@ constexpr int TR = 32;           // rows per tile
 constexpr int TK = 128;          // inner-dimension entries per tile
 constexpr int LDS_STRIDE = TK + 1;  // doubles; odd stride spreads banks
 
-template <bool FIX>
-__device__ __forceinline__ int smod_small(double a, int m, double inv, int lo, int hi) {
-  const double qf = __builtin_floor(__builtin_fma(a, inv, 0.5));
-  int ri = (int)__builtin_fma(-qf, (double)m, a);
-  if (FIX) {
-    ri = ri > hi ? ri - m : ri;
-    ri = ri < lo ? ri + m : ri;
-  }
-  return ri;
-}
-
 // Low bytes of four words as one word (three byte permutes).
 __device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
   const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.0, b1.0, 0, 0
@@ -55,27 +47,11 @@ __device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Same without correction, kept in FP64 (|a| < 2^50).
-__device__ __forceinline__ double smod_exact_d(double a, double m, double inv) {
-  const double qf = __builtin_floor(__builtin_fma(a, inv, 0.5));
-  return __builtin_fma(-qf, m, a);
-}
-
 // The s residues of 16 consecutive entries of one row, A' exact integers in
 // a[] (|A'| < 2^kmag), as one 16-byte store per modulus at dst + t plane_stride.
 template <int MODE>  // 0: kmag <= 50, 1: kmag <= 53, 2: kmag > 53
 __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueConsts& c, int8_t* dst,
                                                  long plane_stride) {
-  constexpr bool BIG = MODE == 2;
-  double ahi[BIG ? 16 : 1];
-  if (BIG) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      ahi[j] = __builtin_floor(a[j] * 0x1p-32);
-      a[j] = __builtin_fma(ahi[j], -0x1p32, a[j]);  // low part, in [0, 2^32)
-    }
-  }
-
   if (MODE == 0) {
     // |A'| < 2^50: A' + 1.5 2^52 is exact, and so is fma(-q, m, A' + 1.5 2^52)
     // = 1.5 2^52 + r, whose low 32 bits are r in two's complement
@@ -100,21 +76,31 @@ __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueC
     }
     return;
   }
+  // |A'| >= 2^50: A' = a2 2^52 + a1 2^26 + a0 (MODE 2; a2 = 0 for MODE 1),
+  // a0 and a1 in [0, 2^26), all exact; v = a2 (2^52 mod m) + a1 (2^26 mod m)
+  // + a0 is congruent to A' and |v| < 2^35, so one uncorrected reduction of v
+  // gives the residue.
+  constexpr bool BIG = MODE == 2;
+  double a1[16], a2[BIG ? 16 : 1];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (BIG) {
+      a2[j] = __builtin_floor(a[j] * 0x1p-52);
+      a[j] = __builtin_fma(a2[j], -0x1p52, a[j]);  // in [0, 2^52)
+    }
+    a1[j] = __builtin_floor(a[j] * 0x1p-26);
+    a[j] = __builtin_fma(a1[j], -0x1p26, a[j]);  // a0, in [0, 2^26)
+  }
   for (int t = 0; t < c.s; ++t) {
-    const int m = c.m[t];
-    const double inv = c.inv[t];
-    const int lo = c.lo[t], hi = c.hi[t];
+    const double md = (double)c.m[t], inv = c.inv[t], c26 = c.c26[t];
+    const double c52 = BIG ? c.c52[t] : 0.0;
     uint32_t rb[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      int ri;
-      if (BIG) {
-        const double rh = smod_exact_d(ahi[j], (double)m, inv);
-        ri = smod_small<false>(__builtin_fma(rh, c.c32[t], a[j]), m, inv, lo, hi);
-      } else {
-        ri = smod_small<true>(a[j], m, inv, lo, hi);
-      }
-      rb[j] = (uint32_t)ri;
+      double v = __builtin_fma(a1[j], c26, a[j]);
+      if (BIG) v = __builtin_fma(a2[j], c52, v);
+      const double qf = __builtin_floor(__builtin_fma(v, inv, 0.5));
+      rb[j] = (uint32_t)(int)__builtin_fma(-qf, md, v);
     }
     uint4 out;
     out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
