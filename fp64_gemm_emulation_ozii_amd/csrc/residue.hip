@@ -13,24 +13,16 @@
 // 16-byte store per modulus into the K-contiguous plane the GEMM reads.
 //
 // Exactness.  a * 2^(k - e) is exact (a power-of-two scaling) unless it
-// falls below 2^-1022, where it is below 1 and truncates to 0 anyway.
-// The symmetric residue is r = A' - m floor(A'/m + 1/2), which lies in
-// [-floor(m/2), ceil(m/2) - 1] for odd and even m alike.  The quotient is
-// taken as q = floor(fma(A', RN(1/m), 1/2)); the fma result is within
-// 2^(k-52) 1.01 / m of A'/m + 1/2.  For odd m, A'/m + 1/2 = (2A' + m) / 2m has
-// an odd numerator, so it is at least 1/2m away from every integer, and for
-// m = 256 every step is exact: with k <= 50 the floor is therefore always
-// the exact one and r = fma(-q, m, A') needs no correction.  Wider A'
-// (|A'| < 2^78 since k <= 77 for s <= 20) is split once per element as
-// A' = a2 2^52 + a1 2^26 + a0 with a2 = floor(A' 2^-52) and a0, a1 in
-// [0, 2^26), all exact (a2 = 0 and one split while |A'| < 2^53); per modulus
-// v = a2 (2^52 mod m) + a1 (2^26 mod m) + a0 is an exact integer congruent to
-// A' with |v| < 2^35, so the uncorrected reduction of v is the residue: 5 or
-// 6 FP64 operations per modulus, where a +-m correction (50 < k <= 53) or a
-// second reduction of the high part (k > 53) took 8.  Same calls at 8192^3:
-// 2.5% faster at s = 15 under the conservative budget, 0.7-0.9% under
-// OS II-fast at s = 14 and 15.
+// falls below 2^-1022, where it is below 1 and truncates to 0 anyway.  The
+// residues of the truncated integers come from residue_arith.h: one
+// uncorrected reduction per modulus while |A'| < 2^50, and for wider A'
+// (|A'| < 2^78 since k <= 77 for s <= 20) a split into 26-bit pieces once per
+// entry, then 5 or 6 FP64 operations per modulus, where a +-m correction
+// (50 < k <= 53) or a second reduction of a 2^32 high part (k > 53) took 8
+// (same calls at 8192^3: 2.5% faster at s = 15 under the conservative
+// budget, 0.7-0.9% under OS II-fast at s = 14 and 15).
 #include "oz_internal.h"
+#include "residue_arith.h"
 
 namespace oz {
 
@@ -52,10 +44,7 @@ __device__ __forceinline__ uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_
 template <int MODE>  // 0: kmag <= 50, 1: kmag <= 53, 2: kmag > 53
 __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueConsts& c, int8_t* dst,
                                                  long plane_stride) {
-  if (MODE == 0) {
-    // |A'| < 2^50: A' + 1.5 2^52 is exact, and so is fma(-q, m, A' + 1.5 2^52)
-    // = 1.5 2^52 + r, whose low 32 bits are r in two's complement
-    // (|r| <= 128 < 2^51); no conversion instruction is needed
+  if (MODE == 0) {  // |A'| < 2^50 (residue_arith.h)
     double am[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) am[j] = a[j] + 0x1.8p52;
@@ -63,10 +52,7 @@ __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueC
       const double md = (double)c.m[t], inv = c.inv[t];
       uint32_t rb[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const double qf = __builtin_floor(__builtin_fma(a[j], inv, 0.5));
-        rb[j] = (uint32_t)__builtin_bit_cast(uint64_t, __builtin_fma(-qf, md, am[j]));
-      }
+      for (int j = 0; j < 16; ++j) rb[j] = residue_narrow(a[j], am[j], md, inv);
       uint4 out;
       out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
       out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
@@ -76,32 +62,18 @@ __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueC
     }
     return;
   }
-  // |A'| >= 2^50: A' = a2 2^52 + a1 2^26 + a0 (MODE 2; a2 = 0 for MODE 1),
-  // a0 and a1 in [0, 2^26), all exact; v = a2 (2^52 mod m) + a1 (2^26 mod m)
-  // + a0 is congruent to A' and |v| < 2^35, so one uncorrected reduction of v
-  // gives the residue.
+  // |A'| >= 2^50: split once into 26-bit pieces, one reduction per modulus
+  // (residue_arith.h)
   constexpr bool BIG = MODE == 2;
-  double a1[16], a2[BIG ? 16 : 1];
+  double a1[16], a2[16] = {};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (BIG) {
-      a2[j] = __builtin_floor(a[j] * 0x1p-52);
-      a[j] = __builtin_fma(a2[j], -0x1p52, a[j]);  // in [0, 2^52)
-    }
-    a1[j] = __builtin_floor(a[j] * 0x1p-26);
-    a[j] = __builtin_fma(a1[j], -0x1p26, a[j]);  // a0, in [0, 2^26)
-  }
+  for (int j = 0; j < 16; ++j) split_wide<BIG>(a[j], a1[j], a2[j]);
   for (int t = 0; t < c.s; ++t) {
     const double md = (double)c.m[t], inv = c.inv[t], c26 = c.c26[t];
     const double c52 = BIG ? c.c52[t] : 0.0;
     uint32_t rb[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      double v = __builtin_fma(a1[j], c26, a[j]);
-      if (BIG) v = __builtin_fma(a2[j], c52, v);
-      const double qf = __builtin_floor(__builtin_fma(v, inv, 0.5));
-      rb[j] = (uint32_t)(int)__builtin_fma(-qf, md, v);
-    }
+    for (int j = 0; j < 16; ++j) rb[j] = (uint32_t)residue_wide<BIG>(a[j], a1[j], a2[j], c26, c52, md, inv);
     uint4 out;
     out.x = pack_bytes(rb[0], rb[1], rb[2], rb[3]);
     out.y = pack_bytes(rb[4], rb[5], rb[6], rb[7]);
