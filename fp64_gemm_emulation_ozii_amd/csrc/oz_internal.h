@@ -104,6 +104,9 @@ hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64
 hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
                                    hipStream_t st);
 hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st);
+// launch_row_max_partial and launch_col_exp as one launch (q >= 1).
+hipError_t launch_scale_pair(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride, int nchunks,
+                             const double* B, int n, int ldb, int32_t* f, hipStream_t st);
 // OS II-fast: replace e (f) by e' (f') from Cauchy-Schwarz row (column) norm bounds.
 hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
                            int kappa, int kb, int32_t* e, hipStream_t st);
@@ -117,6 +120,11 @@ hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, in
 bool col_residue_fits(int q);
 hipError_t launch_col_residue(const double* X, int rows, int q, long rs, int32_t* ex, const ResidueConsts& c,
                               int8_t* planes, int rows_pad, int q_pad, hipStream_t st);
+// The residues of column-major A (m x q) and B (q x n) as one launch, the
+// same planes as two launch_residue calls write (m, n, q >= 1).
+hipError_t launch_residue_pair(const double* A, int m, int lda, const int32_t* e, int8_t* Aplanes, int m_pad,
+                               const double* B, int n, int ldb, const int32_t* f, int8_t* Bplanes, int n_pad, int q,
+                               int q_pad, const ResidueConsts& c, hipStream_t st);
 hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad,
                           double* prime, long prime_rs, long prime_ls, hipStream_t st);

@@ -473,14 +473,24 @@ int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda
   int ka = 0, kb = 0;
   if (fast) fast_budget(s, &ka, &kb);
   const int kbase = std::max(ka, kb);
-  if (m > 0) {
-    OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, x.stream));
+  if (m > 0 && n > 0 && q > 0) {
+    // A's partial row maxima and B's column maxima in one launch
+    OZ_CHECK(launch_scale_pair(A, m, q, lda, pmax, mp, nch, B, n, ldb, f, x.stream));
     OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
-    if (fast) OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, x.stream));
-  }
-  if (n > 0) {
-    OZ_CHECK(launch_col_exp(B, q, n, ldb, f, x.stream));
-    if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
+    if (fast) {
+      OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, x.stream));
+      OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
+    }
+  } else {
+    if (m > 0) {
+      OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, x.stream));
+      OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
+      if (fast) OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, x.stream));
+    }
+    if (n > 0) {
+      OZ_CHECK(launch_col_exp(B, q, n, ldb, f, x.stream));
+      if (fast) OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
+    }
   }
   if (x.bound == OZGEMM_BOUND_ACCU && m > 0 && n > 0 && q > 0) {
     int mpc, npc, qpc;
@@ -699,8 +709,8 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   const bool b_one_pass = x.bound != OZGEMM_BOUND_ACCU && col_residue_fits(q);
   if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
   if (ev) OZ_CHECK(hipEventRecord((*ev)[1], x.stream));
-  OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
   if (x.panels > 1) {
+    OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
     // Panel pipeline (Ozaki II notes §8 and §11: the CRT of one part of C
     // runs while the products of the next part do).  Column panel p of C
     // keeps its B residue planes and product residues contiguous (planes of
@@ -732,10 +742,12 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
     if (ev) OZ_CHECK(hipEventRecord((*ev)[4], x.stream));
     return OZGEMM_OK;
   }
-  if (b_one_pass)
+  if (b_one_pass) {
+    OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
     OZ_CHECK(launch_col_residue(B, n, q, ldb, f, rc, Bres, np, qp, x.stream));
-  else
-    OZ_CHECK(launch_residue(B, n, q, ldb, 1, f, rc, Bres, np, qp, nullptr, 0, 0, x.stream));
+  } else {  // A's and B's residues in one launch
+    OZ_CHECK(launch_residue_pair(A, m, lda, e, Ares, mp, B, n, ldb, f, Bres, np, q, qp, rc, x.stream));
+  }
   if (ev) OZ_CHECK(hipEventRecord((*ev)[2], x.stream));
   SplitChoice split{};
   int cus = 0;

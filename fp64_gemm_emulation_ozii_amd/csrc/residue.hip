@@ -83,15 +83,16 @@ __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueC
   }
 }
 
+// Tile (bx, by) of residue_kernel: rows by*TR.., inner-dimension entries
+// bx*TK.., staged through `tile` (TR * LDS_STRIDE doubles of LDS).
 template <bool ROWS_CONTIG, int MODE>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
-__global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
-                                                       long ls, const int32_t* __restrict__ ex, ResidueConsts c,
-                                                       int8_t* __restrict__ planes, long plane_stride, int q_pad,
-                                                       double* __restrict__ prime, long prime_rs, long prime_ls) {
-  __shared__ double tile[TR * LDS_STRIDE];
+__device__ __forceinline__ void residue_tile(double* tile, int bx, int by, const double* __restrict__ X, int rows,
+                                             int q, long rs, long ls, const int32_t* __restrict__ ex,
+                                             const ResidueConsts& c, int8_t* __restrict__ planes, long plane_stride,
+                                             int q_pad, double* __restrict__ prime, long prime_rs, long prime_ls) {
   const int tid = threadIdx.x;
-  const int r0 = blockIdx.y * TR;
-  const int l0 = blockIdx.x * TK;
+  const int r0 = by * TR;
+  const int l0 = bx * TK;
 
   // ---- coalesced load into LDS (zero outside the matrix) ----
   // All loads are issued before any is used: out-of-range lanes read a
@@ -161,6 +162,39 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
   }
 
   write_residues16<MODE>(a, c, planes + (long)grow * q_pad + l0 + cseg, plane_stride);
+}
+
+template <bool ROWS_CONTIG, int MODE>
+__global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__ X, int rows, int q, long rs,
+                                                       long ls, const int32_t* __restrict__ ex, ResidueConsts c,
+                                                       int8_t* __restrict__ planes, long plane_stride, int q_pad,
+                                                       double* __restrict__ prime, long prime_rs, long prime_ls) {
+  __shared__ double tile[TR * LDS_STRIDE];
+  residue_tile<ROWS_CONTIG, MODE>(tile, blockIdx.x, blockIdx.y, X, rows, q, rs, ls, ex, c, planes, plane_stride,
+                                  q_pad, prime, prime_rs, prime_ls);
+}
+
+// A's and B's residues in one launch (column-major A: rows contiguous; B:
+// the inner dimension contiguous): blocks [0, na) are A's tiles, the rest
+// B's, each in row-major order of a (q_pad / TK)-wide grid.  For small
+// products the two passes' ramp-up and drain then overlap.
+template <int MODE>
+__global__ __launch_bounds__(256) void residue_pair_kernel(const double* __restrict__ A, int m, long lda,
+                                                            const int32_t* __restrict__ e,
+                                                            int8_t* __restrict__ Aplanes, int m_pad,
+                                                            const double* __restrict__ B, int n, long ldb,
+                                                            const int32_t* __restrict__ f,
+                                                            int8_t* __restrict__ Bplanes, int n_pad, int q, int q_pad,
+                                                            ResidueConsts c, int na) {
+  __shared__ double tile[TR * LDS_STRIDE];
+  const int gx = q_pad / TK;
+  const int b = blockIdx.x;
+  if (b < na)
+    residue_tile<true, MODE>(tile, b % gx, b / gx, A, m, q, 1, lda, e, c, Aplanes, (long)m_pad * q_pad, q_pad,
+                             nullptr, 0, 0);
+  else
+    residue_tile<false, MODE>(tile, (b - na) % gx, (b - na) / gx, B, n, q, ldb, 1, f, c, Bplanes,
+                              (long)n_pad * q_pad, q_pad, nullptr, 0, 0);
 }
 
 
@@ -259,6 +293,23 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
     else OZ_RES_LAUNCH(false, 2);
   }
 #undef OZ_RES_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_residue_pair(const double* A, int m, int lda, const int32_t* e, int8_t* Aplanes, int m_pad,
+                               const double* B, int n, int ldb, const int32_t* f, int8_t* Bplanes, int n_pad, int q,
+                               int q_pad, const ResidueConsts& c, hipStream_t st) {
+  if (q < 1 || m < 1 || n < 1) return hipErrorInvalidValue;
+  const long na = (long)(q_pad / TK) * (m_pad / TR), nb = (long)(q_pad / TK) * (n_pad / TR);
+  if (na + nb > 0x7fffffffL) return hipErrorInvalidValue;
+  const int mode = c.kmag <= 50 ? 0 : (c.kmag <= 53 ? 1 : 2);
+#define OZ_RES_PAIR(MD)                                                                                       \
+  hipLaunchKernelGGL((residue_pair_kernel<MD>), dim3((unsigned)(na + nb)), dim3(256), 0, st, A, m, (long)lda, e, \
+                     Aplanes, m_pad, B, n, (long)ldb, f, Bplanes, n_pad, q, q_pad, c, (int)na)
+  if (mode == 0) OZ_RES_PAIR(0);
+  else if (mode == 1) OZ_RES_PAIR(1);
+  else OZ_RES_PAIR(2);
+#undef OZ_RES_PAIR
   return hipGetLastError();
 }
 

@@ -25,11 +25,12 @@
 
 namespace oz {
 
-__global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __restrict__ A, int m, int q,
-                                                               long lda, int chunk,
-                                                               uint64_t* __restrict__ pmax, int m_stride) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int l0 = blockIdx.y * chunk;
+// Block (bx, by) of the partial row maxima: rows bx*256.., columns by*chunk..
+__device__ __forceinline__ void row_max_partial_block(const double* __restrict__ A, int m, int q, long lda,
+                                                      int chunk, uint64_t* __restrict__ pmax, int m_stride, int bx,
+                                                      int by) {
+  const int i = bx * 256 + threadIdx.x;
+  const int l0 = by * chunk;
   const int l1 = min(q, l0 + chunk);
   uint64_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (i < m) {
@@ -47,7 +48,13 @@ __global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __re
   }
 #pragma unroll
   for (int u = 1; u < 8; ++u) v[0] = umax64(v[0], v[u]);
-  pmax[(long)blockIdx.y * m_stride + i] = v[0];
+  pmax[(long)by * m_stride + i] = v[0];
+}
+
+__global__ __launch_bounds__(256) void row_max_partial_kernel(const double* __restrict__ A, int m, int q,
+                                                               long lda, int chunk,
+                                                               uint64_t* __restrict__ pmax, int m_stride) {
+  row_max_partial_block(A, m, q, lda, chunk, pmax, m_stride, blockIdx.x, blockIdx.y);
 }
 
 // 64 rows per block, four threads per row each taking every fourth chunk
@@ -74,10 +81,11 @@ __global__ __launch_bounds__(256) void row_exp_finalize_kernel(const uint64_t* _
     e[i] = exponent_of_bits(umax64(umax64(part[0][r], part[1][r]), umax64(part[2][r], part[3][r])));
 }
 
-__global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__ B, int q, int n, long ldb,
-                                                       int32_t* __restrict__ f) {
+// Block bx of the column maxima: columns 4 bx.., one wavefront each.
+__device__ __forceinline__ void col_exp_block(const double* __restrict__ B, int q, int n, long ldb,
+                                              int32_t* __restrict__ f, int bx) {
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int j = bx * 4 + (threadIdx.x >> 6);
   if (j >= n) return;  // whole wavefront exits together
   const double* col = B + (long)j * ldb;
   uint64_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -91,6 +99,26 @@ __global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__
   for (int u = 1; u < 8; ++u) v = umax64(v, w[u]);
   for (int off = 32; off > 0; off >>= 1) v = umax64(v, (uint64_t)__shfl_xor((unsigned long long)v, off, 64));
   if (lane == 0) f[j] = exponent_of_bits(v);
+}
+
+__global__ __launch_bounds__(256) void col_exp_kernel(const double* __restrict__ B, int q, int n, long ldb,
+                                                       int32_t* __restrict__ f) {
+  col_exp_block(B, q, n, ldb, f, blockIdx.x);
+}
+
+// A's partial row maxima and B's column maxima in one launch (they are
+// independent): blocks [0, na) are row_max_partial_kernel's in row-major
+// order of its (gxa x nchunks) grid, the rest col_exp_kernel's.  For small
+// products the two kernels' ramp-up and drain then overlap.
+__global__ __launch_bounds__(256) void scale_pair_kernel(const double* __restrict__ A, int m, int q, long lda,
+                                                          int chunk, uint64_t* __restrict__ pmax, int m_stride,
+                                                          int gxa, int na, const double* __restrict__ B, int n,
+                                                          long ldb, int32_t* __restrict__ f) {
+  const int b = blockIdx.x;
+  if (b < na)
+    row_max_partial_block(A, m, q, lda, chunk, pmax, m_stride, b % gxa, b / gxa);
+  else
+    col_exp_block(B, q, n, ldb, f, b - na);
 }
 
 __global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
@@ -164,6 +192,15 @@ hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, in
                                    hipStream_t st) {
   hipLaunchKernelGGL(row_exp_finalize_kernel, dim3((m + 63) / 64), dim3(256), 0, st, pmax, m, m_stride, nchunks,
                      e);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_pair(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride, int nchunks,
+                             const double* B, int n, int ldb, int32_t* f, hipStream_t st) {
+  const int chunk = (q + nchunks - 1) / nchunks;
+  const int gxa = (m + 255) / 256, na = gxa * nchunks, nb = (n + 3) / 4;
+  hipLaunchKernelGGL(scale_pair_kernel, dim3(na + nb), dim3(256), 0, st, A, m, q, (long)lda, chunk, pmax, m_stride,
+                     gxa, na, B, n, (long)ldb, f);
   return hipGetLastError();
 }
 

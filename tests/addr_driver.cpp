@@ -17,6 +17,8 @@
 //         (preceded by "<nout>"): int32 output, eight wavefronts
 //   reduce <m_pad> <n_pad> <s> <parts>
 //   residue <rows> <rows_pad> <q> <q_pad> <s> <rs> <ls> <one_pass>
+//   residue_pair <m> <m_pad> <lda> <n> <n_pad> <ldb> <q> <q_pad> <s>
+//   scale_pair <m> <m_pad> <lda> <n> <ldb> <q> <nchunks>
 //   crt <m> <n> <m_pad> <n_pad> <s> <ldc>
 // Output: one line "ok <accesses>" or "bad <what> ..." per input line.
 #include <cstdio>
@@ -193,12 +195,11 @@ void reduce(int m_pad, int n_pad, int s, int P) {
 
 // The residue kernels (and the accu band kernel, the same tile walk): a tile
 // of 32 rows x 128 entries per block, 16-byte stores per modulus.
-void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, bool one_pass) {
+// One 32 x 128 tile (bx, by) of residue_kernel.
+void residue_tile(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, int bx, int by) {
   const long plane_stride = (long)rows_pad * q_pad;
   const long src_size = rows < 1 ? 0 : (rows - 1) * rs + (q - 1) * ls + 1;
-  if (!one_pass) {
-    for (int by = 0; by < rows_pad / 32; ++by)
-      for (int bx = 0; bx < q_pad / 128; ++bx)
+  check(bx >= 0 && bx < q_pad / 128 && by >= 0 && by < rows_pad / 32, "residue tile", bx, by);
         for (int tid = 0; tid < 256; ++tid) {
           const int r0 = by * 32, l0 = bx * 128;
           if (rows >= 1) {
@@ -223,6 +224,14 @@ void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, 
             in_range(t * plane_stride + (long)(r0 + r) * q_pad + l0 + cseg, 16, s * plane_stride, "residue store");
           in_range((long)bx * rows_pad + r0 + r, 1, (long)(q_pad / 128) * rows_pad, "band partial sum");
         }
+}
+
+void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, bool one_pass) {
+  const long plane_stride = (long)rows_pad * q_pad;
+  const long src_size = rows < 1 ? 0 : (rows - 1) * rs + (q - 1) * ls + 1;
+  if (!one_pass) {
+    for (int by = 0; by < rows_pad / 32; ++by)
+      for (int bx = 0; bx < q_pad / 128; ++bx) residue_tile(rows, rows_pad, q, q_pad, s, rs, ls, bx, by);
   } else {
     for (int j = 0; j < rows_pad; ++j) {
       if (j < rows)
@@ -232,6 +241,57 @@ void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, 
           in_range(t * plane_stride + (long)j * q_pad + 16L * seg, 16, s * plane_stride, "column residue store");
     }
   }
+}
+
+// residue_pair_kernel: blocks [0, na) are column-major A's tiles, the rest
+// B's, each decoded from the linear block id over a (q_pad / 128)-wide grid;
+// every tile of both grids must come up exactly once.
+void residue_pair(int m, int m_pad, long lda, int n, int n_pad, long ldb, int q, int q_pad, int s) {
+  const int gx = q_pad / 128;
+  const long na = (long)gx * (m_pad / 32), nb = (long)gx * (n_pad / 32);
+  std::vector<int> seen_a(na, 0), seen_b(nb, 0);
+  for (long b = 0; b < na + nb; ++b) {
+    if (b < na) {
+      const int bx = (int)(b % gx), by = (int)(b / gx);
+      residue_tile(m, m_pad, q, q_pad, s, 1, lda, bx, by);
+      ++seen_a[(long)by * gx + bx];
+    } else {
+      const int bx = (int)((b - na) % gx), by = (int)((b - na) / gx);
+      residue_tile(n, n_pad, q, q_pad, s, ldb, 1, bx, by);
+      ++seen_b[(long)by * gx + bx];
+    }
+  }
+  for (long t = 0; t < na; ++t) check(seen_a[t] == 1, "A tile count", t, seen_a[t]);
+  for (long t = 0; t < nb; ++t) check(seen_b[t] == 1, "B tile count", t, seen_b[t]);
+}
+
+// scale_pair_kernel: blocks [0, na) are row_max_partial_kernel's over a
+// (gxa x nchunks) grid, the rest col_exp_kernel's (four columns each).
+void scale_pair(int m, int m_pad, long lda, int n, long ldb, int q, int nchunks) {
+  const int chunk = (q + nchunks - 1) / nchunks, gxa = (m + 255) / 256;
+  const long na = (long)gxa * nchunks, nb = (n + 3) / 4;
+  const long a_size = (long)(m - 1) + (long)(q - 1) * lda + 1, b_size = (long)(q - 1) + (long)(n - 1) * ldb + 1;
+  std::vector<int> seen(na, 0);
+  for (long b = 0; b < na + nb; ++b) {
+    if (b < na) {
+      const int bx = (int)(b % gxa), by = (int)(b / gxa);
+      ++seen[(long)by * gxa + bx];
+      for (int tid = 0; tid < 256; ++tid) {
+        const int i = bx * 256 + tid, l0 = by * chunk, l1 = q < l0 + chunk ? q : l0 + chunk;
+        if (i < m)
+          for (int l = l0; l < l1; ++l) in_range(i + (long)l * lda, 1, a_size, "row max load");
+        in_range((long)by * m_pad + i, 1, (long)nchunks * m_pad, "row max partial store");
+      }
+    } else {
+      for (int w = 0; w < 4; ++w) {
+        const long j = (b - na) * 4 + w;
+        if (j >= n) continue;
+        for (int l = 0; l < q; ++l) in_range(l + j * ldb, 1, b_size, "column max load");
+        in_range(j, 1, n, "column exponent store");
+      }
+    }
+  }
+  for (long t = 0; t < na; ++t) check(seen[t] == 1, "row max block count", t, seen[t]);
 }
 
 // CRT: four rows of one column per thread, two columns per thread pass.
@@ -287,6 +347,16 @@ int main() {
       long rs, ls;
       if (std::scanf("%d %d %d %d %d %ld %ld %d", &rows, &rows_pad, &q, &q_pad, &s, &rs, &ls, &one) != 8) return 1;
       residue(rows, rows_pad, q, q_pad, s, rs, ls, one != 0);
+    } else if (!std::strcmp(cmd, "residue_pair")) {
+      int m, mp, n, np, q, qp, s;
+      long lda, ldb;
+      if (std::scanf("%d %d %ld %d %d %ld %d %d %d", &m, &mp, &lda, &n, &np, &ldb, &q, &qp, &s) != 9) return 1;
+      residue_pair(m, mp, lda, n, np, ldb, q, qp, s);
+    } else if (!std::strcmp(cmd, "scale_pair")) {
+      int m, mp, n, q, nch;
+      long lda, ldb;
+      if (std::scanf("%d %d %ld %d %ld %d %d", &m, &mp, &lda, &n, &ldb, &q, &nch) != 7) return 1;
+      scale_pair(m, mp, lda, n, ldb, q, nch);
     } else if (!std::strcmp(cmd, "crt")) {
       int m, n, mp, np, s;
       long ldc;

@@ -32,7 +32,8 @@ def run(driver, lines):
     out = subprocess.run([driver], input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     res = out.stdout.split("\n")[:-1]
-    assert len(res) == sum(1 for l in lines if l.split()[0] in ("gemm", "plan", "reduce", "residue", "crt"))
+    assert len(res) == sum(1 for l in lines if l.split()[0] in ("gemm", "plan", "reduce", "residue", "crt",
+                                                                 "residue_pair", "scale_pair"))
     return res
 
 
@@ -121,6 +122,20 @@ def test_residue_and_crt_index_ranges(driver, rows, q):
              f"crt {rows} 3 {rp} 256 20 {rows}"]
     if 4096 <= q <= 8192:
         lines.append(f"residue {rows} {rp} {q} {qp} 14 {q} 1 1")  # B in one pass
+    for r in run(driver, lines):
+        assert r.startswith("ok"), r
+
+
+@pytest.mark.parametrize("m,n,q", [(1, 1, 1), (300, 257, 1000), (257, 33, 129), (1024, 1024, 1024)])
+def test_pair_launches_stay_in_bounds(driver, m, n, q):
+    """The one-launch forms of A's and B's residue passes and of their scale
+    passes: every block decodes to a tile of the two separate grids, each
+    tile comes up once, and every access stays inside its buffer."""
+    mp, np_, qp = pad(m, 256), pad(n, 256), pad(q, 128)
+    lines = [f"residue_pair {m} {mp} {m + 3} {n} {np_} {q + 1} {q} {qp} 14",
+             f"residue_pair {m} {mp} {m} {n} {np_} {q} {q} {qp} 20"]
+    for nch in (1, 8, min(128, max(1, q // 8))):
+        lines.append(f"scale_pair {m} {mp} {m + 5} {n} {q + 2} {q} {nch}")
     for r in run(driver, lines):
         assert r.startswith("ok"), r
 
