@@ -111,6 +111,10 @@ hipError_t launch_scale_pair(const double* A, int m, int q, int lda, uint64_t* p
 hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
                            int kappa, int kb, int32_t* e, hipStream_t st);
 hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, int kb, int32_t* f, hipStream_t st);
+// launch_row_fast and launch_col_fast with A's and B's norm passes as one launch.
+hipError_t launch_fast_pair(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
+                            int kappa_a, const double* B, int n, int ldb, int kappa_b, int kb, int32_t* e,
+                            int32_t* f, hipStream_t st);
 
 // Residues of the rows of X where element (r, l) sits at X[r*rs + l*ls].
 // Writes `rows_pad` x q_pad int8 planes (plane stride rows_pad*q_pad).

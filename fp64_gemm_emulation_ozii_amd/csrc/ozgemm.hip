@@ -477,10 +477,7 @@ int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda
     // A's partial row maxima and B's column maxima in one launch
     OZ_CHECK(launch_scale_pair(A, m, q, lda, pmax, mp, nch, B, n, ldb, f, x.stream));
     OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
-    if (fast) {
-      OZ_CHECK(launch_row_fast(A, m, q, lda, pmax, mp, nch, ka, kbase, e, x.stream));
-      OZ_CHECK(launch_col_fast(B, q, n, ldb, kb, kbase, f, x.stream));
-    }
+    if (fast) OZ_CHECK(launch_fast_pair(A, m, q, lda, pmax, mp, nch, ka, B, n, ldb, kb, kbase, e, f, x.stream));
   } else {
     if (m > 0) {
       OZ_CHECK(launch_row_max_partial(A, m, q, lda, pmax, mp, nch, x.stream));

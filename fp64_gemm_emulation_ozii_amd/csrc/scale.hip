@@ -121,12 +121,12 @@ __global__ __launch_bounds__(256) void scale_pair_kernel(const double* __restric
     col_exp_block(B, q, n, ldb, f, b - na);
 }
 
-__global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
-                                                                long lda, int chunk,
-                                                                const int32_t* __restrict__ e,
-                                                                uint64_t* __restrict__ psum, int m_stride) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int l0 = blockIdx.y * chunk;
+// Block (bx, by) of the partial row norm bounds: rows bx*256.., columns by*chunk..
+__device__ __forceinline__ void row_norm_partial_block(const double* __restrict__ A, int m, int q, long lda,
+                                                       int chunk, const int32_t* __restrict__ e,
+                                                       uint64_t* __restrict__ psum, int m_stride, int bx, int by) {
+  const int i = bx * 256 + threadIdx.x;
+  const int l0 = by * chunk;
   const int l1 = min(q, l0 + chunk);
   uint64_t s0 = 0, s1 = 0;
   if (i < m) {
@@ -145,7 +145,14 @@ __global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __r
       }
     }
   }
-  psum[(long)blockIdx.y * m_stride + i] = s0 + s1;
+  psum[(long)by * m_stride + i] = s0 + s1;
+}
+
+__global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
+                                                                long lda, int chunk,
+                                                                const int32_t* __restrict__ e,
+                                                                uint64_t* __restrict__ psum, int m_stride) {
+  row_norm_partial_block(A, m, q, lda, chunk, e, psum, m_stride, blockIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(256) void row_fast_finalize_kernel(const uint64_t* __restrict__ psum, int m,
@@ -158,10 +165,11 @@ __global__ __launch_bounds__(256) void row_fast_finalize_kernel(const uint64_t* 
   e[i] = fast_exponent(e[i], S, kappa, kb);
 }
 
-__global__ __launch_bounds__(256) void col_fast_kernel(const double* __restrict__ B, int q, int n, long ldb,
-                                                        int kappa, int kb, int32_t* __restrict__ f) {
+// Block bx of the column norm bounds: columns 4 bx.., one wavefront each.
+__device__ __forceinline__ void col_fast_block(const double* __restrict__ B, int q, int n, long ldb, int kappa,
+                                               int kb, int32_t* __restrict__ f, int bx) {
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int j = bx * 4 + (threadIdx.x >> 6);
   if (j >= n) return;  // whole wavefront exits together
   const int fj = f[j];
   uint64_t S = 0;
@@ -178,6 +186,25 @@ __global__ __launch_bounds__(256) void col_fast_kernel(const double* __restrict_
     for (int off = 32; off > 0; off >>= 1) S += (uint64_t)__shfl_xor((unsigned long long)S, off, 64);
   }
   if (lane == 0) f[j] = fast_exponent(fj, S, kappa, kb);
+}
+
+__global__ __launch_bounds__(256) void col_fast_kernel(const double* __restrict__ B, int q, int n, long ldb,
+                                                        int kappa, int kb, int32_t* __restrict__ f) {
+  col_fast_block(B, q, n, ldb, kappa, kb, f, blockIdx.x);
+}
+
+// OS II-fast's partial row norm bounds of A and column bounds of B in one
+// launch (independent, like scale_pair_kernel's two halves).
+__global__ __launch_bounds__(256) void fast_pair_kernel(const double* __restrict__ A, int m, int q, long lda,
+                                                         int chunk, const int32_t* __restrict__ e,
+                                                         uint64_t* __restrict__ psum, int m_stride, int gxa, int na,
+                                                         const double* __restrict__ B, int n, long ldb, int kappa_b,
+                                                         int kb, int32_t* __restrict__ f) {
+  const int b = blockIdx.x;
+  if (b < na)
+    row_norm_partial_block(A, m, q, lda, chunk, e, psum, m_stride, b % gxa, b / gxa);
+  else
+    col_fast_block(B, q, n, ldb, kappa_b, kb, f, b - na);
 }
 
 hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,
@@ -217,6 +244,18 @@ hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psu
                      m_stride);
   hipLaunchKernelGGL(row_fast_finalize_kernel, dim3((m + 255) / 256), dim3(256), 0, st, psum, m, m_stride, nchunks,
                      kappa, kb, e);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_pair(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
+                            int kappa_a, const double* B, int n, int ldb, int kappa_b, int kb, int32_t* e,
+                            int32_t* f, hipStream_t st) {
+  const int chunk = (q + nchunks - 1) / nchunks;
+  const int gxa = (m + 255) / 256, na = gxa * nchunks, nb = (n + 3) / 4;
+  hipLaunchKernelGGL(fast_pair_kernel, dim3(na + nb), dim3(256), 0, st, A, m, q, (long)lda, chunk, e, psum,
+                     m_stride, gxa, na, B, n, (long)ldb, kappa_b, kb, f);
+  hipLaunchKernelGGL(row_fast_finalize_kernel, dim3((m + 255) / 256), dim3(256), 0, st, psum, m, m_stride, nchunks,
+                     kappa_a, kb, e);
   return hipGetLastError();
 }
 

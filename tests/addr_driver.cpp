@@ -267,6 +267,8 @@ void residue_pair(int m, int m_pad, long lda, int n, int n_pad, long ldb, int q,
 
 // scale_pair_kernel: blocks [0, na) are row_max_partial_kernel's over a
 // (gxa x nchunks) grid, the rest col_exp_kernel's (four columns each).
+// fast_pair_kernel (OS II-fast's norm passes) decodes its blocks the same way
+// and reads the same elements of A and B.
 void scale_pair(int m, int m_pad, long lda, int n, long ldb, int q, int nchunks) {
   const int chunk = (q + nchunks - 1) / nchunks, gxa = (m + 255) / 256;
   const long na = (long)gxa * nchunks, nb = (n + 3) / 4;
