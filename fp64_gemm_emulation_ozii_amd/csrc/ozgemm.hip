@@ -620,7 +620,6 @@ int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const d
   return 0;
 }
 
-// Argument checks of ozgemm_dgemm and ozgemm_dgemm_noalloc (BLAS style).
 // Phase-timing events only carry timestamps, read after the caller has
 // synchronised, so they skip the system-scope release a default event record
 // performs: that fence (a cache write-back between dependent kernels) cost
@@ -628,6 +627,7 @@ int s1_split(const S1Layout& L, int m, int n, int q, int k, int variant, const d
 // untimed; 74 us without the fence).
 constexpr unsigned kTimingEventFlags = hipEventDisableSystemFence;
 
+// Argument checks of ozgemm_dgemm and ozgemm_dgemm_noalloc (BLAS style).
 int check_dgemm_args(int m, int n, int q, const double* A, int lda, const double* B, int ldb, const double* C,
                      int ldc, int s) {
   const int st = check_common(m, n, q, A, lda, B, ldb);
