@@ -197,7 +197,6 @@ __global__ __launch_bounds__(256) void residue_pair_kernel(const double* __restr
                               (long)n_pad * q_pad, q_pad, nullptr, 0, 0);
 }
 
-
 // B in one pass (Ozaki II notes §15: scaling, truncation, modulo and packing
 // fused): one block per row j of the B planes, i.e. per column of B, which
 // is contiguous.  The block loads the column into LDS (coalesced, all loads
@@ -275,6 +274,7 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad, double* prime,
                           long prime_rs, long prime_ls, hipStream_t st) {
   if (q < 1) return hipErrorInvalidValue;  // q = 0 has no residues (callers handle it)
+  if (q_pad % TK || rows_pad % TR || q_pad < q || rows_pad < rows) return hipErrorInvalidValue;  // whole tiles
   if (rows_pad / TR > 65535) return hipErrorInvalidValue;  // grid.y
   dim3 grid(q_pad / TK, rows_pad / TR);
   const long plane_stride = (long)rows_pad * q_pad;
@@ -300,6 +300,8 @@ hipError_t launch_residue_pair(const double* A, int m, int lda, const int32_t* e
                                const double* B, int n, int ldb, const int32_t* f, int8_t* Bplanes, int n_pad, int q,
                                int q_pad, const ResidueConsts& c, hipStream_t st) {
   if (q < 1 || m < 1 || n < 1) return hipErrorInvalidValue;
+  if (q_pad % TK || m_pad % TR || n_pad % TR || q_pad < q || m_pad < m || n_pad < n)
+    return hipErrorInvalidValue;  // whole tiles
   const long na = (long)(q_pad / TK) * (m_pad / TR), nb = (long)(q_pad / TK) * (n_pad / TR);
   if (na + nb > 0x7fffffffL) return hipErrorInvalidValue;
   const int mode = c.kmag <= 50 ? 0 : (c.kmag <= 53 ? 1 : 2);
