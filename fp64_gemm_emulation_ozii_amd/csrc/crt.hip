@@ -111,6 +111,9 @@ __global__ void fill_zero_kernel(double* C, int m, int n, long ldc) {
 
 hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e, const int32_t* f,
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
+  // each thread reads four bytes of a column of every plane: m_pad must hold
+  // whole groups of four rows
+  if (m < 1 || n < 1 || m_pad < m || n_pad < n || m_pad % 4 || ldc < m) return hipErrorInvalidValue;
   // two columns per thread (the second one's loads overlap the first's
   // arithmetic)
   dim3 grid((m + 1023) / 1024, std::min((n + 1) / 2, 65535));
