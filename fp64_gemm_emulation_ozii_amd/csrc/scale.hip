@@ -207,8 +207,16 @@ __global__ __launch_bounds__(256) void fast_pair_kernel(const double* __restrict
     col_fast_block(B, q, n, ldb, kappa_b, kb, f, b - na);
 }
 
+// The partial-sum kernels write one word per row of every 256-row block,
+// padding rows included, into each of the nchunks rows of stride m_stride.
+// q = 0 is valid: every row (column) then has the exponent of zero.
+inline bool row_args_ok(int m, int q, int m_stride, int nchunks) {
+  return m >= 1 && q >= 0 && nchunks >= 1 && nchunks <= 65535 && m_stride >= (m + 255) / 256 * 256;
+}
+
 hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride,
                                   int nchunks, hipStream_t st) {
+  if (!row_args_ok(m, q, m_stride, nchunks)) return hipErrorInvalidValue;
   const int chunk = (q + nchunks - 1) / nchunks;
   dim3 grid((m + 255) / 256, nchunks);
   hipLaunchKernelGGL(row_max_partial_kernel, grid, dim3(256), 0, st, A, m, q, (long)lda, chunk, pmax, m_stride);
@@ -217,6 +225,7 @@ hipError_t launch_row_max_partial(const double* A, int m, int q, int lda, uint64
 
 hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, int nchunks, int32_t* e,
                                    hipStream_t st) {
+  if (!row_args_ok(m, 1, m_stride, nchunks)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(row_exp_finalize_kernel, dim3((m + 63) / 64), dim3(256), 0, st, pmax, m, m_stride, nchunks,
                      e);
   return hipGetLastError();
@@ -224,6 +233,7 @@ hipError_t launch_row_exp_finalize(const uint64_t* pmax, int m, int m_stride, in
 
 hipError_t launch_scale_pair(const double* A, int m, int q, int lda, uint64_t* pmax, int m_stride, int nchunks,
                              const double* B, int n, int ldb, int32_t* f, hipStream_t st) {
+  if (!row_args_ok(m, q, m_stride, nchunks) || n < 1) return hipErrorInvalidValue;
   const int chunk = (q + nchunks - 1) / nchunks;
   const int gxa = (m + 255) / 256, na = gxa * nchunks, nb = (n + 3) / 4;
   hipLaunchKernelGGL(scale_pair_kernel, dim3(na + nb), dim3(256), 0, st, A, m, q, (long)lda, chunk, pmax, m_stride,
@@ -232,12 +242,14 @@ hipError_t launch_scale_pair(const double* A, int m, int q, int lda, uint64_t* p
 }
 
 hipError_t launch_col_exp(const double* B, int q, int n, int ldb, int32_t* f, hipStream_t st) {
+  if (n < 1 || q < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(col_exp_kernel, dim3((n + 3) / 4), dim3(256), 0, st, B, q, n, (long)ldb, f);
   return hipGetLastError();
 }
 
 hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
                            int kappa, int kb, int32_t* e, hipStream_t st) {
+  if (!row_args_ok(m, q, m_stride, nchunks)) return hipErrorInvalidValue;
   const int chunk = (q + nchunks - 1) / nchunks;
   dim3 grid((m + 255) / 256, nchunks);
   hipLaunchKernelGGL(row_norm_partial_kernel, grid, dim3(256), 0, st, A, m, q, (long)lda, chunk, e, psum,
@@ -250,6 +262,7 @@ hipError_t launch_row_fast(const double* A, int m, int q, int lda, uint64_t* psu
 hipError_t launch_fast_pair(const double* A, int m, int q, int lda, uint64_t* psum, int m_stride, int nchunks,
                             int kappa_a, const double* B, int n, int ldb, int kappa_b, int kb, int32_t* e,
                             int32_t* f, hipStream_t st) {
+  if (!row_args_ok(m, q, m_stride, nchunks) || n < 1) return hipErrorInvalidValue;
   const int chunk = (q + nchunks - 1) / nchunks;
   const int gxa = (m + 255) / 256, na = gxa * nchunks, nb = (n + 3) / 4;
   hipLaunchKernelGGL(fast_pair_kernel, dim3(na + nb), dim3(256), 0, st, A, m, q, (long)lda, chunk, e, psum,
@@ -260,6 +273,7 @@ hipError_t launch_fast_pair(const double* A, int m, int q, int lda, uint64_t* ps
 }
 
 hipError_t launch_col_fast(const double* B, int q, int n, int ldb, int kappa, int kb, int32_t* f, hipStream_t st) {
+  if (n < 1 || q < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(col_fast_kernel, dim3((n + 3) / 4), dim3(256), 0, st, B, q, n, (long)ldb, kappa, kb, f);
   return hipGetLastError();
 }

@@ -141,6 +141,35 @@ def test_q_zero_writes_zero_and_empty_shapes():
     L.ozgemm_dgemm(4, 0, 3, dummy, 4, dummy, 3, Cd, 4, 14)
 
 
+@pytest.mark.parametrize("bound", ["conservative", "fast"])
+def test_stage_scale_empty_inner_dimension(bound):
+    """q = 0 through the scale entry point: every row and column is empty,
+    so each exponent is the oracle's exponent of an empty row (0) under both
+    budgets; no entry of A or B is read."""
+    import torch
+    m, n = 300, 200
+    A, B = np.zeros((m, 0)), np.zeros((0, n))
+    want_e = oz.row_exponents(A)
+    want_f = oz.col_exponents(B)
+    if bound == "fast":
+        ka, kb = oz.cs_budget(oz.crt_constants(oz.greedy_moduli(14))[0])
+        base = max(ka, kb)
+        want_e = oz.fast_exponents(A, want_e, ka, base)
+        want_f = oz.fast_exponents(B.T, want_f, kb, base)
+    dummy = torch.zeros(8, dtype=torch.float64, device="cuda")
+    e = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    f = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    log(f"stage_scale q = 0, {bound}")
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_FAST if bound == "fast" else L.OZGEMM_BOUND_CONSERVATIVE)
+    try:
+        L.ozgemm_stage_scale(m, n, 0, 14, dummy, m, dummy, 1, e, f)
+        torch.cuda.synchronize()
+    finally:
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
+    assert np.array_equal(e.cpu().numpy(), want_e)
+    assert np.array_equal(f.cpu().numpy(), want_f)
+
+
 def test_invariants_on_gpu():
     A, B = hpl_like(60, 70, 50, 1.0, seed=8)
     C, _ = run_dgemm(A, B, 14)
