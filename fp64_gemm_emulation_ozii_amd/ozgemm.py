@@ -212,7 +212,8 @@ def ozgemm_set_stream(stream=None) -> int:
 
 
 def ozgemm_set_panels(panels: int) -> int:
-    """Column panels of the ozgemm_dgemm pipeline: 0 automatic, 1 off, P forced."""
+    """Column panels of the ozgemm_dgemm pipeline: 0 or 1 no pipeline (the
+    default), 2..OZGEMM_PANELS_MAX that many panels where the shape allows."""
     return _check(lib().ozgemm_set_panels(panels), "ozgemm_set_panels")
 
 
