@@ -14,7 +14,8 @@ Every C must equal the oracle's bit for bit (NaN positions alike) and, for
 Scheme II, lie within 2^-50 (|A||B|)_ij of it.  The Scheme I sweep draws
 16 cases of the same kinds with k in 2..10 slices and the RN or the Hybrid
 variant.  12 more Scheme II cases draw q from [4000, 9000), around the range
-where B's exponents are taken in its residue pass.
+where B's exponents are taken in its residue pass, and 10 run the OS II-accu
+budget with phi up to 16.
 """
 import numpy as np
 import pytest
@@ -146,6 +147,55 @@ def test_random_one_pass_range_case(case):
         configure(MAX_M, MAX_N, MAX_Q, 20)
     ref = oz.dgemm(A, B, s, bound=bound)
     assert same_doubles(C, ref), first_diff(C, ref)
+
+
+# ---- 10 Scheme II cases under the OS II-accu bit budget ----
+
+def draw_accu_cases(count: int, seed: int = 20261205):
+    """The same kinds of case under OS II-accu (Ozaki II notes §9), whose
+    budget depends on the range of every entry of |A'||B'|: q up to 3000,
+    phi up to 16 (wide exponent ranges are what the budget is for).  Short
+    and long q alternate, and the special rows and phi cycle through every
+    kind and value (ten distinct pairs)."""
+    kinds = ["none", "zero", "tiny", "huge", "nonfinite"]
+    phis = [0.5, 1.0, 4.0, 16.0, 0.0]
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        m = int(rng.integers(1, MAX_M + 1))
+        n = int(rng.integers(1, MAX_N + 1))
+        q = int(rng.integers(1, 600)) if len(cases) % 2 == 0 else int(rng.integers(600, 3001))
+        s = int(rng.integers(8, 21))
+        M, _, _ = oz.crt_constants(oz.greedy_moduli(s))
+        if oz.kbits(M, q) < 1:
+            continue
+        phi = phis[(len(cases) // 2) % len(phis)]
+        pads = tuple(int(rng.integers(0, 4)) for _ in range(3))
+        special = kinds[len(cases) % len(kinds)]
+        cases.append((m, n, q, s, phi, pads, special, int(rng.integers(0, 2**31))))
+    return cases
+
+
+ACCU_CASES = draw_accu_cases(10)
+
+
+@pytest.mark.parametrize("case", range(len(ACCU_CASES)))
+def test_random_accu_case(case):
+    m, n, q, s, phi, pads, special, seed = ACCU_CASES[case]
+    log(f"random accu case {case}: m={m} n={n} q={q} s={s} phi={phi} pads={pads} special={special}")
+    A, B = make_inputs(m, n, q, phi, special, seed)
+    L.ozgemm_set_bound(L.OZGEMM_BOUND_ACCU)
+    try:
+        C, _ = run_dgemm(A, B, s, lda=m + pads[0], ldb=q + pads[1], ldc=m + pads[2])
+    finally:
+        L.ozgemm_set_bound(L.OZGEMM_BOUND_CONSERVATIVE)
+    ref = oz.dgemm(A, B, s, bound="accu")
+    assert same_doubles(C, ref), first_diff(C, ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        finite_rows = np.isfinite(A).all(axis=1)
+        finite_cols = np.isfinite(B).all(axis=0)
+        sub = np.ix_(finite_rows, finite_cols)
+        assert within_tolerance(C[sub], ref[sub], A[finite_rows], B[:, finite_cols])
 
 
 # ---- Scheme I: 16 cases of the same kinds, k in 2..10, RN or Hybrid ----
