@@ -125,10 +125,15 @@ bool col_residue_fits(int q);
 hipError_t launch_col_residue(const double* X, int rows, int q, long rs, int32_t* ex, const ResidueConsts& c,
                               int8_t* planes, int rows_pad, int q_pad, hipStream_t st);
 // The residues of column-major A (m x q) and B (q x n) as one launch, the
-// same planes as two launch_residue calls write (m, n, q >= 1).
-hipError_t launch_residue_pair(const double* A, int m, int lda, const int32_t* e, int8_t* Aplanes, int m_pad,
+// same planes as two launch_residue calls write (m, n, q >= 1).  With pmax
+// non-null, A's row exponents are not read from e but taken from the
+// nchunks partial row maxima of the scale step (pmax[c * m_stride + i]) and
+// written to e by the tiles of the first K columns: the row-exponent
+// finalisation folded into this launch.
+hipError_t launch_residue_pair(const double* A, int m, int lda, int32_t* e, int8_t* Aplanes, int m_pad,
                                const double* B, int n, int ldb, const int32_t* f, int8_t* Bplanes, int n_pad, int q,
-                               int q_pad, const ResidueConsts& c, hipStream_t st);
+                               int q_pad, const ResidueConsts& c, hipStream_t st, const uint64_t* pmax = nullptr,
+                               int m_stride = 0, int nchunks = 0);
 hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, const int32_t* ex,
                           const ResidueConsts& c, int8_t* planes, int rows_pad, int q_pad,
                           double* prime, long prime_rs, long prime_ls, hipStream_t st);

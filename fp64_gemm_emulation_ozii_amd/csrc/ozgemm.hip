@@ -260,6 +260,11 @@ void crt_weights(int s, double* out) {
 // Global configuration and workspace layout
 // ---------------------------------------------------------------------------
 constexpr int NCH_MAX = 256;  // partial row-max chunks of A
+// m x chunks up to which run_dgemm folds the row-exponent finalisation into
+// the paired residue pass.  Same-box A/B: 1024^3 (32768) 5% faster per call;
+// 2048^3 (131072) no faster, the extra partial reads cost the residue pass
+// what the saved launch gains.
+constexpr long FOLD_MAX_PARTIALS = 1L << 16;
 
 struct Layout {
   size_t consts, pmax, e, f, ares, bres, rt, rt_bytes, total;
@@ -464,8 +469,11 @@ bool accu_fits(const Layout& lay, int m, int n, int q) {
          lay.rt_bytes >= accu_scratch_bytes(mpc, npc, qpc) && (size_t)qpc / K_PAD * 4 <= (size_t)NCH_MAX * 8;
 }
 
+// With fold_e (conservative budget, both operands) A's row exponents are
+// left to the paired residue pass, which reduces the partial row maxima
+// itself (launch_residue_pair with pmax).
 int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda, const double* B, int ldb,
-              int32_t* e, int32_t* f) {
+              int32_t* e, int32_t* f, bool fold_e = false) {
   const int mp = x.row_stride;
   uint64_t* pmax = reinterpret_cast<uint64_t*>(x.ws + x.lay.pmax);
   const int nch = nchunks_for(m, q);
@@ -476,7 +484,7 @@ int run_scale(const Ctx& x, int m, int n, int q, int s, const double* A, int lda
   if (m > 0 && n > 0 && q > 0) {
     // A's partial row maxima and B's column maxima in one launch
     OZ_CHECK(launch_scale_pair(A, m, q, lda, pmax, mp, nch, B, n, ldb, f, x.stream));
-    OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
+    if (!fold_e) OZ_CHECK(launch_row_exp_finalize(pmax, m, mp, nch, e, x.stream));
     if (fast) OZ_CHECK(launch_fast_pair(A, m, q, lda, pmax, mp, nch, ka, B, n, ldb, kb, kbase, e, f, x.stream));
   } else {
     if (m > 0) {
@@ -704,7 +712,14 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   // OS II-fast with the column's norm bound too); OS II-accu needs them
   // before its bound, so it keeps two passes
   const bool b_one_pass = x.bound != OZGEMM_BOUND_ACCU && col_residue_fits(q);
-  if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f))) return st;
+  // Small products under the conservative budget skip the row-exponent
+  // finalisation launch: the paired residue pass reduces the partial row
+  // maxima itself (every A tile re-reads its rows' partials, so only while
+  // they are few).
+  const int nch = nchunks_for(m, q);
+  const bool fold_e = x.bound == OZGEMM_BOUND_CONSERVATIVE && !b_one_pass && x.panels <= 1 &&
+                      (long)m * nch <= FOLD_MAX_PARTIALS;
+  if ((st = run_scale(x, m, b_one_pass ? 0 : n, q, s, A, lda, B, ldb, e, f, fold_e))) return st;
   if (ev) OZ_CHECK(hipEventRecord((*ev)[1], x.stream));
   if (x.panels > 1) {
     OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
@@ -742,6 +757,9 @@ int run_dgemm(const Ctx& x, const double* wtab, int m, int n, int q, const doubl
   if (b_one_pass) {
     OZ_CHECK(launch_residue(A, m, q, 1, lda, e, rc, Ares, mp, qp, nullptr, 0, 0, x.stream));
     OZ_CHECK(launch_col_residue(B, n, q, ldb, f, rc, Bres, np, qp, x.stream));
+  } else if (fold_e) {  // A's and B's residues in one launch, A's exponents from the partial maxima
+    OZ_CHECK(launch_residue_pair(A, m, lda, e, Ares, mp, B, n, ldb, f, Bres, np, q, qp, rc, x.stream,
+                                 reinterpret_cast<const uint64_t*>(x.ws + x.lay.pmax), x.row_stride, nch));
   } else {  // A's and B's residues in one launch
     OZ_CHECK(launch_residue_pair(A, m, lda, e, Ares, mp, B, n, ldb, f, Bres, np, q, qp, rc, x.stream));
   }

@@ -83,16 +83,36 @@ __device__ __forceinline__ void write_residues16(double (&a)[16], const ResidueC
   }
 }
 
+// The row-exponent finalisation folded into A's residue tiles: the partial
+// row maxima of the scale step (nchunks words per row, stride m_stride) and
+// where the exponents go.
+struct FoldedExp {
+  const uint64_t* pmax;
+  int m_stride;
+  int nchunks;
+  int32_t* e_out;
+};
+
 // Tile (bx, by) of residue_kernel: rows by*TR.., inner-dimension entries
-// bx*TK.., staged through `tile` (TR * LDS_STRIDE doubles of LDS).
-template <bool ROWS_CONTIG, int MODE>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
+// bx*TK.., staged through `tile` (TR * LDS_STRIDE doubles of LDS).  With
+// FOLD the row exponents come from the partial row maxima (the eight threads
+// of a row each take every eighth chunk) instead of ex, and the tiles with
+// bx = 0 write them to fold.e_out.
+template <bool ROWS_CONTIG, int MODE, bool FOLD = false>  // MODE 0: k <= 50, 1: k <= 53, 2: k > 53
 __device__ __forceinline__ void residue_tile(double* tile, int bx, int by, const double* __restrict__ X, int rows,
                                              int q, long rs, long ls, const int32_t* __restrict__ ex,
                                              const ResidueConsts& c, int8_t* __restrict__ planes, long plane_stride,
-                                             int q_pad, double* __restrict__ prime, long prime_rs, long prime_ls) {
+                                             int q_pad, double* __restrict__ prime, long prime_rs, long prime_ls,
+                                             FoldedExp fold = {nullptr, 0, 0, nullptr}) {
   const int tid = threadIdx.x;
   const int r0 = by * TR;
   const int l0 = bx * TK;
+  const int grow = r0 + (tid >> 3);  // the row this thread converts (below)
+
+  // partial maxima first, so that their latency overlaps the tile's loads
+  uint64_t pm = 0;
+  if (FOLD && grow < rows)
+    for (int cc = tid & 7; cc < fold.nchunks; cc += 8) pm = umax64(pm, fold.pmax[(long)cc * fold.m_stride + grow]);
 
   // ---- coalesced load into LDS (zero outside the matrix) ----
   // All loads are issued before any is used: out-of-range lanes read a
@@ -136,10 +156,18 @@ __device__ __forceinline__ void residue_tile(double* tile, int bx, int by, const
   // ---- each thread: one row, 16 consecutive entries ----
   const int r = tid >> 3;          // 0..31
   const int cseg = (tid & 7) * 16; // 0..112
-  const int grow = r0 + r;
   int e = 0;
   bool zero_row = true;
-  if (grow < rows) {
+  if (FOLD) {
+    // the row's maximum over the eight threads of the row (lanes 8 j .. 8 j + 7)
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) pm = umax64(pm, (uint64_t)__shfl_xor((unsigned long long)pm, off, 64));
+    if (grow < rows) {
+      e = exponent_of_bits(pm);
+      zero_row = (e == OZGEMM_EXP_NONFINITE);
+      if (bx == 0 && (tid & 7) == 0) fold.e_out[grow] = e;
+    }
+  } else if (grow < rows) {
     e = ex[grow];
     zero_row = (e == OZGEMM_EXP_NONFINITE);
   }
@@ -178,20 +206,20 @@ __global__ __launch_bounds__(256) void residue_kernel(const double* __restrict__
 // the inner dimension contiguous): blocks [0, na) are A's tiles, the rest
 // B's, each in row-major order of a (q_pad / TK)-wide grid.  For small
 // products the two passes' ramp-up and drain then overlap.
-template <int MODE>
+template <int MODE, bool FOLD>
 __global__ __launch_bounds__(256) void residue_pair_kernel(const double* __restrict__ A, int m, long lda,
                                                             const int32_t* __restrict__ e,
                                                             int8_t* __restrict__ Aplanes, int m_pad,
                                                             const double* __restrict__ B, int n, long ldb,
                                                             const int32_t* __restrict__ f,
                                                             int8_t* __restrict__ Bplanes, int n_pad, int q, int q_pad,
-                                                            ResidueConsts c, int na) {
+                                                            ResidueConsts c, int na, FoldedExp fold) {
   __shared__ double tile[TR * LDS_STRIDE];
   const int gx = q_pad / TK;
   const int b = blockIdx.x;
   if (b < na)
-    residue_tile<true, MODE>(tile, b % gx, b / gx, A, m, q, 1, lda, e, c, Aplanes, (long)m_pad * q_pad, q_pad,
-                             nullptr, 0, 0);
+    residue_tile<true, MODE, FOLD>(tile, b % gx, b / gx, A, m, q, 1, lda, e, c, Aplanes, (long)m_pad * q_pad,
+                                   q_pad, nullptr, 0, 0, fold);
   else
     residue_tile<false, MODE>(tile, (b - na) % gx, (b - na) / gx, B, n, q, ldb, 1, f, c, Bplanes,
                               (long)n_pad * q_pad, q_pad, nullptr, 0, 0);
@@ -296,21 +324,31 @@ hipError_t launch_residue(const double* X, int rows, int q, long rs, long ls, co
   return hipGetLastError();
 }
 
-hipError_t launch_residue_pair(const double* A, int m, int lda, const int32_t* e, int8_t* Aplanes, int m_pad,
+hipError_t launch_residue_pair(const double* A, int m, int lda, int32_t* e, int8_t* Aplanes, int m_pad,
                                const double* B, int n, int ldb, const int32_t* f, int8_t* Bplanes, int n_pad, int q,
-                               int q_pad, const ResidueConsts& c, hipStream_t st) {
+                               int q_pad, const ResidueConsts& c, hipStream_t st, const uint64_t* pmax,
+                               int m_stride, int nchunks) {
   if (q < 1 || m < 1 || n < 1) return hipErrorInvalidValue;
   if (q_pad % TK || m_pad % TR || n_pad % TR || q_pad < q || m_pad < m || n_pad < n)
     return hipErrorInvalidValue;  // whole tiles
+  if (pmax != nullptr && (nchunks < 1 || m_stride < m)) return hipErrorInvalidValue;
   const long na = (long)(q_pad / TK) * (m_pad / TR), nb = (long)(q_pad / TK) * (n_pad / TR);
   if (na + nb > 0x7fffffffL) return hipErrorInvalidValue;
   const int mode = c.kmag <= 50 ? 0 : (c.kmag <= 53 ? 1 : 2);
-#define OZ_RES_PAIR(MD)                                                                                       \
-  hipLaunchKernelGGL((residue_pair_kernel<MD>), dim3((unsigned)(na + nb)), dim3(256), 0, st, A, m, (long)lda, e, \
-                     Aplanes, m_pad, B, n, (long)ldb, f, Bplanes, n_pad, q, q_pad, c, (int)na)
-  if (mode == 0) OZ_RES_PAIR(0);
-  else if (mode == 1) OZ_RES_PAIR(1);
-  else OZ_RES_PAIR(2);
+  const FoldedExp fold{pmax, m_stride, nchunks, e};
+#define OZ_RES_PAIR(MD, FD)                                                                                    \
+  hipLaunchKernelGGL((residue_pair_kernel<MD, FD>), dim3((unsigned)(na + nb)), dim3(256), 0, st, A, m, (long)lda, \
+                     FD ? nullptr : e, Aplanes, m_pad, B, n, (long)ldb, f, Bplanes, n_pad, q, q_pad, c, (int)na,  \
+                     fold)
+  if (pmax != nullptr) {
+    if (mode == 0) OZ_RES_PAIR(0, true);
+    else if (mode == 1) OZ_RES_PAIR(1, true);
+    else OZ_RES_PAIR(2, true);
+  } else {
+    if (mode == 0) OZ_RES_PAIR(0, false);
+    else if (mode == 1) OZ_RES_PAIR(1, false);
+    else OZ_RES_PAIR(2, false);
+  }
 #undef OZ_RES_PAIR
   return hipGetLastError();
 }

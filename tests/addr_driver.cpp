@@ -17,7 +17,8 @@
 //         (preceded by "<nout>"): int32 output, eight wavefronts
 //   reduce <m_pad> <n_pad> <s> <parts>
 //   residue <rows> <rows_pad> <q> <q_pad> <s> <rs> <ls> <one_pass>
-//   residue_pair <m> <m_pad> <lda> <n> <n_pad> <ldb> <q> <q_pad> <s>
+//   residue_pair <m> <m_pad> <lda> <n> <n_pad> <ldb> <q> <q_pad> <s> <m_stride> <nchunks>
+//         (nchunks 0: A's exponents read, not folded)
 //   scale_pair <m> <m_pad> <lda> <n> <ldb> <q> <nchunks>
 //   crt <m> <n> <m_pad> <n_pad> <s> <ldc>
 // Output: one line "ok <accesses>" or "bad <what> ..." per input line.
@@ -246,15 +247,30 @@ void residue(int rows, int rows_pad, int q, int q_pad, int s, long rs, long ls, 
 // residue_pair_kernel: blocks [0, na) are column-major A's tiles, the rest
 // B's, each decoded from the linear block id over a (q_pad / 128)-wide grid;
 // every tile of both grids must come up exactly once.
-void residue_pair(int m, int m_pad, long lda, int n, int n_pad, long ldb, int q, int q_pad, int s) {
+// With nchunks > 0 (the row-exponent finalisation folded in) every A tile
+// also reads its rows' partial row maxima (nchunks words of stride m_stride)
+// and the tiles with bx = 0 write the rows' exponents.
+void residue_pair(int m, int m_pad, long lda, int n, int n_pad, long ldb, int q, int q_pad, int s, int m_stride,
+                  int nchunks) {
   const int gx = q_pad / 128;
   const long na = (long)gx * (m_pad / 32), nb = (long)gx * (n_pad / 32);
-  std::vector<int> seen_a(na, 0), seen_b(nb, 0);
+  std::vector<int> seen_a(na, 0), seen_b(nb, 0), e_written(m, 0);
   for (long b = 0; b < na + nb; ++b) {
     if (b < na) {
       const int bx = (int)(b % gx), by = (int)(b / gx);
       residue_tile(m, m_pad, q, q_pad, s, 1, lda, bx, by);
       ++seen_a[(long)by * gx + bx];
+      if (nchunks > 0)
+        for (int tid = 0; tid < 256; ++tid) {
+          const int grow = by * 32 + (tid >> 3);
+          if (grow >= m) continue;
+          for (int cc = tid & 7; cc < nchunks; cc += 8)
+            in_range((long)cc * m_stride + grow, 1, (long)nchunks * m_stride, "partial row max load");
+          if (bx == 0 && (tid & 7) == 0) {
+            in_range(grow, 1, m, "folded exponent store");
+            ++e_written[grow];
+          }
+        }
     } else {
       const int bx = (int)((b - na) % gx), by = (int)((b - na) / gx);
       residue_tile(n, n_pad, q, q_pad, s, ldb, 1, bx, by);
@@ -263,6 +279,8 @@ void residue_pair(int m, int m_pad, long lda, int n, int n_pad, long ldb, int q,
   }
   for (long t = 0; t < na; ++t) check(seen_a[t] == 1, "A tile count", t, seen_a[t]);
   for (long t = 0; t < nb; ++t) check(seen_b[t] == 1, "B tile count", t, seen_b[t]);
+  if (nchunks > 0)
+    for (int i = 0; i < m; ++i) check(e_written[i] == 1, "folded exponent writes", i, e_written[i]);
 }
 
 // scale_pair_kernel: blocks [0, na) are row_max_partial_kernel's over a
@@ -350,10 +368,12 @@ int main() {
       if (std::scanf("%d %d %d %d %d %ld %ld %d", &rows, &rows_pad, &q, &q_pad, &s, &rs, &ls, &one) != 8) return 1;
       residue(rows, rows_pad, q, q_pad, s, rs, ls, one != 0);
     } else if (!std::strcmp(cmd, "residue_pair")) {
-      int m, mp, n, np, q, qp, s;
+      int m, mp, n, np, q, qp, s, mstride, nch;
       long lda, ldb;
-      if (std::scanf("%d %d %ld %d %d %ld %d %d %d", &m, &mp, &lda, &n, &np, &ldb, &q, &qp, &s) != 9) return 1;
-      residue_pair(m, mp, lda, n, np, ldb, q, qp, s);
+      if (std::scanf("%d %d %ld %d %d %ld %d %d %d %d %d", &m, &mp, &lda, &n, &np, &ldb, &q, &qp, &s, &mstride,
+                     &nch) != 11)
+        return 1;
+      residue_pair(m, mp, lda, n, np, ldb, q, qp, s, mstride, nch);
     } else if (!std::strcmp(cmd, "scale_pair")) {
       int m, mp, n, q, nch;
       long lda, ldb;

@@ -130,12 +130,19 @@ def test_residue_and_crt_index_ranges(driver, rows, q):
 def test_pair_launches_stay_in_bounds(driver, m, n, q):
     """The one-launch forms of A's and B's residue passes and of their scale
     passes: every block decodes to a tile of the two separate grids, each
-    tile comes up once, and every access stays inside its buffer."""
+    tile comes up once, and every access stays inside its buffer; with the
+    row-exponent finalisation folded in, every row's exponent is stored
+    exactly once."""
     mp, np_, qp = pad(m, 256), pad(n, 256), pad(q, 128)
-    lines = [f"residue_pair {m} {mp} {m + 3} {n} {np_} {q + 1} {q} {qp} 14",
-             f"residue_pair {m} {mp} {m} {n} {np_} {q} {q} {qp} 20"]
+    lines = [f"residue_pair {m} {mp} {m + 3} {n} {np_} {q + 1} {q} {qp} 14 0 0",
+             f"residue_pair {m} {mp} {m} {n} {np_} {q} {q} {qp} 20 0 0"]
     for nch in (1, 8, min(128, max(1, q // 8))):
         lines.append(f"scale_pair {m} {mp} {m + 5} {n} {q + 2} {q} {nch}")
+        # the row-exponent finalisation folded into the residue pass: the
+        # partial maxima the scale pass wrote (stride m_pad, or a larger
+        # configured one), and one exponent store per row
+        lines.append(f"residue_pair {m} {mp} {m + 3} {n} {np_} {q + 1} {q} {qp} 14 {mp} {nch}")
+        lines.append(f"residue_pair {m} {mp} {m} {n} {np_} {q} {q} {qp} 14 {mp + 512} {nch}")
     for r in run(driver, lines):
         assert r.startswith("ok"), r
 
