@@ -128,24 +128,29 @@ __device__ __forceinline__ void row_norm_partial_block(const double* __restrict_
   const int i = bx * 256 + threadIdx.x;
   const int l0 = by * chunk;
   const int l1 = min(q, l0 + chunk);
-  uint64_t s0 = 0, s1 = 0;
+  uint64_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (i < m) {
     const int ei = e[i];
     if (ei != OZGEMM_EXP_NONFINITE) {
       const double* p = A + i + (long)l0 * lda;
       int l = l0;
-      for (; l + 2 <= l1; l += 2) {
-        s0 += norm_term(__builtin_nontemporal_load(p), ei);
-        s1 += norm_term(__builtin_nontemporal_load(p + lda), ei);
-        p += 2 * lda;
+      for (; l + 8 <= l1; l += 8) {  // eight independent loads in flight (the sum is exact in any order)
+        double x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(p + u * lda);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] += norm_term(x[u], ei);
+        p += 8 * lda;
       }
       for (; l < l1; ++l) {
-        s0 += norm_term(*p, ei);
+        v[0] += norm_term(*p, ei);
         p += lda;
       }
     }
   }
-  psum[(long)by * m_stride + i] = s0 + s1;
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v[0] += v[u];
+  psum[(long)by * m_stride + i] = v[0];
 }
 
 __global__ __launch_bounds__(256) void row_norm_partial_kernel(const double* __restrict__ A, int m, int q,
@@ -175,14 +180,19 @@ __device__ __forceinline__ void col_fast_block(const double* __restrict__ B, int
   uint64_t S = 0;
   if (fj != OZGEMM_EXP_NONFINITE) {
     const double* col = B + (long)j * ldb;
-    uint64_t s0 = 0, s1 = 0;
+    uint64_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int l = lane;
-    for (; l + 64 < q; l += 128) {
-      s0 += norm_term(__builtin_nontemporal_load(col + l), fj);
-      s1 += norm_term(__builtin_nontemporal_load(col + l + 64), fj);
+    for (; l + 448 < q; l += 512) {  // eight independent loads in flight (the sum is exact in any order)
+      double x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(col + l + 64 * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] += norm_term(x[u], fj);
     }
-    for (; l < q; l += 64) s0 += norm_term(col[l], fj);
-    S = s0 + s1;
+    for (; l < q; l += 64) w[0] += norm_term(col[l], fj);
+    S = w[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) S += w[u];
     for (int off = 32; off > 0; off >>= 1) S += (uint64_t)__shfl_xor((unsigned long long)S, off, 64);
   }
   if (lane == 0) f[j] = fast_exponent(fj, S, kappa, kb);
