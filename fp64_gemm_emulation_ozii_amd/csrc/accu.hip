@@ -59,19 +59,19 @@ __device__ __forceinline__ uint32_t pack4(const int* v) {
          ((uint32_t)(v[3] & 0xff) << 24);
 }
 
-// Bands of the rows of X (element (r, l) at X[r rs + l ls]) into two int8
-// planes (rows_pad x q_pad, K-contiguous, zero padding), and per tile of 128
-// inner-dimension entries the sum of each row's Lo values:
-// psum[blockIdx.x * rows_pad + r].
+// Tile (bx, by) of the bands of the rows of X (element (r, l) at
+// X[r rs + l ls]) into two int8 planes (rows_pad x q_pad, K-contiguous, zero
+// padding), and per tile of 128 inner-dimension entries the sum of each
+// row's Lo values: psum[bx * rows_pad + r].  `tile` is TR * LDS_STRIDE
+// doubles of LDS.
 template <bool ROWS_CONTIG>
-__global__ __launch_bounds__(256) void accu_band_kernel(const double* __restrict__ X, int rows, int q, long rs, long ls,
-                                                         const int32_t* __restrict__ ex, int8_t* __restrict__ Hp,
-                                                         int8_t* __restrict__ Lp, int q_pad, int rows_pad,
-                                                         int32_t* __restrict__ psum) {
-  __shared__ double tile[TR * LDS_STRIDE];
+__device__ __forceinline__ void band_tile(double* tile, int bx, int by, const double* __restrict__ X, int rows, int q,
+                                          long rs, long ls, const int32_t* __restrict__ ex, int8_t* __restrict__ Hp,
+                                          int8_t* __restrict__ Lp, int q_pad, int rows_pad,
+                                          int32_t* __restrict__ psum) {
   const int tid = threadIdx.x;
-  const int r0 = blockIdx.y * TR;
-  const int l0 = blockIdx.x * TK;
+  const int r0 = by * TR;
+  const int l0 = bx * TK;
   if (rows < 1) {
     for (int idx = tid; idx < TR * LDS_STRIDE; idx += 256) tile[idx] = 0.0;
   } else if (ROWS_CONTIG) {
@@ -132,25 +132,46 @@ __global__ __launch_bounds__(256) void accu_band_kernel(const double* __restrict
   // the 8 threads of a row are 8 consecutive lanes of one wavefront
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
-  if ((tid & 7) == 0) psum[(long)blockIdx.x * rows_pad + grow] = sum;
+  if ((tid & 7) == 0) psum[(long)bx * rows_pad + grow] = sum;
 }
 
-// Row sums of Lo: out[r] = sum over the nchunks tiles of psum.
-__global__ __launch_bounds__(256) void accu_rowsum_kernel(const int32_t* __restrict__ psum, int rows_pad, int nchunks,
-                                                           int32_t* __restrict__ out) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows_pad) return;
-  int s = 0;
-  for (int c = 0; c < nchunks; ++c) s += psum[(long)c * rows_pad + r];
-  out[r] = s;
+// A's bands (column-major A: rows contiguous) and B's (its columns as rows:
+// the inner dimension contiguous) in one launch: blocks [0, na) are A's
+// tiles, the rest B's, each in row-major order of a (q_pad / TK)-wide grid.
+__global__ __launch_bounds__(256) void accu_band_pair_kernel(
+    const double* __restrict__ A, int m, long lda, const int32_t* __restrict__ e, int8_t* __restrict__ AH,
+    int8_t* __restrict__ AL, int m_pad, int32_t* __restrict__ psumA, const double* __restrict__ B, int n, long ldb,
+    const int32_t* __restrict__ f, int8_t* __restrict__ BH, int8_t* __restrict__ BL, int n_pad,
+    int32_t* __restrict__ psumB, int q, int q_pad, int na) {
+  __shared__ double tile[TR * LDS_STRIDE];
+  const int gx = q_pad / TK;
+  const int b = blockIdx.x;
+  if (b < na)
+    band_tile<true>(tile, b % gx, b / gx, A, m, q, 1L, lda, e, AH, AL, q_pad, m_pad, psumA);
+  else
+    band_tile<false>(tile, (b - na) % gx, (b - na) / gx, B, n, q, ldb, 1L, f, BH, BL, q_pad, n_pad, psumB);
 }
 
-// The product plan: output 0 = H_A H_B^T; output 1 = H_A Lo_B^T + Lo_A H_B^T.
-__global__ void accu_plan_kernel(int4* plan) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
+// Row sums of Lo for A's rows (blocks [0, ga)) and B's columns (the rest):
+// out[r] = sum over the nchunks tiles of psum.  Block 0 also writes the
+// product plan: output 0 = H_A H_B^T; output 1 = H_A Lo_B^T + Lo_A H_B^T.
+__global__ __launch_bounds__(256) void accu_rowsum_pair_kernel(const int32_t* __restrict__ psumA, int m_pad,
+                                                                int32_t* __restrict__ RS,
+                                                                const int32_t* __restrict__ psumB, int n_pad,
+                                                                int32_t* __restrict__ CS, int nchunks, int ga,
+                                                                int4* __restrict__ plan) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     plan[0] = make_int4(0, 0, 1, 0);
     plan[1] = make_int4(0, 1, 2, 1);
   }
+  const bool is_a = (int)blockIdx.x < ga;
+  const int32_t* psum = is_a ? psumA : psumB;
+  const int rows_pad = is_a ? m_pad : n_pad;
+  const int r = (is_a ? blockIdx.x : blockIdx.x - ga) * 256 + threadIdx.x;
+  if (r >= rows_pad) return;
+  int s = 0;
+  for (int c = 0; c < nchunks; ++c) s += psum[(long)c * rows_pad + r];
+  (is_a ? RS : CS)[r] = s;
 }
 
 __device__ __forceinline__ int block_reduce(int v, bool take_max, int* red) {
@@ -290,14 +311,15 @@ hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const d
   int32_t* psumB = reinterpret_cast<int32_t*>(take((size_t)nk * 4 * np));
   int4* plan = reinterpret_cast<int4*>(take(2 * sizeof(int4)));
 
-  // bands of A's rows (A column-major: rows contiguous) and of B's columns
-  hipLaunchKernelGGL(accu_band_kernel<true>, dim3(nk, m_pad / TR), dim3(256), 0, st, A, m, q, 1L, (long)lda, e,
-                     Aplanes, Aplanes + mp * q_pad, q_pad, m_pad, psumA);
-  hipLaunchKernelGGL(accu_band_kernel<false>, dim3(nk, n_pad / TR), dim3(256), 0, st, B, n, q, (long)ldb, 1L, f,
-                     Bplanes, Bplanes + np * q_pad, q_pad, n_pad, psumB);
-  hipLaunchKernelGGL(accu_rowsum_kernel, dim3(m_pad / 256), dim3(256), 0, st, psumA, m_pad, nk, RS);
-  hipLaunchKernelGGL(accu_rowsum_kernel, dim3(n_pad / 256), dim3(256), 0, st, psumB, n_pad, nk, CS);
-  hipLaunchKernelGGL(accu_plan_kernel, dim3(1), dim3(64), 0, st, plan);
+  // bands of A's rows (A column-major: rows contiguous) and of B's columns,
+  // then their Lo row sums and the product plan: two launches
+  const long na = (long)nk * (m_pad / TR), nb = (long)nk * (n_pad / TR);
+  if (na + nb > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accu_band_pair_kernel, dim3((unsigned)(na + nb)), dim3(256), 0, st, A, m, (long)lda, e, Aplanes,
+                     Aplanes + mp * q_pad, m_pad, psumA, B, n, (long)ldb, f, Bplanes, Bplanes + np * q_pad, n_pad,
+                     psumB, q, q_pad, (int)na);
+  hipLaunchKernelGGL(accu_rowsum_pair_kernel, dim3(m_pad / 256 + n_pad / 256), dim3(256), 0, st, psumA, m_pad, RS,
+                     psumB, n_pad, CS, nk, m_pad / 256, plan);
   hipError_t err = launch_gemm_multi(Aplanes, Bplanes, m_pad, n_pad, q_pad, plan, 2, P, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(accu_combine_kernel, dim3(n), dim3(256), 0, st, P, m, m_pad, (long)(mp * np), RS, CS, K2, kmax,
