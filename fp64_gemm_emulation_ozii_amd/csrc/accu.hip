@@ -153,13 +153,17 @@ __global__ __launch_bounds__(256) void accu_band_pair_kernel(
 }
 
 // Row sums of Lo for A's rows (blocks [0, ga)) and B's columns (the rest):
-// out[r] = sum over the nchunks tiles of psum.  Block 0 also writes the
-// product plan: output 0 = H_A H_B^T; output 1 = H_A Lo_B^T + Lo_A H_B^T.
+// out[r] = sum over the nchunks tiles of psum, 64 rows per block, four
+// threads per row each adding every fourth tile sum (eight loads in
+// flight), combined through LDS.  (One thread per row with a serial loop
+// took 29 us per operand at 8192^3.)  Block 0 also writes the product plan:
+// output 0 = H_A H_B^T; output 1 = H_A Lo_B^T + Lo_A H_B^T.
 __global__ __launch_bounds__(256) void accu_rowsum_pair_kernel(const int32_t* __restrict__ psumA, int m_pad,
                                                                 int32_t* __restrict__ RS,
                                                                 const int32_t* __restrict__ psumB, int n_pad,
                                                                 int32_t* __restrict__ CS, int nchunks, int ga,
                                                                 int4* __restrict__ plan) {
+  __shared__ int part[4][64];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     plan[0] = make_int4(0, 0, 1, 0);
     plan[1] = make_int4(0, 1, 2, 1);
@@ -167,11 +171,21 @@ __global__ __launch_bounds__(256) void accu_rowsum_pair_kernel(const int32_t* __
   const bool is_a = (int)blockIdx.x < ga;
   const int32_t* psum = is_a ? psumA : psumB;
   const int rows_pad = is_a ? m_pad : n_pad;
-  const int r = (is_a ? blockIdx.x : blockIdx.x - ga) * 256 + threadIdx.x;
-  if (r >= rows_pad) return;
-  int s = 0;
-  for (int c = 0; c < nchunks; ++c) s += psum[(long)c * rows_pad + r];
-  (is_a ? RS : CS)[r] = s;
+  const int lr = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int r = (is_a ? blockIdx.x : blockIdx.x - ga) * 64 + lr;
+  int v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < rows_pad) {
+    int c = g;
+    for (; c + 28 < nchunks; c += 32)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += psum[(long)(c + 4 * u) * rows_pad + r];
+    for (; c < nchunks; c += 4) v[0] += psum[(long)c * rows_pad + r];
+  }
+#pragma unroll
+  for (int u = 1; u < 8; ++u) v[0] += v[u];
+  part[g][lr] = v[0];
+  __syncthreads();
+  if (g == 0 && r < rows_pad) (is_a ? RS : CS)[r] = part[0][lr] + part[1][lr] + part[2][lr] + part[3][lr];
 }
 
 __device__ __forceinline__ int block_reduce(int v, bool take_max, int* red) {
@@ -266,7 +280,22 @@ __global__ __launch_bounds__(256) void accu_colfinal_kernel(const int8_t* __rest
   const int j = blockIdx.x;
   const long col = (long)j * m_pad;
   int v = kmax;
-  for (int i = threadIdx.x; i < m; i += 256) v = min(v, K2 - (int)L[col + i] - a[i]);
+  // four consecutive rows per thread and step, so that both loads stay
+  // contiguous across the lanes: 4 bytes of L and 16 of a (both allocated
+  // to m_pad entries, so whole groups stay in bounds; rows >= m are
+  // skipped).  Byte loads, one row per thread and step, took 47 us at
+  // 8192^3; 16 rows per thread (a read at a 64-byte lane stride) 56 us.
+#pragma unroll 4
+  for (int i0 = threadIdx.x * 4; i0 < m; i0 += 256 * 4) {
+    const uint32_t lw = *reinterpret_cast<const uint32_t*>(L + col + i0);
+    const int4 av = *reinterpret_cast<const int4*>(a + i0);
+    const int aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int li = (int)(int8_t)(lw >> (8 * b));
+      if (i0 + b < m) v = min(v, K2 - li - aa[b]);
+    }
+  }
   v = block_reduce(v, false, red);
   if (threadIdx.x == 0) {
     const int fj = f[j];
@@ -318,8 +347,8 @@ hipError_t launch_accu_exponents(const double* A, int m, int q, int lda, const d
   hipLaunchKernelGGL(accu_band_pair_kernel, dim3((unsigned)(na + nb)), dim3(256), 0, st, A, m, (long)lda, e, Aplanes,
                      Aplanes + mp * q_pad, m_pad, psumA, B, n, (long)ldb, f, Bplanes, Bplanes + np * q_pad, n_pad,
                      psumB, q, q_pad, (int)na);
-  hipLaunchKernelGGL(accu_rowsum_pair_kernel, dim3(m_pad / 256 + n_pad / 256), dim3(256), 0, st, psumA, m_pad, RS,
-                     psumB, n_pad, CS, nk, m_pad / 256, plan);
+  hipLaunchKernelGGL(accu_rowsum_pair_kernel, dim3(m_pad / 64 + n_pad / 64), dim3(256), 0, st, psumA, m_pad, RS,
+                     psumB, n_pad, CS, nk, m_pad / 64, plan);
   hipError_t err = launch_gemm_multi(Aplanes, Bplanes, m_pad, n_pad, q_pad, plan, 2, P, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(accu_combine_kernel, dim3(n), dim3(256), 0, st, P, m, m_pad, (long)(mp * np), RS, CS, K2, kmax,
