@@ -109,14 +109,18 @@ __global__ void fill_zero_kernel(double* C, int m, int n, long ldc) {
 
 }  // namespace
 
+constexpr long CRT_ONE_COLUMN = 1L << 23;
+
 hipError_t launch_crt(const uint8_t* rt, int m, int n, int m_pad, int n_pad, const int32_t* e, const int32_t* f,
                       const CrtConsts& c, double* C, int ldc, hipStream_t st) {
   // each thread reads four bytes of a column of every plane: m_pad must hold
   // whole groups of four rows
   if (m < 1 || n < 1 || m_pad < m || n_pad < n || m_pad % 4 || ldc < m) return hipErrorInvalidValue;
   // two columns per thread (the second one's loads overlap the first's
-  // arithmetic)
-  dim3 grid((m + 1023) / 1024, std::min((n + 1) / 2, 65535));
+  // arithmetic); outputs of at most CRT_ONE_COLUMN entries take one column
+  // per thread, twice the blocks, for more loads in flight
+  const bool one_col = (long)m * n <= CRT_ONE_COLUMN;
+  dim3 grid((m + 1023) / 1024, std::min(one_col ? n : (n + 1) / 2, 65535));
   const long plane = (long)m_pad * n_pad;
   const int ng = (c.s + 3) / 4;
   if (ng < 1 || ng > 5) return hipErrorInvalidValue;

@@ -318,7 +318,9 @@ void scale_pair(int m, int m_pad, long lda, int n, long ldb, int q, int nchunks)
 void crt(int m, int n, int m_pad, int n_pad, int s, long ldc) {
   const long plane = (long)m_pad * n_pad;
   const int NG = (s + 3) / 4;
-  const int gx = (m + 1023) / 1024, gy = (n + 1) / 2 < 65535 ? (n + 1) / 2 : 65535;
+  // one column per thread for outputs of at most 2^23 entries, else two
+  const long cols = (long)m * n <= (1L << 23) ? n : (n + 1) / 2;
+  const int gx = (m + 1023) / 1024, gy = (int)(cols < 65535 ? cols : 65535);
   for (int bx = 0; bx < gx; ++bx)
     for (int tx = 0; tx < 256; ++tx) {
       const long i0 = ((long)bx * 256 + tx) * 4;

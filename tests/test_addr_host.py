@@ -113,6 +113,13 @@ def test_plan_form(driver, plan, planes):
         assert r.startswith("ok"), r
 
 
+def test_crt_two_column_form_index_ranges(driver):
+    """Outputs above 2^23 entries take two columns per thread (smaller ones
+    one): a ragged 4100 x 2100 output, padded leading dimension."""
+    for r in run(driver, [f"crt 4100 2100 {pad(4100, 256)} {pad(2100, 256)} 14 4103"]):
+        assert r.startswith("ok"), r
+
+
 @pytest.mark.parametrize("rows,q", [(1, 1), (300, 1000), (257, 129), (33, 4097)])
 def test_residue_and_crt_index_ranges(driver, rows, q):
     rp, qp = pad(rows, 256), pad(q, 128)
